@@ -1,0 +1,329 @@
+// Fused forward of the adapted 4-bit layer for many tokens:
+//     y = x W_bf16^T + (s u) B^T
+// [QLoRA "The QLoRA recipe" stage 3 / "The complete QLoRA forward pass": each
+// weight block is brought back to bf16 on the fly, multiplied by the input,
+// and the adapter correction is added; QA-LoRA abstract for the INT4 groups.]
+//
+// Tile: 256 tokens x 256 output features per workgroup of 4 waves; wave w
+// owns features [64w, 64w+64) for all 256 tokens, so every 4-bit weight is
+// decoded exactly once per workgroup, straight from HBM into registers
+// (byte-permute lookup, no LDS), and reused by 8 MFMAs.  The 256x128 bf16
+// token tile of each K step is streamed into LDS with direct-to-LDS loads
+// (double buffered, XOR-swizzled 16-byte chunks: conflict-free reads).
+// The adapter term is 2*ceil(r/16) extra MFMA k-steps on the same
+// accumulators, with s*u split into hi + lo bf16 halves.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace qlin {
+
+namespace {
+
+constexpr int kTM = 256;
+constexpr int kTN = 256;
+constexpr int kKS = 128;
+constexpr int kXTile = kTM * kKS * 2;  // bytes
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t xoff(int row, int chunk) {
+  return static_cast<uint32_t>(row * 256 + ((chunk ^ (row & 7)) << 4));
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+// contiguous run of tiles (tile order: token tile major) so that the
+// workgroups resident on one XCD share their token rows in its L2.
+__device__ __forceinline__ int remap_xcd(int bid, int n) {
+  const int q = n >> 3, rem = n & 7;
+  const int xcd = bid & 7, idx = bid >> 3;
+  return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+}
+
+template <int FMT>
+struct StepParams;
+template <>
+struct StepParams<kFmtNF4> {
+  float scale[2];  // per row
+};
+template <>
+struct StepParams<kFmtINT4> {
+  uint32_t sz[2][2];  // per row, per group: scale (lo16) | zero (hi16)
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_params(const WeightView& w, const int64_t (&nr)[2],
+                                            int64_t kblk, bool valid, StepParams<FMT>& p);
+
+template <>
+__device__ __forceinline__ void load_params<kFmtNF4>(const WeightView& w, const int64_t (&nr)[2],
+                                                     int64_t kblk, bool valid,
+                                                     StepParams<kFmtNF4>& p) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    p.scale[r] = valid ? nf4_block_scale(w, nr[r] * (w.K >> 6) + kblk) : 0.0f;
+}
+
+template <>
+__device__ __forceinline__ void load_params<kFmtINT4>(const WeightView& w, const int64_t (&nr)[2],
+                                                      int64_t kblk, bool valid,
+                                                      StepParams<kFmtINT4>& p) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int64_t g = nr[r] * (w.K >> 5) + kblk * 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      p.sz[r][q] = valid ? (static_cast<uint32_t>(w.scale[g + q]) |
+                            (static_cast<uint32_t>(w.zero[g + q]) << 16))
+                         : 0u;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ Lut16 step_lut(const WeightView& w, const StepParams<FMT>& p, int r,
+                                          int q);
+template <>
+__device__ __forceinline__ Lut16 step_lut<kFmtNF4>(const WeightView& w,
+                                                   const StepParams<kFmtNF4>& p, int r, int) {
+  return lut_nf4(w.cb, p.scale[r]);
+}
+template <>
+__device__ __forceinline__ Lut16 step_lut<kFmtINT4>(const WeightView&,
+                                                    const StepParams<kFmtINT4>& p, int r, int q) {
+  return lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.sz[r][q] & 0xFFFFu)),
+                  half_bits_to_f32(static_cast<uint16_t>(p.sz[r][q] >> 16)));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXTile];
+  __shared__ uint32_t s_ticket;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t M = a.M, N = a.w.N, K = a.w.K;
+  const int tiles_m = static_cast<int>((M + kTM - 1) / kTM);
+  const int tiles_n = static_cast<int>((N + kTN - 1) / kTN);
+  const int n_work = tiles_m * tiles_n * a.splits;
+  const int t = remap_xcd(static_cast<int>(blockIdx.x), n_work);
+  const int sp = t % a.splits;
+  const int tmn = t / a.splits;
+  const int tm = tmn / tiles_n, tn = tmn % tiles_n;
+  const int64_t m0 = static_cast<int64_t>(tm) * kTM, n0 = static_cast<int64_t>(tn) * kTN;
+  const int64_t ksteps = (K + kKS - 1) / kKS;
+  const int64_t per = (ksteps + a.splits - 1) / a.splits;
+  const int64_t ks0 = sp * per;
+  const int64_t ks1 = ks0 + per < ksteps ? ks0 + per : ksteps;
+
+  int64_t nr[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int64_t n = n0 + wave * 64 + r * 32 + l32;
+    nr[r] = n < N ? n : N - 1;
+  }
+  const uint8_t* crow0 = a.w.codes + nr[0] * (K >> 1);
+  const uint8_t* crow1 = a.w.codes + nr[1] * (K >> 1);
+
+  f32x16 acc[2][8];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms) acc[r][ms] = f32x16{};
+
+  auto load_x = [&](int64_t ks, int buf) {
+    const int64_t kb = ks * kKS;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = (i * 4 + wave) * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 7);
+      int64_t m = m0 + row;
+      m = m < M ? m : M - 1;
+      int64_t k = kb + c * 8;
+      k = k < K ? k : K - 8;
+      const uint16_t* src = a.x + m * K + k;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(&s_x[buf][(i * 4 + wave) * 1024]), 16, 0,
+                                       0);
+    }
+  };
+
+  u32x4 cc[2][2], cn[2][2];
+  StepParams<FMT> pc, pn;
+  auto load_codes = [&](int64_t ks, u32x4 (&c)[2][2], StepParams<FMT>& p) {
+    const int64_t kk = ks * kKS + h * 64;
+    const bool valid = kk < K;
+    const int64_t off = kk >> 1;
+    if (valid) {
+      c[0][0] = *reinterpret_cast<const u32x4*>(crow0 + off);
+      c[0][1] = *reinterpret_cast<const u32x4*>(crow0 + off + 16);
+      c[1][0] = *reinterpret_cast<const u32x4*>(crow1 + off);
+      c[1][1] = *reinterpret_cast<const u32x4*>(crow1 + off + 16);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) c[r][0] = c[r][1] = u32x4{0, 0, 0, 0};
+    }
+    load_params<FMT>(a.w, nr, kk >> 6, valid, p);
+  };
+
+  load_x(ks0, 0);
+  load_codes(ks0, cc, pc);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int64_t ks = ks0; ks < ks1; ++ks) {
+    const int buf = static_cast<int>((ks - ks0) & 1);
+    if (ks + 1 < ks1) {
+      load_x(ks + 1, buf ^ 1);
+      load_codes(ks + 1, cn, pn);
+    }
+    const bool wvalid = ks * kKS + h * 64 < K;
+    constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
+    Lut16 lut[2][NL];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int q = 0; q < NL; ++q) lut[r][q] = step_lut<FMT>(a.w, pc, r, q);
+
+    const uint8_t* xb = s_x[buf];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      u32x4 wf[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t word = cc[r][tt >> 2][tt & 3];
+        const u32x4 d = lut_decode8(lut[r][NL == 1 ? 0 : (tt >> 2)], word);
+        wf[r] = wvalid ? d : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int ms = 0; ms < 8; ++ms) {
+        const u32x4 xf = *reinterpret_cast<const u32x4*>(xb + xoff(ms * 32 + l32, 8 * h + tt));
+        acc[0][ms] = mfma32(wf[0], xf, acc[0][ms]);
+        acc[1][ms] = mfma32(wf[1], xf, acc[1][ms]);
+      }
+      // keep each k16 sub-step's operands live only within the sub-step
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      cc[r][0] = cn[r][0];
+      cc[r][1] = cn[r][1];
+    }
+    pc = pn;
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // adapter term: acc += B[n][j] * (s u[m][j]) over j, in k16 steps.
+  // Loads use clamped indices and a select (no divergent branches).
+  if (sp == 0 && a.u != nullptr && a.r > 0) {
+    const int rr = a.r;
+    const int jsteps = (rr + 15) / 16;
+    for (int jt = 0; jt < jsteps; ++jt) {
+      const int j0 = jt * 16 + h * 8;
+      u32x4 bf[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint16_t* brow = a.B + nr[r] * rr;
+        uint32_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ja = j0 + 2 * e, jb = ja + 1;
+          const uint32_t lo = brow[ja < rr ? ja : rr - 1];
+          const uint32_t hi = brow[jb < rr ? jb : rr - 1];
+          v[e] = (ja < rr ? lo : 0u) | ((jb < rr ? hi : 0u) << 16);
+        }
+        bf[r] = u32x4{v[0], v[1], v[2], v[3]};
+      }
+#pragma unroll
+      for (int ms = 0; ms < 8; ++ms) {
+        int64_t m = m0 + ms * 32 + l32;
+        m = m < M ? m : M - 1;
+        const float* urow = a.u + m * rr;
+        float hv[8], lv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + e;
+          const float uraw = urow[j < rr ? j : rr - 1];
+          split_bf16(j < rr ? a.s * uraw : 0.0f, hv[e], lv[e]);
+        }
+        u32x4 uh, ul;
+        uh.x = pack_bf16x2(hv[0], hv[1]); uh.y = pack_bf16x2(hv[2], hv[3]);
+        uh.z = pack_bf16x2(hv[4], hv[5]); uh.w = pack_bf16x2(hv[6], hv[7]);
+        ul.x = pack_bf16x2(lv[0], lv[1]); ul.y = pack_bf16x2(lv[2], lv[3]);
+        ul.z = pack_bf16x2(lv[4], lv[5]); ul.w = pack_bf16x2(lv[6], lv[7]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          acc[r][ms] = mfma32(bf[r], uh, acc[r][ms]);
+          acc[r][ms] = mfma32(bf[r], ul, acc[r][ms]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  if (a.splits > 1) {
+    float* part = a.partial + (static_cast<int64_t>(tmn) * a.splits + sp) * (kTM * kTN);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) part[((r * 8 + ms) * 16 + v) * 256 + tid] = acc[r][ms][v];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_ticket = atomicAdd(a.counters + tmn, 1u);
+    __syncthreads();
+    if (s_ticket != static_cast<uint32_t>(a.splits - 1)) return;
+    __threadfence();
+    const float* base = a.partial + static_cast<int64_t>(tmn) * a.splits * (kTM * kTN);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float sum = 0.0f;
+          for (int s2 = 0; s2 < a.splits; ++s2)
+            sum += __builtin_nontemporal_load(base + s2 * (kTM * kTN) +
+                                              ((r * 8 + ms) * 16 + v) * 256 + tid);
+          acc[r][ms][v] = sum;
+        }
+    if (tid == 0) a.counters[tmn] = 0u;
+  }
+
+  // store: lane holds D[n = 8i + 4h + t][m = l32] of each 32x32 tile
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms) {
+      const int64_t m = m0 + ms * 32 + l32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = n0 + wave * 64 + r * 32 + 8 * i + 4 * h;
+        if (n >= N) continue;
+        u32x2 o;
+        o.x = pack_bf16x2(acc[r][ms][4 * i + 0], acc[r][ms][4 * i + 1]);
+        o.y = pack_bf16x2(acc[r][ms][4 * i + 2], acc[r][ms][4 * i + 3]);
+        *reinterpret_cast<u32x2*>(a.y + m * N + n) = o;
+      }
+    }
+}
+
+}  // namespace
+
+int fwd_gemm_tiles(int64_t M, int64_t N) {
+  return static_cast<int>(((M + kTM - 1) / kTM) * ((N + kTN - 1) / kTN));
+}
+int64_t fwd_gemm_partial_floats(int64_t M, int64_t N, int splits) {
+  return splits > 1 ? static_cast<int64_t>(fwd_gemm_tiles(M, N)) * splits * kTM * kTN : 0;
+}
+
+hipError_t launch_fwd_gemm(const FwdArgs& a, int fmt, hipStream_t stream) {
+  const int grid = fwd_gemm_tiles(a.M, a.w.N) * a.splits;
+  if (fmt == kFmtNF4)
+    hipLaunchKernelGGL(k_fwd_gemm<kFmtNF4>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_fwd_gemm<kFmtINT4>, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace qlin

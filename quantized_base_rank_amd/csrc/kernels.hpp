@@ -1,0 +1,143 @@
+// Host-visible launchers of the library's HIP kernels and their argument
+// blocks.  Only the C ABI layer (api.cpp) calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace qlin {
+
+// ---------------------------------------------------------------- quantizers
+hipError_t launch_quant_nf4(const float* W, int64_t n_blocks, int dq, const double* mids15,
+                            uint8_t* codes, void* absmax, float* absmax2, hipStream_t stream);
+hipError_t launch_quant_int4(const float* W, int64_t n_groups, uint8_t* codes, uint16_t* scale,
+                             uint16_t* zero, hipStream_t stream);
+hipError_t launch_dequant(const WeightView& w, int fmt, uint16_t* out, hipStream_t stream);
+
+// ------------------------------------------------------------ adapter ops
+struct NtArgs {  // C[m][j] = alpha * sum_k X[m][k] Y[j][k]
+  const uint16_t* X;  int64_t ldx;
+  const uint16_t* Y;  int64_t ldy;
+  float* C;           int64_t ldc;
+  int64_t M, K;       // K % 16 == 0
+  int32_t J;          // <= 128
+  int32_t splits;
+  float alpha;
+  float* partial;     // nt_partial_floats(M, splits)
+  uint32_t* counters; // nt_tiles(M)
+};
+hipError_t launch_nt_skinny(const NtArgs& a, hipStream_t stream);
+int nt_tiles(int64_t M);
+int64_t nt_partial_floats(int64_t M, int splits);
+
+struct TnArgs {  // C[p][j] (or C[j][p]) = alpha * sum_m X[m][p] Z[m][j]
+  const uint16_t* X;  int64_t ldx;
+  const float* Z;     int64_t ldz;
+  uint16_t* C;        int64_t ldc;
+  int64_t M, P;
+  int32_t J;          // <= 128
+  int32_t splits;
+  int32_t out_transposed;
+  float alpha;
+  float* partial;
+  uint32_t* counters;
+};
+hipError_t launch_tn_skinny(const TnArgs& a, hipStream_t stream);
+int tn_tiles(int64_t P);
+int64_t tn_partial_floats(int64_t P, int splits);
+
+hipError_t launch_transpose16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                              hipStream_t stream);
+
+struct QaArgs {  // pooled-adapter helpers (QA-LoRA)
+  const uint16_t* x;  // [M][K]
+  const uint16_t* A;  // [r][G]
+  const float* du;    // [M][r]
+  const float* P_in;  // [M][G]
+  float* P_out;       // [M][G]
+  float* u_out;       // [M][r]
+  float* Gq_out;      // [M][G]
+  uint16_t* dA_out;   // [r][G]
+  int64_t M, K, G;
+  int32_t r, pool;
+};
+hipError_t launch_qa_pool_u(const QaArgs& a, hipStream_t stream);
+hipError_t launch_qa_grad_in(const QaArgs& a, hipStream_t stream);
+hipError_t launch_qa_dA(const QaArgs& a, hipStream_t stream);
+
+// ------------------------------------------------- fused 4-bit GEMM kernels
+// y[M][N] = x W_bf16^T + (s u) B^T, large M (MFMA tiles of 256 x 256).
+struct FwdArgs {
+  WeightView w;
+  const uint16_t* x;   // [M][K]
+  int64_t M;
+  const uint16_t* B;   // [N][r] adapter
+  const float* u;      // [M][r] fp32, or nullptr (no adapter term)
+  int32_t r;
+  float s;
+  uint16_t* y;         // [M][N]
+  int32_t splits;      // split of the K loop across workgroups (>= 1)
+  float* partial;      // fwd_gemm_partial_floats
+  uint32_t* counters;  // fwd_gemm_tiles
+};
+hipError_t launch_fwd_gemm(const FwdArgs& a, int fmt, hipStream_t stream);
+int fwd_gemm_tiles(int64_t M, int64_t N);
+int64_t fwd_gemm_partial_floats(int64_t M, int64_t N, int splits);
+
+// dX[M][K] = dY W_bf16 + du A (+ Gq repeated over groups), large M.
+struct DxArgs {
+  WeightView w;
+  const uint16_t* dy;  // [M][N]
+  int64_t M;
+  const uint16_t* At;  // [K][r] (A transposed) or nullptr
+  const float* du;     // [M][r] or nullptr
+  int32_t r;
+  const float* Gq;     // [M][K/pool] pooled-adapter input gradient, or nullptr
+  int32_t pool;        // power of two
+  int32_t pool_shift;  // log2(pool)
+  uint16_t* dx;        // [M][K]
+};
+hipError_t launch_dx_gemm(const DxArgs& a, int fmt, hipStream_t stream);
+
+// Small-M (M <= 16) weight-streaming kernels, split along the reduction.
+struct GemvFwdArgs {
+  WeightView w;
+  const uint16_t* x;   // [M][K]
+  int64_t M;           // 1..16
+  const uint16_t* B;   // [N][r]
+  const float* u;      // [M][r] or nullptr
+  int32_t r;
+  float s;
+  uint16_t* y;         // [M][N]
+  int32_t splits;      // K split
+  float* partial;      // [splits][16][N]
+  uint32_t* counters;  // [N / 64]
+};
+hipError_t launch_gemv_fwd(const GemvFwdArgs& a, int fmt, hipStream_t stream);
+int gemv_fwd_splits(int64_t K);
+int64_t gemv_fwd_partial_floats(int64_t N, int64_t K);
+int gemv_fwd_tiles(int64_t N);
+
+struct GemvDxArgs {
+  WeightView w;
+  const uint16_t* dy;  // [M][N]
+  int64_t M;           // 1..16
+  const uint16_t* A;   // [r][K/pool] adapter A (natural layout)
+  const float* du;     // [M][r] or nullptr
+  int32_t r;
+  const float* Gq;     // [M][K/pool] or nullptr
+  int32_t pool;        // power of two
+  int32_t pool_shift;  // log2(pool)
+  uint16_t* dx;        // [M][K]
+  int32_t splits;      // N split
+  float* partial;      // [splits][16][K]
+  uint32_t* counters;  // [K / kGemvDxCols]
+};
+hipError_t launch_gemv_dx(const GemvDxArgs& a, int fmt, hipStream_t stream);
+int gemv_dx_splits(int64_t N);
+int64_t gemv_dx_partial_floats(int64_t N, int64_t K);
+int gemv_dx_tiles(int64_t K);
+
+}  // namespace qlin

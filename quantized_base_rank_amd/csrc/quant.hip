@@ -1,0 +1,206 @@
+// Quantizers (run once per frozen layer) and the test-only dequantizer.
+//
+// NF4: [QLoRA "Background: what is quantization?", "Innovation 1: 4-bit
+// NormalFloat (NF4)", "Innovation 2: Double Quantization", "The same idea in
+// code"].  INT4: [QA-LoRA abstract, group-wise INT4].
+//
+// Every decision that yields an integer (nearest level, the 8-bit absmax
+// code, the INT4 code) is taken with exact or correctly rounded IEEE
+// arithmetic, so codes and constants are reproducible bit for bit.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+#pragma clang fp contract(off)
+
+namespace qlin {
+
+namespace {
+
+// Midpoints of neighbouring levels, as float64 (exact for fp32 levels).
+struct Midpoints {
+  double m[15];
+};
+
+// One workgroup = one group of 256 consecutive blocks of 64 weights.  Each
+// wave handles 64 blocks, four at a time: 16 lanes per block, 4 weights per
+// lane.
+__global__ __launch_bounds__(256) void k_quant_nf4(const float* __restrict__ W, int64_t n_blocks,
+                                                   int dq, Midpoints mids,
+                                                   uint8_t* __restrict__ codes,
+                                                   void* __restrict__ absmax_out,
+                                                   float* __restrict__ absmax2_out) {
+  __shared__ float s_abs[256];
+  __shared__ int s_bad[256];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int sub = lane >> 4, li = lane & 15;
+  const int64_t g = blockIdx.x;
+  const int64_t blk0 = g * 256;
+
+  for (int it = 0; it < 16; ++it) {
+    const int local = wave * 64 + it * 4 + sub;  // block within the group
+    const int64_t b = blk0 + local;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (b < n_blocks) v = reinterpret_cast<const float4*>(W + b * 64)[li];
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    int bad = !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      a = fmaxf(a, __shfl_xor(a, o, 64));
+      bad |= __shfl_xor(bad, o, 64);
+    }
+    // nearest level of w / a: count midpoints m with w > m * a (exact in fp64)
+    const double ad = static_cast<double>(a);
+    double thr[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k) thr[k] = mids.m[k] * ad;
+    const float w4[4] = {v.x, v.y, v.z, v.w};
+    uint32_t nib[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double wd = static_cast<double>(w4[e]);
+      uint32_t idx = 0;
+#pragma unroll
+      for (int k = 0; k < 15; ++k) idx += (wd > thr[k]) ? 1u : 0u;
+      nib[e] = (a == 0.0f) ? 7u : idx;
+    }
+    if (b < n_blocks) {
+      const uint16_t packed =
+          static_cast<uint16_t>(nib[0] | (nib[1] << 4) | (nib[2] << 8) | (nib[3] << 12));
+      reinterpret_cast<uint16_t*>(codes + b * 32)[li] = packed;
+      if (li == 0) {
+        s_abs[local] = a;
+        s_bad[local] = bad;
+        if (!dq) static_cast<float*>(absmax_out)[b] = bad ? __builtin_nanf("") : a;
+      }
+    } else if (li == 0) {
+      s_abs[local] = 0.0f;
+      s_bad[local] = 0;
+    }
+  }
+  if (!dq) return;
+  __syncthreads();
+  // second level: s2 = group max; q = round_half_even(127 a / s2) in fp64
+  float m = s_abs[tid];
+  int bad = s_bad[tid];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o, 64));
+    bad |= __shfl_xor(bad, o, 64);
+  }
+  __shared__ float s_wmax[4];
+  __shared__ int s_wbad[4];
+  if (lane == 0) {
+    s_wmax[wave] = m;
+    s_wbad[wave] = bad;
+  }
+  __syncthreads();
+  const float s2 = fmaxf(fmaxf(s_wmax[0], s_wmax[1]), fmaxf(s_wmax[2], s_wmax[3]));
+  const int gbad = s_wbad[0] | s_wbad[1] | s_wbad[2] | s_wbad[3];
+  const int64_t b = blk0 + tid;
+  if (b < n_blocks) {
+    int8_t q = 0;
+    if (s2 > 0.0f) {
+      const double r = (127.0 * static_cast<double>(s_abs[tid])) / static_cast<double>(s2);
+      q = static_cast<int8_t>(__builtin_rint(r));
+    }
+    static_cast<int8_t*>(absmax_out)[b] = q;
+  }
+  if (tid == 0) absmax2_out[g] = gbad ? __builtin_nanf("") : s2;
+}
+
+// Group-wise asymmetric INT4: 8 lanes per group of 32, 4 weights per lane.
+__global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ W, int64_t n_groups,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint16_t* __restrict__ scale,
+                                                    uint16_t* __restrict__ zero) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t grp = t >> 3;
+  const int li = threadIdx.x & 7;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (grp < n_groups) v = reinterpret_cast<const float4*>(W + grp * 32)[li];
+  float lo = fminf(fminf(v.x, v.y), fminf(v.z, v.w));
+  float hi = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+  int bad = 0;
+  const float w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bad |= !(isfinite(w4[e]) && fabsf(w4[e]) <= 65504.0f);
+#pragma unroll
+  for (int o = 4; o > 0; o >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o, 64));
+    hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    bad |= __shfl_xor(bad, o, 64);
+  }
+  const _Float16 beta_h = static_cast<_Float16>(lo);
+  const float range = hi - lo;
+  const _Float16 alpha_h = static_cast<_Float16>(range / 15.0f);
+  const float beta = static_cast<float>(beta_h);
+  const float alpha = static_cast<float>(alpha_h);
+  uint32_t nib[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float q = 0.0f;
+    if (alpha != 0.0f) {
+      const float r = (w4[e] - beta) / alpha;
+      q = fminf(fmaxf(__builtin_rintf(r), 0.0f), 15.0f);
+    }
+    nib[e] = static_cast<uint32_t>(q);
+  }
+  if (grp < n_groups) {
+    reinterpret_cast<uint16_t*>(codes + grp * 16)[li] =
+        static_cast<uint16_t>(nib[0] | (nib[1] << 4) | (nib[2] << 8) | (nib[3] << 12));
+    if (li == 0) {
+      scale[grp] = bad ? static_cast<uint16_t>(0x7E00u) : __builtin_bit_cast(uint16_t, alpha_h);
+      zero[grp] = __builtin_bit_cast(uint16_t, beta_h);
+    }
+  }
+}
+
+// Test-only: W_bf16 through the same lookup-table decode as the fused
+// kernels.  One thread per 8 consecutive weights.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant(WeightView w, uint16_t* __restrict__ out) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = w.N * w.K / 8;
+  if (t >= total) return;
+  const int64_t e0 = t * 8;
+  const int64_t row = e0 / w.K, col = e0 % w.K;
+  const Lut16 lut = make_lut<FMT>(w, row, col / FmtTraits<FMT>::kBlock);
+  const uint32_t word = reinterpret_cast<const uint32_t*>(w.codes)[t];
+  reinterpret_cast<u32x4*>(out)[t] = lut_decode8(lut, word);
+}
+
+}  // namespace
+
+hipError_t launch_quant_nf4(const float* W, int64_t n_blocks, int dq, const double* mids15,
+                            uint8_t* codes, void* absmax, float* absmax2, hipStream_t stream) {
+  Midpoints m;
+  for (int i = 0; i < 15; ++i) m.m[i] = mids15[i];
+  const int64_t groups = (n_blocks + 255) / 256;
+  hipLaunchKernelGGL(k_quant_nf4, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, stream, W,
+                     n_blocks, dq, m, codes, absmax, absmax2);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int4(const float* W, int64_t n_groups, uint8_t* codes, uint16_t* scale,
+                             uint16_t* zero, hipStream_t stream) {
+  const int64_t threads = n_groups * 8;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_quant_int4, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, W,
+                     n_groups, codes, scale, zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const WeightView& w, int fmt, uint16_t* out, hipStream_t stream) {
+  const int64_t total = w.N * w.K / 8;
+  const int64_t blocks = (total + 255) / 256;
+  if (fmt == kFmtNF4)
+    hipLaunchKernelGGL(k_dequant<kFmtNF4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, w, out);
+  else
+    hipLaunchKernelGGL(k_dequant<kFmtINT4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, w, out);
+  return hipGetLastError();
+}
+
+}  // namespace qlin

@@ -1,0 +1,124 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+include/qlin.h declares, computes the NF4 levels on the host bit-identically
+to the oracle, sizes workspaces, and rejects bad arguments before enqueuing
+anything."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from quantized_base_rank_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlin.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libqlin.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlin_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_codebook_bit_identical_to_oracle(oracle):
+    from quantized_base_rank_amd import qlin_nf4_codebook
+    got = qlin_nf4_codebook()
+    ref = oracle.nf4_codebook()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for st in range(8):
+        assert L.qlin_status_string(st)
+    assert L.qlin_status_string(99) == b"unknown status"
+
+
+def _qw(fmt=1, block=64, dq=256, d_out=4096, d_in=4096, aligned=True):
+    p = 0x1000 if aligned else 0x1004
+    return _lib.QWeightStruct(fmt, block, dq, 0, d_out, d_in, p, p, p, p, p)
+
+
+def test_workspace_bytes_host_only():
+    L = _lib.lib()
+    for M in (1, 16, 4096):
+        n = L.qlin_workspace_bytes(ctypes.byref(_qw()), M, 16, 1)
+        assert n > 0 and n % 256 == 0
+    assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 0, 16, 1) == 0
+    assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 0, 1) == 0
+    assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 129, 1) == 0
+    # pooled adapter needs the INT4 group format with pool == group
+    assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 16, 32) == 0
+    q4 = _qw(fmt=2, block=32, dq=0, d_out=4096, d_in=11008)
+    assert L.qlin_workspace_bytes(ctypes.byref(q4), 2048, 64, 32) > 0
+
+
+def test_argument_errors_return_before_any_launch():
+    L = _lib.lib()
+    ok = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1004)
+    ws = ctypes.c_void_p(0x2000)
+    big = 1 << 40
+    qw = _qw()
+    # fwd: null input, misaligned input, bad rank, bad shape, bad pool, no workspace
+    assert L.qlin_fwd(ctypes.byref(qw), None, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 1
+    assert L.qlin_fwd(ctypes.byref(qw), bad, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 3
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, 0, 2.0, 1, ok, None, ws, big, None) == 2
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 0, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 2
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, 16, float("nan"), 1, ok, None, ws, big,
+                      None) == 2
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, 16, 2.0, 32, ok, None, ws, big, None) == 5
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, 16, 2.0, 1, ok, None, None, big, None) == 6
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, 16, None) == 6
+    assert L.qlin_fwd(None, ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 1
+    # descriptor errors
+    assert L.qlin_fwd(ctypes.byref(_qw(d_in=100)), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big,
+                      None) == 2
+    assert L.qlin_fwd(ctypes.byref(_qw(d_out=100)), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big,
+                      None) == 2
+    assert L.qlin_fwd(ctypes.byref(_qw(block=32)), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big,
+                      None) == 5
+    assert L.qlin_fwd(ctypes.byref(_qw(fmt=7)), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big,
+                      None) == 5
+    assert L.qlin_fwd(ctypes.byref(_qw(aligned=False)), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws,
+                      big, None) == 3
+    # bwd: missing gradient outputs
+    assert L.qlin_bwd(ctypes.byref(qw), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ok, None, ok, ws,
+                      big, None) == 1
+    assert L.qlin_bwd(ctypes.byref(qw), ok, 16, ok, ok, 16, 2.0, 1, None, None, ok, ok, ok, ws,
+                      big, None) == 1
+    # quantizers
+    assert L.qlin_quantize_nf4(None, 4, 64, 64, 256, ok, ok, ok, None) == 1
+    assert L.qlin_quantize_nf4(ok, 4, 64, 32, 256, ok, ok, ok, None) == 5
+    assert L.qlin_quantize_nf4(ok, 4, 96, 64, 256, ok, ok, ok, None) == 2
+    assert L.qlin_quantize_nf4(ok, 4, 64, 64, 128, ok, ok, ok, None) == 5
+    assert L.qlin_quantize_nf4(ok, 4, 64, 64, 256, ok, ok, None, None) == 1
+    assert L.qlin_quantize_nf4(bad, 4, 64, 64, 256, ok, ok, ok, None) == 3
+    assert L.qlin_quantize_int4_group(ok, 4, 64, 64, ok, ok, ok, None) == 5
+    assert L.qlin_quantize_int4_group(ok, 4, 48, 32, ok, ok, ok, None) == 2
+    assert L.qlin_quantize_int4_group(ok, 4, 64, 32, ok, None, ok, None) == 1
+    # dequant helper
+    assert L.qlin_dequant_bf16(ctypes.byref(qw), None, None) == 1
+    assert L.qlin_nf4_codebook(None) == 1
+
+
+def test_binding_raises_without_library(monkeypatch):
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libqlin.so")
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()
