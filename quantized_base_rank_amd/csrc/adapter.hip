@@ -42,16 +42,32 @@ __global__ __launch_bounds__(256) void k_nt_skinny(NtArgs a) {
 
   const int64_t mrow = m0 + l32 < a.M ? m0 + l32 : a.M - 1;
   const uint16_t* xrow = a.X + mrow * a.ldx;
-  for (int64_t st = s_begin + wave; st < s_end; st += 4) {
-    const int64_t k = st * 16 + h * 8;
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(xrow + k);
+  // each wave keeps kNtU k16 steps of loads in flight
+  constexpr int kNtU = 4;
+  for (int64_t st0 = s_begin + wave * kNtU; st0 < s_end; st0 += 4 * kNtU) {
+    u32x4 xa[kNtU], yb[kNtU][4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (q < jsub) {
+    for (int u = 0; u < kNtU; ++u) {
+      const int64_t st = st0 + u < s_end ? st0 + u : s_end - 1;
+      const int64_t k = st * 16 + h * 8;
+      xa[u] = *reinterpret_cast<const u32x4*>(xrow + k);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         const int j = q * 32 + l32;
-        u32x4 yb = u32x4{0, 0, 0, 0};
-        if (j < a.J) yb = *reinterpret_cast<const u32x4*>(a.Y + static_cast<int64_t>(j) * a.ldy + k);
-        acc[q] = mfma32(xa, yb, acc[q]);
+        const int jc = j < a.J ? j : a.J - 1;
+        yb[u][q] = u32x4{0, 0, 0, 0};
+        if (q < jsub) {  // uniform
+          const u32x4 d = *reinterpret_cast<const u32x4*>(a.Y + static_cast<int64_t>(jc) * a.ldy + k);
+          if (j < a.J) yb[u][q] = d;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kNtU; ++u) {
+      if (st0 + u < s_end) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < jsub) acc[q] = mfma32(xa[u], yb[u][q], acc[q]);
       }
     }
   }
@@ -77,20 +93,20 @@ __global__ __launch_bounds__(256) void k_nt_skinny(NtArgs a) {
   float* part = a.partial + (static_cast<int64_t>(tile) * a.splits + split) * (4 * 16 * 64);
   if (a.splits > 1) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part[(q * 16 + e) * 64 + lane] = sum[e];
-    __threadfence();
-    __syncthreads();
+    for (int e = 0; e < 16; ++e) st_sys(part + (q * 16 + e) * 64 + lane, sum[e]);
     __shared__ uint32_t s_ticket;
-    if (tid == 0) s_ticket = atomicAdd(a.counters + tile, 1u);
-    __syncthreads();
-    if (s_ticket != static_cast<uint32_t>(a.splits - 1)) return;
-    __threadfence();
+    if (publish_and_ticket(a.counters + tile, &s_ticket) != static_cast<uint32_t>(a.splits - 1))
+      return;
     const float* base = a.partial + static_cast<int64_t>(tile) * a.splits * (4 * 16 * 64);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = 0.0f;
-      for (int sp = 0; sp < a.splits; ++sp) v += __builtin_nontemporal_load(base + sp * (4 * 16 * 64) + (q * 16 + e) * 64 + lane);
-      sum[e] = v;
+    for (int e = 0; e < 16; ++e) sum[e] = 0.0f;
+    for (int sp = 0; sp < a.splits; ++sp) {
+      float v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        v[e] = ld_sys(base + sp * (4 * 16 * 64) + (q * 16 + e) * 64 + lane);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum[e] += v[e];
     }
     if (tid == 0) a.counters[tile] = 0u;
   }
@@ -201,24 +217,27 @@ __global__ __launch_bounds__(256) void k_tn_skinny(TnArgs a) {
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) part[((wave * 2 + qq) * 16 + e) * 64 + lane] = sum[qq][e];
-    __threadfence();
-    __syncthreads();
+      for (int e = 0; e < 16; ++e) st_sys(part + ((wave * 2 + qq) * 16 + e) * 64 + lane, sum[qq][e]);
     __shared__ uint32_t s_ticket;
-    if (tid == 0) s_ticket = atomicAdd(a.counters + tile, 1u);
-    __syncthreads();
-    if (s_ticket != static_cast<uint32_t>(a.splits - 1)) return;
-    __threadfence();
+    if (publish_and_ticket(a.counters + tile, &s_ticket) != static_cast<uint32_t>(a.splits - 1))
+      return;
     const float* base = a.partial + static_cast<int64_t>(tile) * a.splits * kPart;
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = 0.0f;
-        for (int sp = 0; sp < a.splits; ++sp)
-          v += __builtin_nontemporal_load(base + sp * kPart + ((wave * 2 + qq) * 16 + e) * 64 + lane);
-        sum[qq][e] = v;
-      }
+      for (int e = 0; e < 16; ++e) sum[qq][e] = 0.0f;
+    for (int sp = 0; sp < a.splits; ++sp) {
+      float v[2][16];
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          v[qq][e] = ld_sys(base + sp * kPart + ((wave * 2 + qq) * 16 + e) * 64 + lane);
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum[qq][e] += v[qq][e];
+    }
     if (tid == 0) a.counters[tile] = 0u;
   }
   // D[p][j]: lane holds D[8i + 4h + t][l32]

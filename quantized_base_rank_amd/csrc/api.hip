@@ -110,11 +110,13 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   const int64_t N = w->d_out, K = w->d_in, G = K / pool;
   p.small = M <= kSmallM;
   // adapter reductions: aim for ~512 workgroups, each with enough work
-  p.nt_splits_u = static_cast<int>(clamp64(512 / nt_tiles(M), 1, std::max<int64_t>(1, K / 16 / 8)));
-  p.nt_splits_du = static_cast<int>(clamp64(512 / nt_tiles(M), 1, std::max<int64_t>(1, N / 16 / 8)));
+  // ~512 workgroups for large problems, but never fewer than 64 k16 steps
+  // (NT) or 4 token steps (TN) per workgroup
+  p.nt_splits_u = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), K / 16 / 64), 1, 64));
+  p.nt_splits_du = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), N / 16 / 64), 1, 64));
   const int64_t msteps = ceil_div(M, 32);
-  p.tn_splits_dB = static_cast<int>(clamp64(512 / tn_tiles(N), 1, std::max<int64_t>(1, msteps / 2)));
-  p.tn_splits_dA = static_cast<int>(clamp64(512 / tn_tiles(K), 1, std::max<int64_t>(1, msteps / 2)));
+  p.tn_splits_dB = static_cast<int>(clamp64(std::min<int64_t>(1024 / tn_tiles(N), msteps / 4), 1, 64));
+  p.tn_splits_dA = static_cast<int>(clamp64(std::min<int64_t>(1024 / tn_tiles(K), msteps / 4), 1, 64));
   if (!p.small) {
     const int tiles = fwd_gemm_tiles(M, N);
     if (tiles < 192) p.fwd_splits = static_cast<int>(clamp64(ceil_div(256, tiles), 1, std::max<int64_t>(1, ceil_div(K, 128) / 4)));
@@ -129,7 +131,9 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
                                        tn_partial_floats(N, p.tn_splits_dB),
                                        tn_partial_floats(K, p.tn_splits_dA)});
   if (p.small) {
-    partial = std::max<int64_t>({partial, gemv_fwd_partial_floats(N, K), gemv_dx_partial_floats(N, K)});
+    partial = std::max<int64_t>({partial,
+                                 gemv_fwd_partial_floats(N, K),
+                                 gemv_dx_partial_floats(N, K) + gemv_dx_dupart_floats(N, K, r)});
   } else {
     partial = std::max<int64_t>(partial, fwd_gemm_partial_floats(M, N, p.fwd_splits));
   }
@@ -272,14 +276,21 @@ int qlin_fwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   const int fmt = fmt_of(w);
   float* u = u_out != nullptr ? u_out : ws_at<float>(workspace, p.off_u);
   const bool adapter = s != 0.0f;
-  if (adapter || u_out != nullptr) {
+  // the few-token kernel forms u itself for a plain adapter of rank <= 16
+  const bool fuse_u = p.small && pool == 1 && r <= 16;
+  if (!fuse_u && (adapter || u_out != nullptr)) {
     st = compute_u(w, x, M, A, r, pool, u, p, workspace, stream);
     if (st != QLIN_OK) return st;
   }
   if (p.small) {
     GemvFwdArgs a{};
-    a.w = v; a.x = x; a.M = M; a.B = B; a.u = adapter ? u : nullptr; a.r = r; a.s = s; a.y = y;
-    a.splits = p.gf_splits;
+    a.w = v; a.x = x; a.M = M; a.A = A; a.B = B; a.r = r; a.s = s;
+    a.adapter = adapter ? 1 : 0;
+    a.fuse_u = (fuse_u && (adapter || u_out != nullptr)) ? 1 : 0;
+    a.u_in = u;
+    a.y = y; a.u_out = u_out;
+    a.splits = gemv_fwd_splits(w->d_in);
+    a.kshare = gemv_fwd_kshare(w->d_in);
     a.partial = ws_at<float>(workspace, p.off_partial);
     a.counters = ws_at<uint32_t>(workspace, p.off_counters);
     return hip_status(launch_gemv_fwd(a, fmt, stream));
@@ -325,6 +336,17 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     if (st != QLIN_OK) return st;
     u = uw;
   }
+  if (p.small) {
+    // one launch: du, dB, dA and dX folded into the weight-streaming kernel
+    GemvDxArgs a{};
+    a.w = v; a.x = x; a.dy = dy; a.M = M; a.A = A; a.B = B; a.u = u; a.r = r; a.pool = pool;
+    a.pool_shift = __builtin_ctz(static_cast<unsigned>(pool)); a.s = s;
+    a.dx = dx; a.dA = dA; a.dB = dB; a.splits = p.gd_splits;
+    a.partial = partial;
+    a.du_part = partial + gemv_dx_partial_floats(N, K);
+    a.counters = counters;
+    return hip_status(launch_gemv_dx(a, fmt, stream));
+  }
   // du = s dY B  (B^T staged so both operands are contiguous along n)
   QLIN_TRY(launch_transpose16(B, N, r, Bt, stream));
   {
@@ -366,14 +388,6 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   }
   if (dx == nullptr) return QLIN_OK;
   // dX = dY W_bf16 + du A
-  if (p.small) {
-    GemvDxArgs a{};
-    a.w = v; a.dy = dy; a.M = M; a.A = A; a.du = pool == 1 ? du : nullptr; a.r = r;
-    a.Gq = Gq; a.pool = pool; a.pool_shift = __builtin_ctz(static_cast<unsigned>(pool));
-    a.dx = dx; a.splits = p.gd_splits;
-    a.partial = partial; a.counters = counters;
-    return hip_status(launch_gemv_dx(a, fmt, stream));
-  }
   uint16_t* At = nullptr;
   if (pool == 1) {
     At = ws_at<uint16_t>(workspace, p.off_At);

@@ -228,6 +228,129 @@ struct FmtTraits<kFmtINT4> {
   static constexpr int kBlock = 32;
 };
 
+// ------------------------------------------------------- transposed LDS read
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16.  Within each group of 16 lanes, lane p supplies the
+// LDS address of four consecutive 16-bit elements; lane t = 4a + b receives
+// element b of the chunks supplied by lanes a, a + 4, a + 8, a + 12, in that
+// order.  So when lane p points at row kbase + p/4, columns c0 + 4(p%4) ..
+// +3 of a row-major tile, lane t receives rows kbase .. kbase+3 of column
+// c0 + t: four consecutive reduction elements of one operand row, read from a
+// tile stored with the reduction index as its row.
+__device__ __forceinline__ u32x2 ds_read_tr16(const void* lds_addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_addr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand (8 consecutive reduction rows kbase..kbase+7 of column c0 + t)
+// from a row-major bf16 LDS tile with `stride` bytes per row.  `p` is the
+// lane index within its 16-lane group.
+__device__ __forceinline__ u32x4 tr16_operand(const uint8_t* tile, int stride, int kbase, int c0,
+                                              int p) {
+  const uint8_t* a0 = tile + (kbase + (p >> 2)) * stride + (c0 + 4 * (p & 3)) * 2;
+  const u32x2 lo = ds_read_tr16(a0);
+  const u32x2 hi = ds_read_tr16(a0 + 4 * stride);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Raw decode parameters of one (row, 64-element block), loaded ahead of use
+// so that the loads overlap other work; luts_from_params builds the tables.
+// NF4: a = 8-bit code (dq) or fp32 absmax bits, b = fp32 s2 bits (dq).
+// INT4: a, b = (scale | zero << 16) of the block's two 32-element groups.
+struct BlockParams {
+  uint32_t a, b;
+};
+
+template <int FMT>
+__device__ __forceinline__ BlockParams load_block_params(const WeightView& w, int64_t row,
+                                                         int64_t blk64, bool valid) {
+  BlockParams p{0u, 0u};
+  (void)valid;  // indices are clamped by the caller; the loads are unconditional
+  if (FMT == kFmtNF4) {
+    const int64_t b = row * (w.K >> 6) + blk64;
+    if (w.dq) {
+      p.a = static_cast<uint32_t>(static_cast<int32_t>(static_cast<const int8_t*>(w.absmax)[b]));
+      p.b = __float_as_uint(w.absmax2[b >> 8]);
+    } else {
+      p.a = __float_as_uint(static_cast<const float*>(w.absmax)[b]);
+    }
+  } else {
+    const int64_t g = row * (w.K >> 5) + 2 * blk64;
+    p.a = static_cast<uint32_t>(w.scale[g]) | (static_cast<uint32_t>(w.zero[g]) << 16);
+    p.b = static_cast<uint32_t>(w.scale[g + 1]) | (static_cast<uint32_t>(w.zero[g + 1]) << 16);
+  }
+  return p;
+}
+
+// lut[0] decodes elements 0..31 of the block, lut[1] elements 32..63.
+template <int FMT>
+__device__ __forceinline__ void luts_from_params(const WeightView& w, BlockParams p,
+                                                 Lut16 (&lut)[2]) {
+  if (FMT == kFmtNF4) {
+    const float sc = w.dq ? nf4_dq_scale(static_cast<int8_t>(p.a), __uint_as_float(p.b))
+                          : __uint_as_float(p.a);
+    lut[0] = lut_nf4(w.cb, sc);
+    lut[1] = lut[0];
+  } else {
+    lut[0] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.a & 0xFFFFu)),
+                      half_bits_to_f32(static_cast<uint16_t>(p.a >> 16)));
+    lut[1] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.b & 0xFFFFu)),
+                      half_bits_to_f32(static_cast<uint16_t>(p.b >> 16)));
+  }
+}
+
+// ------------------------------------------- split reductions across workgroups
+// Partial sums that another workgroup (possibly on another XCD, with its own
+// L2) will read are written through to device-coherent memory (sc0 sc1
+// stores) and read back the same way, so publishing them needs only a wait
+// for the stores' acknowledgements, not a write-back of the whole L2.
+
+__device__ __forceinline__ void st_sys(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float ld_sys(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_sys4(float* p, f32x4 v) {
+  st_sys(p, v[0]);
+  st_sys(p + 1, v[1]);
+  st_sys(p + 2, v[2]);
+  st_sys(p + 3, v[3]);
+}
+__device__ __forceinline__ f32x4 ld_sys4(const float* p) {
+  return f32x4{ld_sys(p), ld_sys(p + 1), ld_sys(p + 2), ld_sys(p + 3)};
+}
+
+// Wide (16-byte) write-through stores and coherent loads through a buffer
+// resource: buffer_{store,load}_dwordx4 with sc0 sc1.  `off` is a byte offset
+// from the (wave-uniform) base; buffers are < 2 GiB.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+constexpr int kCoherent = 1 | 16;  // sc0 | sc1
+__device__ __forceinline__ void st_sys16(rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 ld_sys16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+
+// Waits until this workgroup's write-through stores are acknowledged, then
+// takes a ticket on `counter` (one per output tile).  Returns the ticket in
+// every thread; the workgroup that draws splits - 1 is the last one.
+__device__ __forceinline__ uint32_t publish_and_ticket(uint32_t* counter, uint32_t* s_ticket) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  return *s_ticket;
+}
+
 // ------------------------------------------------------------- misc helpers
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -100,17 +100,15 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     for (int r = 0; r < 2; ++r) {
       const int64_t n = st * kNS + 2 * p + r;
       rvalid[r] = kvalid && n < N;
+      // unconditional loads from clamped addresses; invalid rows are masked at decode
       const int64_t nc = n < N ? n : N - 1;
       const int64_t kc = kvalid ? kcol : 0;
-      cw[r] = rvalid[r] ? *reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (kc >> 1))
-                        : u32x4{0, 0, 0, 0};
+      cw[r] = *reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (kc >> 1));
       if constexpr (FMT == kFmtNF4) {
-        prm.scale[r] = rvalid[r] ? nf4_block_scale(a.w, nc * (K >> 6) + (kc >> 6)) : 0.0f;
+        prm.scale[r] = nf4_block_scale(a.w, nc * (K >> 6) + (kc >> 6));
       } else {
         const int64_t gi = nc * (K >> 5) + (kc >> 5);
-        prm.sz[r] = rvalid[r] ? (static_cast<uint32_t>(a.w.scale[gi]) |
-                                 (static_cast<uint32_t>(a.w.zero[gi]) << 16))
-                              : 0u;
+        prm.sz[r] = static_cast<uint32_t>(a.w.scale[gi]) | (static_cast<uint32_t>(a.w.zero[gi]) << 16);
       }
     }
   };

@@ -149,18 +149,14 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   StepParams<FMT> pc, pn;
   auto load_codes = [&](int64_t ks, u32x4 (&c)[2][2], StepParams<FMT>& p) {
     const int64_t kk = ks * kKS + h * 64;
-    const bool valid = kk < K;
-    const int64_t off = kk >> 1;
-    if (valid) {
-      c[0][0] = *reinterpret_cast<const u32x4*>(crow0 + off);
-      c[0][1] = *reinterpret_cast<const u32x4*>(crow0 + off + 16);
-      c[1][0] = *reinterpret_cast<const u32x4*>(crow1 + off);
-      c[1][1] = *reinterpret_cast<const u32x4*>(crow1 + off + 16);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 2; ++r) c[r][0] = c[r][1] = u32x4{0, 0, 0, 0};
-    }
-    load_params<FMT>(a.w, nr, kk >> 6, valid, p);
+    // unconditional loads (clamped past the K tail; that half is masked at decode)
+    const int64_t kc = kk < K ? kk : K - 64;
+    const int64_t off = kc >> 1;
+    c[0][0] = *reinterpret_cast<const u32x4*>(crow0 + off);
+    c[0][1] = *reinterpret_cast<const u32x4*>(crow0 + off + 16);
+    c[1][0] = *reinterpret_cast<const u32x4*>(crow1 + off);
+    c[1][1] = *reinterpret_cast<const u32x4*>(crow1 + off + 16);
+    load_params<FMT>(a.w, nr, kc >> 6, true, p);
   };
 
   load_x(ks0, 0);
@@ -266,13 +262,9 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) part[((r * 8 + ms) * 16 + v) * 256 + tid] = acc[r][ms][v];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_ticket = atomicAdd(a.counters + tmn, 1u);
-    __syncthreads();
-    if (s_ticket != static_cast<uint32_t>(a.splits - 1)) return;
-    __threadfence();
+        for (int v = 0; v < 16; ++v) st_sys(part + ((r * 8 + ms) * 16 + v) * 256 + tid, acc[r][ms][v]);
+    if (publish_and_ticket(a.counters + tmn, &s_ticket) != static_cast<uint32_t>(a.splits - 1))
+      return;
     const float* base = a.partial + static_cast<int64_t>(tmn) * a.splits * (kTM * kTN);
 #pragma unroll
     for (int r = 0; r < 2; ++r)
@@ -282,8 +274,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
         for (int v = 0; v < 16; ++v) {
           float sum = 0.0f;
           for (int s2 = 0; s2 < a.splits; ++s2)
-            sum += __builtin_nontemporal_load(base + s2 * (kTM * kTN) +
-                                              ((r * 8 + ms) * 16 + v) * 256 + tid);
+            sum += ld_sys(base + s2 * (kTM * kTN) + ((r * 8 + ms) * 16 + v) * 256 + tid);
           acc[r][ms][v] = sum;
         }
     if (tid == 0) a.counters[tmn] = 0u;

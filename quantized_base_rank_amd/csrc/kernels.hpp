@@ -101,43 +101,54 @@ struct DxArgs {
 };
 hipError_t launch_dx_gemm(const DxArgs& a, int fmt, hipStream_t stream);
 
-// Small-M (M <= 16) weight-streaming kernels, split along the reduction.
+// Few-token (M <= 16) weight-streaming kernels, one launch per pass; the
+// adapter terms are folded into the split reductions.
 struct GemvFwdArgs {
   WeightView w;
   const uint16_t* x;   // [M][K]
   int64_t M;           // 1..16
+  const uint16_t* A;   // [r][K/pool]
   const uint16_t* B;   // [N][r]
-  const float* u;      // [M][r] or nullptr
   int32_t r;
   float s;
+  int32_t adapter;     // 1: add s u B^T
+  int32_t fuse_u;      // 1: form u = x A^T here (plain adapter, r <= 16)
+  const float* u_in;   // [M][r] when the adapter is on and u is not formed here
   uint16_t* y;         // [M][N]
-  int32_t splits;      // K split
-  float* partial;      // [splits][16][N]
-  uint32_t* counters;  // [N / 64]
+  float* u_out;        // [M][r] or nullptr (written when fuse_u)
+  int32_t splits;      // gemv_fwd_splits(K)
+  int64_t kshare;      // gemv_fwd_kshare(K)
+  float* partial;      // gemv_fwd_partial_floats (splits > 1)
+  uint32_t* counters;  // gemv_fwd_tiles
 };
 hipError_t launch_gemv_fwd(const GemvFwdArgs& a, int fmt, hipStream_t stream);
 int gemv_fwd_splits(int64_t K);
-int64_t gemv_fwd_partial_floats(int64_t N, int64_t K);
 int gemv_fwd_tiles(int64_t N);
+int64_t gemv_fwd_kshare(int64_t K);
+int64_t gemv_fwd_partial_floats(int64_t N, int64_t K);
 
 struct GemvDxArgs {
   WeightView w;
+  const uint16_t* x;   // [M][K]
   const uint16_t* dy;  // [M][N]
   int64_t M;           // 1..16
-  const uint16_t* A;   // [r][K/pool] adapter A (natural layout)
-  const float* du;     // [M][r] or nullptr
-  int32_t r;
-  const float* Gq;     // [M][K/pool] or nullptr
-  int32_t pool;        // power of two
-  int32_t pool_shift;  // log2(pool)
-  uint16_t* dx;        // [M][K]
+  const uint16_t* A;   // [r][K/pool]
+  const uint16_t* B;   // [N][r]
+  const float* u;      // [M][r]
+  int32_t r, pool, pool_shift;
+  float s;
+  uint16_t* dx;        // [M][K] or nullptr
+  uint16_t* dA;        // [r][K/pool]
+  uint16_t* dB;        // [N][r]
   int32_t splits;      // N split
-  float* partial;      // [splits][16][K]
-  uint32_t* counters;  // [K / kGemvDxCols]
+  float* partial;      // gemv_dx_partial_floats
+  float* du_part;      // gemv_dx_dupart_floats
+  uint32_t* counters;  // gemv_dx_tiles
 };
 hipError_t launch_gemv_dx(const GemvDxArgs& a, int fmt, hipStream_t stream);
 int gemv_dx_splits(int64_t N);
-int64_t gemv_dx_partial_floats(int64_t N, int64_t K);
 int gemv_dx_tiles(int64_t K);
+int64_t gemv_dx_partial_floats(int64_t N, int64_t K);
+int64_t gemv_dx_dupart_floats(int64_t N, int64_t K, int r);
 
 }  // namespace qlin

@@ -37,11 +37,19 @@ __global__ __launch_bounds__(256) void k_quant_nf4(const float* __restrict__ W, 
   const int64_t g = blockIdx.x;
   const int64_t blk0 = g * 256;
 
+  // issue all 16 loads of this wave's 64 blocks before using any of them
+  float4 vin[16];
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int64_t b = blk0 + wave * 64 + it * 4 + sub;
+    vin[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (b < n_blocks) vin[it] = reinterpret_cast<const float4*>(W + b * 64)[li];
+  }
+#pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int local = wave * 64 + it * 4 + sub;  // block within the group
     const int64_t b = blk0 + local;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (b < n_blocks) v = reinterpret_cast<const float4*>(W + b * 64)[li];
+    const float4 v = vin[it];
     float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     int bad = !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
 #pragma unroll
