@@ -258,7 +258,8 @@ __device__ __forceinline__ u32x4 tr16_operand(const uint8_t* tile, int stride, i
 
 // Raw decode parameters of one (row, 64-element block), loaded ahead of use
 // so that the loads overlap other work; luts_from_params builds the tables.
-// NF4: a = 8-bit code (dq) or fp32 absmax bits, b = fp32 s2 bits (dq).
+// NF4: a = the 8-bit code (meaningful with DQ), b = fp32 bits of the group
+// constant s2 (DQ) or of the block absmax (no DQ).
 // INT4: a, b = (scale | zero << 16) of the block's two 32-element groups.
 struct BlockParams {
   uint32_t a, b;
@@ -270,13 +271,20 @@ __device__ __forceinline__ BlockParams load_block_params(const WeightView& w, in
   BlockParams p{0u, 0u};
   (void)valid;  // indices are clamped by the caller; the loads are unconditional
   if (FMT == kFmtNF4) {
+    // Branch-free: both loads are issued for either layout, from addresses
+    // that are in bounds for both (byte b of an fp32 absmax array; element
+    // b of it, or the group constant), and the result is selected after.
+    // A branch here lets the compiler pull the scale arithmetic next to the
+    // loads, which then waits for every load issued before them.
     const int64_t b = row * (w.K >> 6) + blk64;
-    if (w.dq) {
-      p.a = static_cast<uint32_t>(static_cast<int32_t>(static_cast<const int8_t*>(w.absmax)[b]));
-      p.b = __float_as_uint(w.absmax2[b >> 8]);
-    } else {
-      p.a = __float_as_uint(static_cast<const float*>(w.absmax)[b]);
-    }
+    const float* wide = w.dq ? w.absmax2 + (b >> 8) : static_cast<const float*>(w.absmax) + b;
+    const uint32_t q8 =
+        static_cast<uint32_t>(static_cast<int32_t>(static_cast<const int8_t*>(w.absmax)[b]));
+    // kept raw (no select on the loaded values, which would wait for them):
+    // a = the 8-bit code (used with DQ), b = the fp32 group constant (DQ)
+    // or the fp32 block absmax (no DQ)
+    p.a = q8;
+    p.b = __float_as_uint(*wide);
   } else {
     const int64_t g = row * (w.K >> 5) + 2 * blk64;
     p.a = static_cast<uint32_t>(w.scale[g]) | (static_cast<uint32_t>(w.zero[g]) << 16);
@@ -285,14 +293,18 @@ __device__ __forceinline__ BlockParams load_block_params(const WeightView& w, in
   return p;
 }
 
+// NF4 block scale from raw block constants (computed where the table is
+// built, not where the constants are loaded).
+__device__ __forceinline__ float nf4_params_scale(const WeightView& w, BlockParams p) {
+  return w.dq ? nf4_dq_scale(static_cast<int8_t>(p.a), __uint_as_float(p.b)) : __uint_as_float(p.b);
+}
+
 // lut[0] decodes elements 0..31 of the block, lut[1] elements 32..63.
 template <int FMT>
 __device__ __forceinline__ void luts_from_params(const WeightView& w, BlockParams p,
                                                  Lut16 (&lut)[2]) {
   if (FMT == kFmtNF4) {
-    const float sc = w.dq ? nf4_dq_scale(static_cast<int8_t>(p.a), __uint_as_float(p.b))
-                          : __uint_as_float(p.a);
-    lut[0] = lut_nf4(w.cb, sc);
+    lut[0] = lut_nf4(w.cb, nf4_params_scale(w, p));
     lut[1] = lut[0];
   } else {
     lut[0] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.a & 0xFFFFu)),

@@ -43,7 +43,7 @@ template <int FMT>
 struct DxParams;
 template <>
 struct DxParams<kFmtNF4> {
-  float scale[2];
+  BlockParams bp[2];  // raw: the scale is formed when the table is built
 };
 template <>
 struct DxParams<kFmtINT4> {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
       const int64_t kc = kvalid ? kcol : 0;
       cw[r] = *reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (kc >> 1));
       if constexpr (FMT == kFmtNF4) {
-        prm.scale[r] = nf4_block_scale(a.w, nc * (K >> 6) + (kc >> 6));
+        prm.bp[r] = load_block_params<kFmtNF4>(a.w, nc, kc >> 6, true);
       } else {
         const int64_t gi = nc * (K >> 5) + (kc >> 5);
         prm.sz[r] = static_cast<uint32_t>(a.w.scale[gi]) | (static_cast<uint32_t>(a.w.zero[gi]) << 16);
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       if constexpr (FMT == kFmtNF4)
-        lut[r] = lut_nf4(a.w.cb, prm.scale[r]);
+        lut[r] = lut_nf4(a.w.cb, nf4_params_scale(a.w, prm.bp[r]));
       else
         lut[r] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(prm.sz[r] & 0xFFFFu)),
                           half_bits_to_f32(static_cast<uint16_t>(prm.sz[r] >> 16)));

@@ -43,7 +43,7 @@ template <int FMT>
 struct StepParams;
 template <>
 struct StepParams<kFmtNF4> {
-  float scale[2];  // per row
+  BlockParams bp[2];  // per row, raw: the scale is formed when the table is built
 };
 template <>
 struct StepParams<kFmtINT4> {
@@ -58,9 +58,9 @@ template <>
 __device__ __forceinline__ void load_params<kFmtNF4>(const WeightView& w, const int64_t (&nr)[2],
                                                      int64_t kblk, bool valid,
                                                      StepParams<kFmtNF4>& p) {
+  (void)valid;  // indices are in range; invalid blocks are masked at decode
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
-    p.scale[r] = valid ? nf4_block_scale(w, nr[r] * (w.K >> 6) + kblk) : 0.0f;
+  for (int r = 0; r < 2; ++r) p.bp[r] = load_block_params<kFmtNF4>(w, nr[r], kblk, true);
 }
 
 template <>
@@ -84,7 +84,7 @@ __device__ __forceinline__ Lut16 step_lut(const WeightView& w, const StepParams<
 template <>
 __device__ __forceinline__ Lut16 step_lut<kFmtNF4>(const WeightView& w,
                                                    const StepParams<kFmtNF4>& p, int r, int) {
-  return lut_nf4(w.cb, p.scale[r]);
+  return lut_nf4(w.cb, nf4_params_scale(w, p.bp[r]));
 }
 template <>
 __device__ __forceinline__ Lut16 step_lut<kFmtINT4>(const WeightView&,

@@ -42,18 +42,71 @@ constexpr int kGfChunk = 256;
 constexpr int kGfKShare = 4096;  // K per workgroup at most (bounds activation re-reads)
 constexpr int kGfWaves = 8;
 constexpr int kGfPerWave = kGfKShare / kGfChunk / kGfWaves;  // chunks per wave (2)
+constexpr int kGfSlot = kGfRows * kGfChunk * 2;               // one staged chunk: 8 KB
 
-struct FwdChunk {
-  u32x4 cw[2];
-  BlockParams bp;
-  u32x4 xf[8];
-  u32x4 af[8];
-};
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Stage a [16][256] bf16 chunk (rows `src` + row * ld, columns k0..k0+255)
+// into an 8 KB LDS slot with direct-to-LDS loads.  Each load instruction
+// covers two rows of 512 B, whole 128 B lines per run of lanes.  A row's
+// 16-byte pieces are XOR-swizzled by the row index so that the fragment
+// reads below hit 16 distinct bank groups.  Rows past `rows` repeat the last
+// row and columns past `kmax` repeat the last valid piece (both are masked
+// or discarded by the caller).
+__device__ __forceinline__ void stage_chunk(const uint16_t* src, int64_t ld, int rows, int64_t k0,
+                                            int64_t kmax, uint8_t* slot, int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int row = 2 * t + (lane >> 5);
+    const int q = (lane & 31) ^ (row & 15);
+    const int64_t rc = row < rows ? row : rows - 1;
+    int64_t k = k0 + q * 8;
+    k = k < kmax ? k : kmax - 8;
+    __builtin_amdgcn_global_load_lds(src + rc * ld + k, (lds_ptr_t)(slot + t * 1024), 16, 0, 0);
+  }
+}
+
+// MFMA fragment of a staged chunk: row l16, logical piece q (8 bf16).
+__device__ __forceinline__ u32x4 chunk_frag(const uint8_t* slot, int l16, int q) {
+  return *reinterpret_cast<const u32x4*>(slot + l16 * 512 + ((q ^ l16) << 4));
+}
+
+// Packed codes of a [16 rows][256 columns] chunk for lane (l16, g): the 32
+// bytes of row l16, block g.  They are loaded as whole 128 B row segments
+// (lane L reads row 8j + L/8, bytes 16 (L%8) .. +16 for j = 0, 1) and moved
+// to their lane with ds_bpermute.
+__device__ __forceinline__ void load_chunk_codes(const uint8_t* codes, int64_t ldc, int64_t n0,
+                                                 int64_t N, int64_t byte0, int64_t bmax, int lane,
+                                                 u32x4 (&raw)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int64_t n = n0 + 8 * j + (lane >> 3);
+    n = n < N ? n : N - 1;
+    int64_t b = byte0 + (lane & 7) * 16;
+    b = b < bmax ? b : bmax - 16;
+    raw[j] = *reinterpret_cast<const u32x4*>(codes + n * ldc + b);
+  }
+}
+__device__ __forceinline__ void route_chunk_codes(const u32x4 (&raw)[2], int l16, int g,
+                                                  u32x4 (&cw)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int src = (((l16 & 7) << 3) | (2 * g + h)) << 2;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t v0 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(raw[0][d]));
+      const uint32_t v1 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(raw[1][d]));
+      cw[h][d] = (l16 >> 3) ? v1 : v0;
+    }
+  }
+}
 
 template <int FMT, bool FUSE_U>
 __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
-  __shared__ float s_y[kGfWaves][256];
-  __shared__ float s_u[kGfWaves][256];
+  // per wave: two 8 KB slots (token chunks i = 0, 1; or, with u fused, the
+  // token and adapter chunk of one round); after the products the first
+  // 2 KB of a wave's slots hold its partial y and u
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kGfWaves][2 * kGfSlot];
   __shared__ float s_fu[16 * 128];       // final u [16][r]
   __shared__ uint16_t s_b[16 * 128];     // B rows of this tile [16][r]
   __shared__ uint32_t s_ticket;
@@ -69,10 +122,23 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
   const int64_t krlen = K - kr0 < a.kshare ? K - kr0 : a.kshare;
   const int nch = static_cast<int>((krlen + kGfChunk - 1) / kGfChunk);
   const int64_t n0 = static_cast<int64_t>(tile) * kGfRows;
+  uint8_t* slot0 = s_stage[wave];
+  uint8_t* slot1 = s_stage[wave] + kGfSlot;
 
-  // adapter operands of the epilogue, issued first (small, L2-resident)
-  uint32_t breg[8];
-  float ureg[8];
+  // chunks of this wave (clamped; a chunk past the share is fully masked)
+  int cc[kGfPerWave];
+  bool live[kGfPerWave];
+#pragma unroll
+  for (int i = 0; i < kGfPerWave; ++i) {
+    const int c = wave + i * kGfWaves;
+    live[i] = c < nch;
+    cc[i] = c < nch ? c : nch - 1;
+  }
+  auto chunk_k0 = [&](int i) { return kr0 + static_cast<int64_t>(cc[i]) * kGfChunk; };
+
+  // (1) adapter operands of the epilogue (small, L2-resident)
+  uint32_t breg[4];
+  float ureg[4];
   if (a.adapter) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -86,56 +152,69 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
       }
     }
   }
-
+  // (2) token (and adapter) chunks straight into LDS
+  const int mrows = static_cast<int>(M < 16 ? M : 16);
+  const int arows = r < 16 ? r : 16;
+  stage_chunk(a.x, K, mrows, chunk_k0(0), K, slot0, lane);
+  if (FUSE_U)
+    stage_chunk(a.A, K, arows, chunk_k0(0), K, slot1, lane);
+  else
+    stage_chunk(a.x, K, mrows, chunk_k0(1), K, slot1, lane);
+  // (3) packed codes and block constants of both chunks (HBM stream)
   const int64_t rowc = n0 + l16 < N ? n0 + l16 : N - 1;
-  const uint8_t* crow = a.w.codes + rowc * (K >> 1);
-  const uint16_t* xrow = a.x + (l16 < M ? l16 : M - 1) * K;
-  const uint16_t* arow = a.A + static_cast<int64_t>(l16 < r ? l16 : r - 1) * K;
-
-  // one 256-wide chunk: this lane's row, block g; loads are unconditional
-  // (clamped), invalid blocks are masked at use
-  auto load = [&](int c, FwdChunk& d, bool& valid) {
-    const int64_t kl = static_cast<int64_t>(c) * kGfChunk + g * 64;
-    valid = kl < krlen;
-    const int64_t kb = kr0 + (valid ? kl : 0);
+  u32x4 raw[kGfPerWave][2];
+  BlockParams bp[kGfPerWave];
+  bool vblk[kGfPerWave];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) d.xf[t] = *reinterpret_cast<const u32x4*>(xrow + kb + t * 8);
-    if (FUSE_U) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) d.af[t] = *reinterpret_cast<const u32x4*>(arow + kb + t * 8);
-    }
-    d.cw[0] = *reinterpret_cast<const u32x4*>(crow + (kb >> 1));
-    d.cw[1] = *reinterpret_cast<const u32x4*>(crow + (kb >> 1) + 16);
-    d.bp = load_block_params<FMT>(a.w, rowc, kb >> 6, true);
-  };
+  for (int i = 0; i < kGfPerWave; ++i) {
+    load_chunk_codes(a.w.codes, K >> 1, n0, N, chunk_k0(i) >> 1, K >> 1, lane, raw[i]);
+    const int64_t kl = static_cast<int64_t>(cc[i]) * kGfChunk + g * 64;
+    vblk[i] = live[i] && kl < krlen;
+    const int64_t kb = kr0 + (kl < krlen ? kl : 0);
+    bp[i] = load_block_params<FMT>(a.w, rowc, kb >> 6, true);
+  }
+  // keep every load above ahead of the first use (the scheduler would
+  // otherwise sink some next to their use, one round trip each)
+  __builtin_amdgcn_sched_barrier(0);
 
   f32x4 accy = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
-  FwdChunk ch[kGfPerWave];
-  bool vch[kGfPerWave];
 #pragma unroll
   for (int i = 0; i < kGfPerWave; ++i) {
-    const int c = wave + i * kGfWaves;
-    load(c < nch ? c : nch - 1, ch[i], vch[i]);
-    vch[i] = vch[i] && c < nch;
-  }
+    // token (and adapter) fragments of this chunk
+    const uint8_t* xs = (FUSE_U || i == 0) ? slot0 : slot1;
+    u32x4 xf[8], af[8];
 #pragma unroll
-  for (int i = 0; i < kGfPerWave; ++i) {
+    for (int t = 0; t < 8; ++t) xf[t] = chunk_frag(xs, l16, g * 8 + t);
+    if (FUSE_U) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) af[t] = chunk_frag(slot1, l16, g * 8 + t);
+      if (i + 1 < kGfPerWave) {
+        // the slots are free once the fragments are in registers
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        stage_chunk(a.x, K, mrows, chunk_k0(i + 1), K, slot0, lane);
+        stage_chunk(a.A, K, arows, chunk_k0(i + 1), K, slot1, lane);
+      }
+    }
+    u32x4 cw[2];
+    route_chunk_codes(raw[i], l16, g, cw);
     Lut16 lut[2];
-    luts_from_params<FMT>(a.w, ch[i].bp, lut);
+    luts_from_params<FMT>(a.w, bp[i], lut);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const u32x4 wf = lut_decode8(lut[t >> 2], ch[i].cw[t >> 2][t & 3]);
-      accy = mfma16(vch[i] ? wf : u32x4{0, 0, 0, 0}, ch[i].xf[t], accy);
-      if (FUSE_U) accu = mfma16(ch[i].xf[t], vch[i] ? ch[i].af[t] : u32x4{0, 0, 0, 0}, accu);
+      const u32x4 wf = lut_decode8(lut[t >> 2], cw[t >> 2][t & 3]);
+      accy = mfma16(vblk[i] ? wf : u32x4{0, 0, 0, 0}, xf[t], accy);
+      if (FUSE_U) accu = mfma16(xf[t], vblk[i] ? af[t] : u32x4{0, 0, 0, 0}, accu);
     }
   }
 
-  // combine the waves: lane (l16, g) holds D[4g + v][l16]
+  // combine the waves: lane (l16, g) holds D[4g + v][l16]; each wave's
+  // partials go to the start of its own (now unused) slot
+  float* s_yw = reinterpret_cast<float*>(slot0);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    s_y[wave][lane * 4 + v] = accy[v];
-    if (FUSE_U) s_u[wave][lane * 4 + v] = accu[v];
+    s_yw[lane * 4 + v] = accy[v];
+    if (FUSE_U) s_yw[256 + lane * 4 + v] = accu[v];
   }
   if (a.adapter) {
 #pragma unroll
@@ -155,13 +234,13 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
   const int ysrc = ((en >> 2) * 16 + em) * 4 + (en & 3);
   float ysum = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kGfWaves; ++w) ysum += s_y[w][ysrc];
+  for (int w = 0; w < kGfWaves; ++w) ysum += reinterpret_cast<const float*>(s_stage[w])[ysrc];
   const int um = e8 >> 4, uj = e8 & 15;
   const int usrc = ((um >> 2) * 16 + uj) * 4 + (um & 3);
   float usum = 0.0f;
   if (FUSE_U)
 #pragma unroll
-    for (int w = 0; w < kGfWaves; ++w) usum += s_u[w][usrc];
+    for (int w = 0; w < kGfWaves; ++w) usum += reinterpret_cast<const float*>(s_stage[w])[256 + usrc];
   const bool owner = tid < 256;  // threads that finish one element each
 
   if (S > 1) {
@@ -220,6 +299,26 @@ constexpr int kGdRowsChunk = 128;
 constexpr int kGdRowsSplit = 512;
 constexpr int kGdChunks = kGdRowsSplit / kGdRowsChunk;
 constexpr int kGdWStride = kGdCols * 2 + 32;  // 288 B: rows land 8 banks apart
+constexpr int kGdPre = 8;                     // split partials prefetched per thread
+
+// Raw decode constants of a 32-column piece of one row: NF4 -> its 64-block,
+// INT4 -> its group (a = scale | zero << 16).
+template <int FMT>
+__device__ __forceinline__ BlockParams load_piece_params(const WeightView& w, int64_t row,
+                                                         int64_t col32) {
+  if (FMT == kFmtNF4) return load_block_params<kFmtNF4>(w, row, col32 >> 1, true);
+  const int64_t gi = row * (w.K >> 5) + col32;
+  BlockParams p;
+  p.a = static_cast<uint32_t>(w.scale[gi]) | (static_cast<uint32_t>(w.zero[gi]) << 16);
+  p.b = 0u;
+  return p;
+}
+template <int FMT>
+__device__ __forceinline__ Lut16 piece_lut(const WeightView& w, BlockParams p) {
+  if (FMT == kFmtNF4) return lut_nf4(w.cb, nf4_params_scale(w, p));
+  return lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.a & 0xFFFFu)),
+                  half_bits_to_f32(static_cast<uint16_t>(p.a >> 16)));
+}
 
 template <int FMT>
 __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
@@ -253,40 +352,54 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
   const int db_rows = (kGdRowsSplit + tiles - 1) / tiles;
   const int db0 = tile * db_rows;
 
-  // (1) dY slice: 16 x 512 bf16 = 1024 chunks of 16 B
+  // Every load below is unconditional, from a clamped address; masks are
+  // applied when the values are staged.  (A select on a loaded value next to
+  // its load makes the wave wait for that load and all earlier ones.)
+  // (1) dY slice: 16 x 512 bf16 = 1024 pieces of 16 B
   u32x4 dyr[4];
-  bool dym[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ch = i * 256 + tid;
     const int m = ch >> 6, q = ch & 63;
-    dym[i] = m < M && q * 8 < nlen;
     const int64_t mc = m < M ? m : M - 1;
     const int qc = q * 8 < nlen ? q : 0;
     dyr[i] = *reinterpret_cast<const u32x4*>(a.dy + mc * N + nb0 + qc * 8);
   }
-  // (2) B slice, first 16 adapter columns: 512 rows x 32 B
+  // (2) B slice, adapter columns js*16 .. js*16+15: 512 rows x 32 B
   auto load_b = [&](int js, u32x4 (&br)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ch = i * 256 + tid;
       const int nn = ch >> 1, jh = ch & 1;
       const int j0 = js * 16 + jh * 8;
-      uint32_t v[4] = {0u, 0u, 0u, 0u};
       const int64_t nnc = nn < nlen ? nn : nlen - 1;
       const uint16_t* br16 = a.B + (nb0 + nnc) * r;
       if ((r & 7) == 0) {
-        const int j0c = j0 + 8 <= r ? j0 : 0;
-        const u32x4 d = *reinterpret_cast<const u32x4*>(br16 + j0c);
-        if (nn < nlen && j0 + 8 <= r) {
-          v[0] = d.x; v[1] = d.y; v[2] = d.z; v[3] = d.w;
-        }
-      } else if (nn < nlen) {
+        const int j0c = j0 + 8 <= r ? j0 : r - 8;
+        br[i] = *reinterpret_cast<const u32x4*>(br16 + j0c);
+      } else {
+        uint32_t v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (j0 + e < r) v[e >> 1] |= static_cast<uint32_t>(br16[j0 + e]) << (16 * (e & 1));
+        for (int e = 0; e < 8; ++e) v[e] = br16[j0 + e < r ? j0 + e : r - 1];
+        br[i] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                      v[6] | (v[7] << 16)};
       }
-      br[i] = u32x4{v[0], v[1], v[2], v[3]};
+    }
+  };
+  auto store_b = [&](int js, const u32x4 (&bv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = i * 256 + tid;
+      const int nn = ch >> 1, jh = ch & 1;
+      const int j0 = js * 16 + jh * 8;
+      u32x4 v = bv[i];
+      if (nn >= nlen) v = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t keep = (j0 + e < r ? 0x0000FFFFu : 0u) | (j0 + e + 1 < r ? 0xFFFF0000u : 0u);
+        v[e >> 1] &= keep;
+      }
+      *reinterpret_cast<u32x4*>(s_b + (ch >> 1) * 32 + (ch & 1) * 16) = v;
     }
   };
   u32x4 br[4];
@@ -297,46 +410,45 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
   for (int i = 0; i < 8; ++i) {
     const int idx = i * 256 + tid;
     const int64_t last = M * r - 1;
-    const float v = a.u[idx < last ? idx : last];
-    ur[i] = (idx < 16 * r && idx / r < M) ? v : 0.0f;
+    ur[i] = a.u[idx < last ? idx : last];
   }
-  // (4) weight codes and constants for all chunks (issued last: the loads
-  //     above complete first): row (tid >> 1), block (tid & 1)
-  const int drow = tid >> 1, dblk = tid & 1;
-  const int64_t kb = kc0 + dblk * 64;
+  // (4) weight codes and constants of all chunks, issued last so the loads
+  //     above complete first.  Thread (prow, pp) owns a 32-column piece of
+  //     rows c*128 + q*64 + prow; four threads cover a row's 64 B, so each
+  //     load instruction reads 16 row segments of 64 B.
+  const int prow = tid >> 2, pp = tid & 3;
+  const int64_t pcol = kc0 + pp * 32;
+  const bool pcol_ok = pcol < K;
+  const int64_t pcolc = pcol_ok ? pcol : kc0;
   u32x4 cw[kGdChunks][2];
-  BlockParams bp[kGdChunks];
-  bool ok[kGdChunks];
+  BlockParams bp[kGdChunks][2];
 #pragma unroll
-  for (int c = 0; c < kGdChunks; ++c) {
-    const int64_t nl = c * kGdRowsChunk + drow;
-    ok[c] = do_dx && nl < nlen && kb < K;
-    const int64_t nrow = nb0 + (nl < nlen ? nl : nlen - 1);
-    const int64_t kbc = kb < K ? kb : K - 64;
-    const uint8_t* p = a.w.codes + nrow * (K >> 1) + (kbc >> 1);
-    cw[c][0] = *reinterpret_cast<const u32x4*>(p);
-    cw[c][1] = *reinterpret_cast<const u32x4*>(p + 16);
-    bp[c] = load_block_params<FMT>(a.w, nrow, kbc >> 6, true);
-  }
+  for (int c = 0; c < kGdChunks; ++c)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t nl = c * kGdRowsChunk + q * 64 + prow;
+      const int64_t nrow = nb0 + (nl < nlen ? nl : nlen - 1);
+      cw[c][q] = *reinterpret_cast<const u32x4*>(a.w.codes + nrow * (K >> 1) + (pcolc >> 1));
+      bp[c][q] = load_piece_params<FMT>(a.w, nrow, pcolc >> 5);
+    }
 
-  // (5) stage dY, the first B slice and u
+  // keep the staging below from being scheduled between the loads above
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (5) stage dY, the first B slice and u (masked here)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ch = i * 256 + tid;
-    *reinterpret_cast<u32x4*>(&s_dy[(ch >> 6) * kGdRowsSplit + (ch & 63) * 8]) =
-        dym[i] ? dyr[i] : u32x4{0, 0, 0, 0};
+    const int m = ch >> 6, q = ch & 63;
+    const bool ok = m < M && q * 8 < nlen;
+    *reinterpret_cast<u32x4*>(&s_dy[m * kGdRowsSplit + q * 8]) = ok ? dyr[i] : u32x4{0, 0, 0, 0};
   }
-  auto store_b = [&](const u32x4 (&bv)[4]) {
+  store_b(0, br);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = i * 256 + tid;
-      *reinterpret_cast<u32x4*>(s_b + (ch >> 1) * 32 + (ch & 1) * 16) = bv[i];
-    }
-  };
-  store_b(br);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i * 256 + tid < 16 * r) s_u[i * 256 + tid] = ur[i];
+  for (int i = 0; i < 8; ++i) {
+    const int idx = i * 256 + tid;
+    if (idx < 16 * r) s_u[idx] = idx / r < M ? ur[i] : 0.0f;
+  }
   __syncthreads();
 
   // (6) adapter partial du_p[m][j] = sum_{n in split} dY[m][n] B[n][j]
@@ -346,7 +458,7 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
       u32x4 bn[4];
       load_b(js, bn);
       __syncthreads();
-      store_b(bn);
+      store_b(js, bn);
       __syncthreads();
     }
     f32x4 accd = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -385,15 +497,21 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
   acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nchunks = static_cast<int>((nlen + kGdRowsChunk - 1) / kGdRowsChunk);
   auto decode = [&](int c, uint8_t* wbuf) {
-    Lut16 lut[2];
-    luts_from_params<FMT>(a.w, bp[c], lut);
-    const uint32_t words[8] = {cw[c][0].x, cw[c][0].y, cw[c][0].z, cw[c][0].w,
-                               cw[c][1].x, cw[c][1].y, cw[c][1].z, cw[c][1].w};
-    uint8_t* wrow = wbuf + drow * kGdWStride + dblk * 128;
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const u32x4 d = ok[c] ? lut_decode8(lut[tt >> 2], words[tt]) : u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(wrow + tt * 16) = d;
+    for (int q = 0; q < 2; ++q) {
+      const int row = q * 64 + prow;
+      const bool ok = do_dx && c * kGdRowsChunk + row < nlen && pcol_ok;
+      const Lut16 lut = piece_lut<FMT>(a.w, bp[c][q]);
+      uint8_t* dst = wbuf + row * kGdWStride + pp * 64;
+      // rows 2 apart start 16 banks apart: alternate the store order by row
+      // pair so that the 16 lanes of a store hit distinct banks
+      const int sw = (row >> 1) & 1;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int ss = s ^ sw;
+        const u32x4 d = lut_decode8(lut, cw[c][q][ss]);
+        *reinterpret_cast<u32x4*>(dst + ss * 16) = ok ? d : u32x4{0, 0, 0, 0};
+      }
     }
   };
   if (do_dx) {
@@ -432,7 +550,7 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
   if (publish_and_ticket(a.counters + tile, &s_ticket) != static_cast<uint32_t>(a.splits - 1))
     return;
 
-  // ---- fix-up of this column tile
+  // ---- fix-up of this column tile (the last workgroup of the tile)
   const int S = a.splits;
   const int ps = a.pool_shift;
   const int ncol = K - kc0 < kGdCols ? static_cast<int>(K - kc0) : kGdCols;
@@ -443,42 +561,66 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
   float* s_du = reinterpret_cast<float*>(s_lds);                 // [16][r]   8 KB max
   float* s_px = reinterpret_cast<float*>(s_lds + 8192);          // [16][128] 8 KB
   uint16_t* s_a = reinterpret_cast<uint16_t*>(s_lds + 16384);    // [r][128] 32 KB max
-  // issue loads: partial dX, du partials, x tile, A tile
   const int m = tid >> 4;
   const int cl = (tid & 15) * 8;
   const int64_t kx = kc0 + cl < K ? kc0 + cl : K - 8;
-  constexpr int kPre = 8;  // split partials prefetched per thread
-  f32x4 pd[kPre][2];
+  const bool narrow = r <= 16 && a.pool == 1;  // one load of each kind per thread
+
+  // issue every load before using any: split partials of dX, du partials,
+  // the x tile and (narrow adapters) the A tile
+  f32x4 pd[kGdPre][2];
   const rsrc_t pr = make_rsrc(a.partial);
-  if (do_dx) {
 #pragma unroll
-    for (int sp = 0; sp < kPre; ++sp) {
-      const int spc = sp < S ? sp : S - 1;
-      const uint32_t off = static_cast<uint32_t>(((static_cast<int64_t>(spc) * 16 + m) * K + kx) * 4);
-      pd[sp][0] = ld_sys16(pr, off);
-      pd[sp][1] = ld_sys16(pr, off + 16);
-    }
+  for (int sp = 0; sp < kGdPre; ++sp) {
+    const int spc = sp < S ? sp : S - 1;
+    const uint32_t off = static_cast<uint32_t>(((static_cast<int64_t>(spc) * 16 + m) * K + kx) * 4);
+    pd[sp][0] = ld_sys16(pr, off);
+    pd[sp][1] = ld_sys16(pr, off + 16);
   }
   const float* dub = a.du_part + static_cast<int64_t>(tile) * S * (16 * r);
-  for (int idx = tid; idx < 16 * r; idx += 256) {
-    float dv[kPre];
+  const int dlast = 16 * r - 1;
+  float dv[kGdPre];
 #pragma unroll
-    for (int sp = 0; sp < kPre; ++sp) dv[sp] = ld_sys(dub + (sp < S ? sp : S - 1) * (16 * r) + idx);
+  for (int sp = 0; sp < kGdPre; ++sp)
+    dv[sp] = ld_sys(dub + (sp < S ? sp : S - 1) * (16 * r) + (tid < dlast ? tid : dlast));
+  const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (m < M ? m : M - 1) * K + kx);
+  u32x4 av = u32x4{0u, 0u, 0u, 0u};
+  if (narrow) {
+    const int j = tid >> 4;
+    av = *reinterpret_cast<const u32x4*>(a.A + static_cast<int64_t>(j < r ? j : r - 1) * Ka + ac0 +
+                                         (kc0 + cl < K ? cl : ncol - 8));
+  }
+
+  // stage du (all splits), x (as fp32) and A
+  {
     float v = 0.0f;
 #pragma unroll
-    for (int sp = 0; sp < kPre; ++sp)
+    for (int sp = 0; sp < kGdPre; ++sp)
       if (sp < S) v += dv[sp];
-    for (int sp = kPre; sp < S; ++sp) v += ld_sys(dub + sp * (16 * r) + idx);
-    s_du[idx] = a.s * v;
+    for (int sp = kGdPre; sp < S; ++sp) v += ld_sys(dub + sp * (16 * r) + (tid < dlast ? tid : dlast));
+    if (tid < 16 * r) s_du[tid] = a.s * v;
+    for (int idx = tid + 256; idx < 16 * r; idx += 256) {
+      float w = 0.0f;
+      for (int sp = 0; sp < S; ++sp) w += ld_sys(dub + sp * (16 * r) + idx);
+      s_du[idx] = a.s * w;
+    }
   }
   {
-    const int c = tid & 127, m0 = tid >> 7;
-    for (int mm = m0; mm < 16; mm += 2)
-      s_px[mm * kGdCols + c] = (mm < M && c < ncol) ? bf16_to_f32(a.x[mm * K + kc0 + c]) : 0.0f;
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = m < M && cl + e < ncol;
+      s_px[m * kGdCols + cl + e] = ok ? bf16_to_f32(static_cast<uint16_t>(xw[e >> 1] >> (16 * (e & 1)))) : 0.0f;
+    }
   }
-  for (int idx = tid; idx < r * acols; idx += 256) {
-    const int j = idx / acols, c = idx % acols;
-    s_a[j * kGdCols + c] = a.A[static_cast<int64_t>(j) * Ka + ac0 + c];
+  if (narrow) {
+    const int j = tid >> 4;
+    if (j < r) *reinterpret_cast<u32x4*>(&s_a[j * kGdCols + cl]) = av;
+  } else {
+    for (int idx = tid; idx < r * acols; idx += 256) {
+      const int j = idx / acols, c = idx % acols;
+      s_a[j * kGdCols + c] = a.A[static_cast<int64_t>(j) * Ka + ac0 + c];
+    }
   }
   __syncthreads();
   if (a.pool > 1) {
@@ -492,6 +634,7 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     __syncthreads();
   }
   // dA[j][c] = sum_m du[m][j] P[m][c]
+#pragma unroll 2
   for (int idx = tid; idx < r * acols; idx += 256) {
     const int j = idx / acols, c = idx % acols;
     float t = 0.0f;
@@ -504,14 +647,14 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
 #pragma unroll
-    for (int sp = 0; sp < kPre; ++sp)
+    for (int sp = 0; sp < kGdPre; ++sp)
       if (sp < S)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           sum[e] += pd[sp][0][e];
           sum[4 + e] += pd[sp][1][e];
         }
-    for (int sp = kPre; sp < S; ++sp) {
+    for (int sp = kGdPre; sp < S; ++sp) {
       const uint32_t off = static_cast<uint32_t>(((static_cast<int64_t>(sp) * 16 + m) * K + kx) * 4);
       const f32x4 v0 = ld_sys16(pr, off);
       const f32x4 v1 = ld_sys16(pr, off + 16);
@@ -522,13 +665,31 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
       }
     }
     // adapter term du A (pooled: each group's value repeated over its columns)
+    float t[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = a.pool == 1 ? cl + e : ((cl + e) >> ps);
-      float t = 0.0f;
-      for (int j = 0; j < r; ++j) t += s_du[m * r + j] * bf16_to_f32(s_a[j * kGdCols + c]);
-      sum[e] += t;
+    for (int e = 0; e < 8; ++e) t[e] = 0.0f;
+    if (a.pool == 1) {
+#pragma unroll 4
+      for (int j = 0; j < r; ++j) {
+        const float d = s_du[m * r + j];
+        const u32x4 av8 = *reinterpret_cast<const u32x4*>(&s_a[j * kGdCols + cl]);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          t[e] += d * bf16_lo(av8[e >> 1]);
+          t[e + 1] += d * bf16_hi(av8[e >> 1]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = (cl + e) >> ps;
+        float te = 0.0f;
+        for (int j = 0; j < r; ++j) te += s_du[m * r + j] * bf16_to_f32(s_a[j * kGdCols + c]);
+        t[e] = te;
+      }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] += t[e];
     u32x4 o;
     o.x = pack_bf16x2(sum[0], sum[1]);
     o.y = pack_bf16x2(sum[2], sum[3]);
