@@ -26,8 +26,11 @@ constexpr int kXTile = kTM * kKS * 2;  // bytes
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Token tile in LDS: 256 B per row (128 k), 16-byte chunks XOR-swizzled by
+// the row's low four bits so that 16 consecutive rows (the lanes of one
+// LDS cycle) read 16 distinct bank groups.
 __device__ __forceinline__ uint32_t xoff(int row, int chunk) {
-  return static_cast<uint32_t>(row * 256 + ((chunk ^ (row & 7)) << 4));
+  return static_cast<uint32_t>(row * 256 + ((chunk ^ (row & 15)) << 4));
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
@@ -80,23 +83,30 @@ __device__ __forceinline__ void load_params<kFmtINT4>(const WeightView& w, const
 
 template <int FMT>
 __device__ __forceinline__ Lut16 step_lut(const WeightView& w, const StepParams<FMT>& p, int r,
-                                          int q);
+                                          int q, bool valid);
 template <>
 __device__ __forceinline__ Lut16 step_lut<kFmtNF4>(const WeightView& w,
-                                                   const StepParams<kFmtNF4>& p, int r, int) {
-  return lut_nf4(w.cb, nf4_params_scale(w, p.bp[r]));
+                                                   const StepParams<kFmtNF4>& p, int r, int,
+                                                   bool valid) {
+  // an invalid block (past K) decodes to zeros through a zero scale
+  return lut_nf4(w.cb, valid ? nf4_params_scale(w, p.bp[r]) : 0.0f);
 }
 template <>
 __device__ __forceinline__ Lut16 step_lut<kFmtINT4>(const WeightView&,
-                                                    const StepParams<kFmtINT4>& p, int r, int q) {
-  return lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.sz[r][q] & 0xFFFFu)),
-                  half_bits_to_f32(static_cast<uint16_t>(p.sz[r][q] >> 16)));
+                                                    const StepParams<kFmtINT4>& p, int r, int q,
+                                                    bool valid) {
+  const uint32_t sz = valid ? p.sz[r][q] : 0u;
+  return lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
+                  half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
 }
+
+constexpr int kCTile = kTN * kKS / 2;  // packed codes of one K step: 16 KB
 
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXTile];
-  __shared__ uint32_t s_ticket;
+  // two stages of [token tile 64 KB | packed codes 16 KB] = all 160 KB of LDS
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXTile + kCTile];
+  uint32_t* s_ticket = reinterpret_cast<uint32_t*>(&s_x[0][0]);  // used after the K loop
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5;
@@ -120,89 +130,153 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
     const int64_t n = n0 + wave * 64 + r * 32 + l32;
     nr[r] = n < N ? n : N - 1;
   }
-  const uint8_t* crow0 = a.w.codes + nr[0] * (K >> 1);
-  const uint8_t* crow1 = a.w.codes + nr[1] * (K >> 1);
-
   f32x16 acc[2][8];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms) acc[r][ms] = f32x16{};
 
+  // Token tile source: a buffer resource over this tile's rows of x, so a
+  // load is one instruction with a fixed per-lane offset and a scalar
+  // per-step offset.  Rows past M fall outside the resource (their output
+  // rows are never stored); columns past K in the last step meet weights
+  // masked to zero.
+  const int64_t rows_here = M - m0 < kTM ? M - m0 : kTM;
+  const rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.x + m0 * K), 0, static_cast<int>(rows_here * K * 2), 0x00020000);
+  const int lrow = wave * 4 + (lane >> 4);  // row within each group of 16
+  const uint32_t xvoff = static_cast<uint32_t>(lrow * K * 2 + (((lane & 15) ^ lrow) << 4));
   auto load_x = [&](int64_t ks, int buf) {
-    const int64_t kb = ks * kKS;
+    const uint32_t kb2 = static_cast<uint32_t>(ks * kKS * 2);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = (i * 4 + wave) * 4 + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 7);
-      int64_t m = m0 + row;
-      m = m < M ? m : M - 1;
-      int64_t k = kb + c * 8;
-      k = k < K ? k : K - 8;
-      const uint16_t* src = a.x + m * K + k;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(&s_x[buf][(i * 4 + wave) * 1024]), 16, 0,
-                                       0);
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (lds_ptr_t)(&s_x[buf][(i * 4 + wave) * 1024]), 16, xvoff,
+          static_cast<int>(static_cast<uint32_t>(i * 16 * K * 2) + kb2), 0, 0);
+  };
+  // Packed codes of a K step: 256 rows x 64 B into LDS next to the token
+  // tile.  A load instruction covers 16 rows (4 lanes x 16 B each); the four
+  // 16-byte pieces of a row are XOR-swizzled by (row / 4) % 4 so that the
+  // 16-byte reads of 16 consecutive rows hit distinct banks.  Rows past N
+  // fall outside the resource (their outputs are never stored).
+  const int64_t nrows_here = N - n0 < kTN ? N - n0 : kTN;
+  const rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.w.codes + n0 * (K >> 1)), 0, static_cast<int>(nrows_here * (K >> 1)),
+      0x00020000);
+  const int cpiece = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t cvoff = static_cast<uint32_t>((wave * 16 + (lane >> 2)) * (K >> 1) + cpiece * 16);
+  auto load_codes = [&](int64_t ks, int buf) {
+    const uint32_t kb = static_cast<uint32_t>(ks * (kKS / 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          cr, (lds_ptr_t)(&s_x[buf][kXTile + (i * 4 + wave) * 1024]), 16, cvoff,
+          static_cast<int>(static_cast<uint32_t>(i * 64 * (K >> 1)) + kb), 0, 0);
+  };
+  // this lane's 16 code words of a step: rows wave*64 + r*32 + l32, half h
+  auto read_codes = [&](int buf, u32x4 (&c)[2][2]) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = wave * 64 + r * 32 + l32;
+      const int sw = (row >> 2) & 3;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        c[r][q] = *reinterpret_cast<const u32x4*>(&s_x[buf][kXTile + row * 64 + (((2 * h + q) ^ sw) << 4)]);
     }
   };
-
-  u32x4 cc[2][2], cn[2][2];
-  StepParams<FMT> pc, pn;
-  auto load_codes = [&](int64_t ks, u32x4 (&c)[2][2], StepParams<FMT>& p) {
+  auto load_step_params = [&](int64_t ks, StepParams<FMT>& p) {
     const int64_t kk = ks * kKS + h * 64;
-    // unconditional loads (clamped past the K tail; that half is masked at decode)
-    const int64_t kc = kk < K ? kk : K - 64;
-    const int64_t off = kc >> 1;
-    c[0][0] = *reinterpret_cast<const u32x4*>(crow0 + off);
-    c[0][1] = *reinterpret_cast<const u32x4*>(crow0 + off + 16);
-    c[1][0] = *reinterpret_cast<const u32x4*>(crow1 + off);
-    c[1][1] = *reinterpret_cast<const u32x4*>(crow1 + off + 16);
-    load_params<FMT>(a.w, nr, kc >> 6, true, p);
+    load_params<FMT>(a.w, nr, (kk < K ? kk : K - 64) >> 6, true, p);
   };
 
-  load_x(ks0, 0);
-  load_codes(ks0, cc, pc);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int64_t ks = ks0; ks < ks1; ++ks) {
-    const int buf = static_cast<int>((ks - ks0) & 1);
-    if (ks + 1 < ks1) {
-      load_x(ks + 1, buf ^ 1);
-      load_codes(ks + 1, cn, pn);
-    }
-    const bool wvalid = ks * kKS + h * 64 < K;
-    constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
-    Lut16 lut[2][NL];
+  constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
+  Lut16 lut[2][NL];
+  auto build_luts = [&](const StepParams<FMT>& p, bool valid) {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int q = 0; q < NL; ++q) lut[r][q] = step_lut<FMT>(a.w, pc, r, q);
+      for (int q = 0; q < NL; ++q) lut[r][q] = step_lut<FMT>(a.w, p, r, q, valid);
+  };
+  auto decode_w = [&](const u32x4 (&c)[2][2], int tt, u32x4 (&wf)[2]) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      wf[r] = lut_decode8(lut[r][NL == 1 ? 0 : (tt >> 2)], c[r][tt >> 2][tt & 3]);
+  };
+  auto read_x = [&](const uint8_t* xb, int tt, u32x4 (&xf)[8]) {
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms)
+      xf[ms] = *reinterpret_cast<const u32x4*>(xb + xoff(ms * 32 + l32, 8 * h + tt));
+  };
+  auto step_valid = [&](int64_t ks) { return ks * kKS + h * 64 < K; };
 
+  // Tiles and codes run one K step ahead, block constants two: step ks+1's
+  // tables are built while step ks's last MFMAs run.
+  StepParams<FMT> pc, pn, p2;
+  load_x(ks0, 0);
+  load_codes(ks0, 0);
+  load_step_params(ks0, pc);
+  if (ks0 + 1 < ks1) load_step_params(ks0 + 1, pn);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  build_luts(pc, step_valid(ks0));
+
+  // Two-stage register pipeline over the eight k16 sub-steps of a K step:
+  // while the 16 MFMAs of sub-step tt run, the weight words of tt + 1 are
+  // decoded and its token fragments read from LDS.
+  u32x4 cw[2][2], wf[2][2], xf[2][8];
+  for (int64_t ks = ks0; ks < ks1; ++ks) {
+    const int buf = static_cast<int>((ks - ks0) & 1);
+    const bool more = ks + 1 < ks1;
     const uint8_t* xb = s_x[buf];
+    read_codes(buf, cw);
+    read_x(xb, 0, xf[0]);
+    decode_w(cw, 0, wf[0]);
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      u32x4 wf[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint32_t word = cc[r][tt >> 2][tt & 3];
-        const u32x4 d = lut_decode8(lut[r][NL == 1 ? 0 : (tt >> 2)], word);
-        wf[r] = wvalid ? d : u32x4{0, 0, 0, 0};
+      const int cur = tt & 1, nxt = cur ^ 1;
+      // Next step's loads, one wave at a time: a wave blocks while the load
+      // path takes its 1 KB load instructions, so the waves take turns
+      // (wave w at sub-step 2w) and the other three keep issuing MFMAs.
+      // The target stage was last read before the previous barrier.
+      if (tt == 2 * wave) {
+        if (more) {
+          load_x(ks + 1, buf ^ 1);
+          load_codes(ks + 1, buf ^ 1);
+        }
+        if (ks + 2 < ks1) load_step_params(ks + 2, p2);
+      }
+      if (tt < 7) {
+        decode_w(cw, tt + 1, wf[nxt]);
+        read_x(xb, tt + 1, xf[nxt]);
+      } else if (more) {
+        build_luts(pn, step_valid(ks + 1));
       }
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms) {
-        const u32x4 xf = *reinterpret_cast<const u32x4*>(xb + xoff(ms * 32 + l32, 8 * h + tt));
-        acc[0][ms] = mfma32(wf[0], xf, acc[0][ms]);
-        acc[1][ms] = mfma32(wf[1], xf, acc[1][ms]);
+        acc[0][ms] = mfma32(wf[cur][0], xf[cur][ms], acc[0][ms]);
+        acc[1][ms] = mfma32(wf[cur][1], xf[cur][ms], acc[1][ms]);
       }
-      // keep each k16 sub-step's operands live only within the sub-step
+      if (tt < 7) {
+        // issue order: 2 MFMA, 1 LDS read of the next sub-step, ~7 VALU of
+        // the next decode; x8 (measured best: an LDS read issued ahead of
+        // the MFMA pair delays it, one issued last lands too late)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      cc[r][0] = cn[r][0];
-      cc[r][1] = cn[r][1];
-    }
     pc = pn;
+    pn = p2;
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
@@ -263,7 +337,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
       for (int ms = 0; ms < 8; ++ms)
 #pragma unroll
         for (int v = 0; v < 16; ++v) st_sys(part + ((r * 8 + ms) * 16 + v) * 256 + tid, acc[r][ms][v]);
-    if (publish_and_ticket(a.counters + tmn, &s_ticket) != static_cast<uint32_t>(a.splits - 1))
+    if (publish_and_ticket(a.counters + tmn, s_ticket) != static_cast<uint32_t>(a.splits - 1))
       return;
     const float* base = a.partial + static_cast<int64_t>(tmn) * a.splits * (kTM * kTN);
 #pragma unroll
