@@ -3,13 +3,12 @@
 // abstract: the adapter of the group-wise variant sees pooled inputs.]
 //
 //   NT  C[m][j] = alpha * sum_k X[m][k] * Y[j][k]        u = x A^T, du = s dY B
-//   TN  C[p][j] = alpha * sum_m X[m][p] * Z[m][j]        dB = s dY^T u, dA = du^T x
 //
-// Both reduce over a long dimension with a narrow (rank-r) output, so the
-// reduction is split across workgroups; partial sums are written to the
-// workspace and the last workgroup of each output tile (atomic ticket) adds
-// them in fixed split order, which keeps results bit-identical run to run.
-// fp32 operands (u, du) enter bf16 MFMA as hi + lo pairs.
+// The product reduces over a long dimension with a narrow (rank-r) output,
+// so the reduction is split across workgroups; partial sums are written to
+// the workspace and the last workgroup of each output tile (atomic ticket)
+// adds them in fixed split order, which keeps results bit-identical run to
+// run.  (The transposed products dB and dA are in adapter_tn.hip.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -122,146 +121,6 @@ __global__ __launch_bounds__(256) void k_nt_skinny(NtArgs a) {
     }
 }
 
-// ---------------------------------------------------------------- TN skinny
-// Workgroup: a 64-column tile of X (p), all J (<= 128) columns of Z, a slice
-// of rows m.  Per 32-row step both tiles are staged transposed in LDS (m
-// innermost), Z as hi and lo bf16 halves.  Wave w owns p-sub (w & 1) and the
-// j-subs of parity (w >> 1).
-constexpr int kTnP = 64;
-constexpr int kTnM = 32;
-
-__global__ __launch_bounds__(256) void k_tn_skinny(TnArgs a) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int p_tiles = static_cast<int>((a.P + kTnP - 1) / kTnP);
-  const int tile = blockIdx.x % p_tiles;
-  const int split = blockIdx.x / p_tiles;
-  const int64_t p0 = static_cast<int64_t>(tile) * kTnP;
-  const int64_t m_steps = (a.M + kTnM - 1) / kTnM;
-  const int64_t per = (m_steps + a.splits - 1) / a.splits;
-  const int64_t s_begin = split * per;
-  const int64_t s_end = s_begin + per < m_steps ? s_begin + per : m_steps;
-  const int jsub = (a.J + 31) / 32;
-
-  // [p][m] bf16, row = 32 m = 64 B, padded to 80 B to spread banks
-  constexpr int kRow = 40;  // in uint16 units
-  __shared__ uint16_t s_x[kTnP * kRow];
-  __shared__ uint16_t s_zh[128 * kRow];
-  __shared__ uint16_t s_zl[128 * kRow];
-
-  f32x16 acc[2];
-  acc[0] = f32x16{};
-  acc[1] = f32x16{};
-  const int psub = wave & 1;
-  const int jpar = wave >> 1;
-
-  for (int64_t st = s_begin; st < s_end; ++st) {
-    const int64_t mb = st * kTnM;
-    // stage X[mb..mb+31][p0..p0+63]: 32 rows x 8 chunks of 8 -> 256 chunks
-    {
-      const int mm = tid & 31, pc = tid >> 5;  // pc 0..7
-      const int64_t m = mb + mm;
-      const int64_t p = p0 + pc * 8;
-      uint16_t v[8];
-      if (m < a.M && p + 8 <= a.P) {
-        const u32x4 d = *reinterpret_cast<const u32x4*>(a.X + m * a.ldx + p);
-        v[0] = d.x & 0xFFFF; v[1] = d.x >> 16; v[2] = d.y & 0xFFFF; v[3] = d.y >> 16;
-        v[4] = d.z & 0xFFFF; v[5] = d.z >> 16; v[6] = d.w & 0xFFFF; v[7] = d.w >> 16;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = (m < a.M && p + e < a.P) ? a.X[m * a.ldx + p + e] : static_cast<uint16_t>(0);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_x[(pc * 8 + e) * kRow + mm] = v[e];
-    }
-    // stage Z[mb..mb+31][0..J-1] fp32 -> hi/lo bf16, transposed
-    for (int idx = tid; idx < kTnM * 128; idx += 256) {
-      const int mm = idx & 31, j = idx >> 5;
-      const int64_t m = mb + mm;
-      float z = 0.0f;
-      if (m < a.M && j < a.J) z = a.Z[m * a.ldz + j];
-      float hi, lo;
-      split_bf16(z, hi, lo);
-      s_zh[j * kRow + mm] = static_cast<uint16_t>(__float_as_uint(hi) >> 16);
-      s_zl[j * kRow + mm] = f32_to_bf16(lo);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int mo = kk * 16 + h * 8;
-      const u32x4 xa = *reinterpret_cast<const u32x4*>(&s_x[(psub * 32 + l32) * kRow + mo]);
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        const int q = jpar + 2 * qq;
-        if (q < jsub) {
-          const u32x4 zh = *reinterpret_cast<const u32x4*>(&s_zh[(q * 32 + l32) * kRow + mo]);
-          const u32x4 zl = *reinterpret_cast<const u32x4*>(&s_zl[(q * 32 + l32) * kRow + mo]);
-          acc[qq] = mfma32(xa, zh, acc[qq]);
-          acc[qq] = mfma32(xa, zl, acc[qq]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  // partial layout: [tile][split][wave][qq][16][64]
-  constexpr int kPart = 4 * 2 * 16 * 64;
-  float sum[2][16];
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sum[qq][e] = acc[qq][e];
-  if (a.splits > 1) {
-    float* part = a.partial + (static_cast<int64_t>(tile) * a.splits + split) * kPart;
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st_sys(part + ((wave * 2 + qq) * 16 + e) * 64 + lane, sum[qq][e]);
-    __shared__ uint32_t s_ticket;
-    if (publish_and_ticket(a.counters + tile, &s_ticket) != static_cast<uint32_t>(a.splits - 1))
-      return;
-    const float* base = a.partial + static_cast<int64_t>(tile) * a.splits * kPart;
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sum[qq][e] = 0.0f;
-    for (int sp = 0; sp < a.splits; ++sp) {
-      float v[2][16];
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          v[qq][e] = ld_sys(base + sp * kPart + ((wave * 2 + qq) * 16 + e) * 64 + lane);
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sum[qq][e] += v[qq][e];
-    }
-    if (tid == 0) a.counters[tile] = 0u;
-  }
-  // D[p][j]: lane holds D[8i + 4h + t][l32]
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const int q = jpar + 2 * qq;
-    if (q >= jsub) continue;
-    const int j = q * 32 + l32;
-    if (j >= a.J) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t p = p0 + psub * 32 + 8 * i + 4 * h + t;
-        if (p >= a.P) continue;
-        const uint16_t v = f32_to_bf16(a.alpha * sum[qq][4 * i + t]);
-        if (a.out_transposed)
-          a.C[static_cast<int64_t>(j) * a.ldc + p] = v;
-        else
-          a.C[p * a.ldc + j] = v;
-      }
-  }
-}
-
 // ----------------------------------------------------------- transpose bf16
 __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict__ in, int64_t rows,
                                                      int64_t cols, uint16_t* __restrict__ out) {
@@ -339,17 +198,6 @@ hipError_t launch_nt_skinny(const NtArgs& a, hipStream_t stream) {
 int nt_tiles(int64_t M) { return static_cast<int>((M + kNtRowsPerWg - 1) / kNtRowsPerWg); }
 int64_t nt_partial_floats(int64_t M, int splits) {
   return splits > 1 ? static_cast<int64_t>(nt_tiles(M)) * splits * (4 * 16 * 64) : 0;
-}
-
-hipError_t launch_tn_skinny(const TnArgs& a, hipStream_t stream) {
-  const int p_tiles = static_cast<int>((a.P + kTnP - 1) / kTnP);
-  hipLaunchKernelGGL(k_tn_skinny, dim3(p_tiles * a.splits), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-int tn_tiles(int64_t P) { return static_cast<int>((P + kTnP - 1) / kTnP); }
-int64_t tn_partial_floats(int64_t P, int splits) {
-  return splits > 1 ? static_cast<int64_t>(tn_tiles(P)) * splits * (4 * 2 * 16 * 64) : 0;
 }
 
 hipError_t launch_transpose16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,

@@ -97,10 +97,10 @@ struct Plan {
   bool small = false;
   int fwd_splits = 1;
   int nt_splits_u = 1, nt_splits_du = 1;
-  int tn_splits_dB = 1, tn_splits_dA = 1;
+  int tn2_splits_dB = 1, tn2_splits_dA = 1;
   int gf_splits = 1, gd_splits = 1;
   size_t off_counters = 0, off_u = 0, off_du = 0, off_Bt = 0, off_At = 0, off_P = 0,
-         off_Gq = 0, off_partial = 0, total = 0;
+         off_Gq = 0, off_z = 0, off_partial = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -109,14 +109,15 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   Plan p;
   const int64_t N = w->d_out, K = w->d_in, G = K / pool;
   p.small = M <= kSmallM;
-  // adapter reductions: aim for ~512 workgroups, each with enough work
-  // ~512 workgroups for large problems, but never fewer than 64 k16 steps
-  // (NT) or 4 token steps (TN) per workgroup
+  // u and du reductions: ~512 workgroups, but never fewer than 64 k16
+  // steps per workgroup
   p.nt_splits_u = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), K / 16 / 64), 1, 64));
   p.nt_splits_du = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), N / 16 / 64), 1, 64));
-  const int64_t msteps = ceil_div(M, 32);
-  p.tn_splits_dB = static_cast<int>(clamp64(std::min<int64_t>(1024 / tn_tiles(N), msteps / 4), 1, 64));
-  p.tn_splits_dA = static_cast<int>(clamp64(std::min<int64_t>(1024 / tn_tiles(K), msteps / 4), 1, 64));
+  // token-share splits of the adapter-gradient reductions: ~320 workgroups,
+  // at least 256 tokens per share
+  const int64_t max_shares = std::max<int64_t>(1, M / 256);
+  p.tn2_splits_dB = static_cast<int>(clamp64(ceil_div(320, tn2_tiles(N)), 1, std::min<int64_t>(max_shares, 64)));
+  p.tn2_splits_dA = static_cast<int>(clamp64(ceil_div(320, tn2_tiles(K)), 1, std::min<int64_t>(max_shares, 64)));
   if (!p.small) {
     const int tiles = fwd_gemm_tiles(M, N);
     if (tiles < 192) p.fwd_splits = static_cast<int>(clamp64(ceil_div(256, tiles), 1, std::max<int64_t>(1, ceil_div(K, 128) / 4)));
@@ -124,12 +125,13 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.gf_splits = gemv_fwd_splits(K);
   p.gd_splits = gemv_dx_splits(N);
 
-  int64_t counters = std::max<int64_t>({nt_tiles(M), tn_tiles(N), tn_tiles(K), gemv_fwd_tiles(N),
-                                        gemv_dx_tiles(K), int64_t{fwd_gemm_tiles(M, N)}});
+  int64_t counters = std::max<int64_t>({nt_tiles(M), gemv_fwd_tiles(N),
+                                        gemv_dx_tiles(K), int64_t{fwd_gemm_tiles(M, N)},
+                                        int64_t{tn2_tiles(N)}, int64_t{tn2_tiles(K)}});
   int64_t partial = std::max<int64_t>({nt_partial_floats(M, p.nt_splits_u),
                                        nt_partial_floats(M, p.nt_splits_du),
-                                       tn_partial_floats(N, p.tn_splits_dB),
-                                       tn_partial_floats(K, p.tn_splits_dA)});
+                                       tn2_partial_floats(N, r, p.tn2_splits_dB),
+                                       tn2_partial_floats(K, r, p.tn2_splits_dA)});
   if (p.small) {
     partial = std::max<int64_t>({partial,
                                  gemv_fwd_partial_floats(N, K),
@@ -145,6 +147,7 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.off_At = off;       off = align256(off + (pool == 1 ? static_cast<size_t>(K) * r * sizeof(uint16_t) : 0));
   p.off_P = off;        off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
   p.off_Gq = off;       off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
+  p.off_z = off;        off = align256(off + (p.small ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
   p.off_partial = off;  off = align256(off + static_cast<size_t>(partial) * sizeof(float));
   p.total = off;
   return p;
@@ -356,22 +359,26 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     a.partial = partial; a.counters = counters;
     QLIN_TRY(launch_nt_skinny(a, stream));
   }
-  // dB = s dY^T u
+  // dB = s dY^T u  (u as bf16 hi/lo planes)
+  const int64_t jp = tn2_jp(r);
+  uint16_t* zp = ws_at<uint16_t>(workspace, p.off_z);
   {
-    TnArgs a{};
-    a.X = dy; a.ldx = N; a.Z = u; a.ldz = r; a.C = dB; a.ldc = r;
-    a.M = M; a.P = N; a.J = r; a.splits = p.tn_splits_dB; a.out_transposed = 0; a.alpha = s;
+    QLIN_TRY(launch_split_hl(u, M, r, r, zp, zp + M * jp, stream));
+    Tn2Args a{};
+    a.X = dy; a.ldx = N; a.Zh = zp; a.Zl = zp + M * jp; a.C = dB; a.ldc = r;
+    a.M = M; a.P = N; a.J = r; a.splits = p.tn2_splits_dB; a.out_transposed = 0; a.alpha = s;
     a.partial = partial; a.counters = counters;
-    QLIN_TRY(launch_tn_skinny(a, stream));
+    QLIN_TRY(launch_tn2(a, stream));
   }
   // dA = du^T P
   float* Gq = nullptr;
   if (pool == 1) {
-    TnArgs a{};
-    a.X = x; a.ldx = K; a.Z = du; a.ldz = r; a.C = dA; a.ldc = K;
-    a.M = M; a.P = K; a.J = r; a.splits = p.tn_splits_dA; a.out_transposed = 1; a.alpha = 1.0f;
+    QLIN_TRY(launch_split_hl(du, M, r, r, zp + 2 * M * jp, zp + 3 * M * jp, stream));
+    Tn2Args a{};
+    a.X = x; a.ldx = K; a.Zh = zp + 2 * M * jp; a.Zl = zp + 3 * M * jp; a.C = dA; a.ldc = K;
+    a.M = M; a.P = K; a.J = r; a.splits = p.tn2_splits_dA; a.out_transposed = 1; a.alpha = 1.0f;
     a.partial = partial; a.counters = counters;
-    QLIN_TRY(launch_tn_skinny(a, stream));
+    QLIN_TRY(launch_tn2(a, stream));
   } else {
     QaArgs q{};
     q.x = x; q.A = A; q.du = du; q.M = M; q.K = K; q.G = G; q.r = r; q.pool = pool;

@@ -32,21 +32,24 @@ hipError_t launch_nt_skinny(const NtArgs& a, hipStream_t stream);
 int nt_tiles(int64_t M);
 int64_t nt_partial_floats(int64_t M, int splits);
 
-struct TnArgs {  // C[p][j] (or C[j][p]) = alpha * sum_m X[m][p] Z[m][j]
+struct Tn2Args {  // C[p][j] (or C[j][p]) = alpha * sum_m X[m][p] Z[m][j], Z as bf16 hi/lo planes
   const uint16_t* X;  int64_t ldx;
-  const float* Z;     int64_t ldz;
+  const uint16_t* Zh; const uint16_t* Zl;  // [M][tn2_jp(J)]
   uint16_t* C;        int64_t ldc;
   int64_t M, P;
   int32_t J;          // <= 128
-  int32_t splits;
+  int32_t splits;     // token shares
   int32_t out_transposed;
   float alpha;
-  float* partial;
-  uint32_t* counters;
+  float* partial;     // tn2_partial_floats(P, J, splits)
+  uint32_t* counters; // tn2_tiles(P)
 };
-hipError_t launch_tn_skinny(const TnArgs& a, hipStream_t stream);
-int tn_tiles(int64_t P);
-int64_t tn_partial_floats(int64_t P, int splits);
+int tn2_jp(int J);
+int tn2_tiles(int64_t P);
+int64_t tn2_partial_floats(int64_t P, int J, int splits);
+hipError_t launch_split_hl(const float* Z, int64_t M, int J, int64_t ldz, uint16_t* Zh,
+                           uint16_t* Zl, hipStream_t stream);
+hipError_t launch_tn2(const Tn2Args& a, hipStream_t stream);
 
 hipError_t launch_transpose16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                               hipStream_t stream);
