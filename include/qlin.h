@@ -77,8 +77,10 @@ typedef enum {
  * A packed 4-bit weight W[d_out][d_in] (read-only device memory).
  *
  * codes   uint8[d_out][d_in/2]: two 4-bit indices per byte along each row;
- *         byte j of a row holds element 2j in its low nibble and element
- *         2j+1 in its high nibble.
+ *         every run of 8 elements of a row fills 4 bytes, and byte j of the
+ *         run holds element j in its low nibble and element j + 4 in its
+ *         high nibble (so one little-endian 32-bit word holds elements
+ *         0..3 in its low nibbles and 4..7 in its high nibbles).
  * NF4 (block = 64): element (n, k) belongs to block b = (n*d_in + k)/64 (64
  *         consecutive elements of one row) and decodes to
  *             bf16( fl32( c[idx] * a_hat_b ) ),   ties-to-even,

@@ -155,18 +155,28 @@ def nearest_level_index(w: np.ndarray, a: np.ndarray, codebook: np.ndarray) -> n
 
 
 def pack_nibbles(idx: np.ndarray) -> np.ndarray:
-    """Two 4-bit indices per byte along each row: byte j holds element 2j in
-    its low nibble and element 2j+1 in its high nibble.  [R8]"""
+    """Two 4-bit indices per byte along each row.  Each run of 8 elements
+    fills 4 bytes: byte j of the run holds element j in its low nibble and
+    element j + 4 in its high nibble (rows have a multiple of 8 elements).
+    [R8]"""
     idx = np.asarray(idx, dtype=np.uint8)
-    return (idx[..., 0::2] | (idx[..., 1::2] << 4)).astype(np.uint8)
+    n = idx.shape[-1]
+    assert n % 8 == 0, "rows must hold a multiple of 8 elements"
+    g = idx.reshape(idx.shape[:-1] + (n // 8, 8))
+    out = g[..., 0:4] | (g[..., 4:8] << 4)
+    return out.reshape(idx.shape[:-1] + (n // 2,)).astype(np.uint8)
 
 
 def unpack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles.  [R8]"""
     codes = np.asarray(codes, dtype=np.uint8)
-    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
-    out[..., 0::2] = codes & 0x0F
-    out[..., 1::2] = codes >> 4
-    return out
+    nb = codes.shape[-1]
+    assert nb % 4 == 0, "rows must hold a multiple of 4 bytes"
+    c = codes.reshape(codes.shape[:-1] + (nb // 4, 4))
+    out = np.empty(c.shape[:-1] + (8,), dtype=np.uint8)
+    out[..., 0:4] = c & 0x0F
+    out[..., 4:8] = c >> 4
+    return out.reshape(codes.shape[:-1] + (nb * 2,))
 
 
 def double_quantize(absmax: np.ndarray, dq_block: int = 256):
@@ -288,8 +298,8 @@ def dequant_nf4_cols(codes, absmax, absmax2, cols, block=64, dq_block=256):
     n = codes.shape[0]
     k = codes.shape[1] * 2
     nbr = k // block
-    byte = codes[:, cols // 2]
-    nib = np.where((cols % 2)[None, :] == 0, byte & 0x0F, byte >> 4)
+    byte = codes[:, (cols // 8) * 4 + cols % 4]
+    nib = np.where((cols % 8)[None, :] < 4, byte & 0x0F, byte >> 4)
     bids = np.arange(n)[:, None] * nbr + (cols // block)[None, :]
     if dq_block:
         step = (np.asarray(absmax2, F32)[bids // dq_block] * DQ_INV127).astype(F32)

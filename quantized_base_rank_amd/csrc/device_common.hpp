@@ -111,54 +111,23 @@ __device__ __forceinline__ uint32_t lut_plane4(const uint32_t (&plane)[4], uint3
   return perm(b, a, pick);
 }
 
-// Decode one dword of 8 packed indices (element e in nibble e) into four
-// dwords of bf16 pairs.  Natural order: out[j] = (elem 2j | elem 2j+1 << 16).
+// Decode one dword of 8 packed indices into four dwords of bf16 pairs,
+// out[j] = (element 2j | element 2j+1 << 16).  Byte b of the dword holds
+// element b in its low nibble and element b + 4 in its high nibble, so the
+// low nibbles are elements 0..3 and the high nibbles elements 4..7, and one
+// byte interleave per output pair puts them in natural order.
 __device__ __forceinline__ u32x4 lut_decode8(const Lut16& t, uint32_t w) {
-  const uint32_t se = w & 0x07070707u;                              // e0 e2 e4 e6
-  const uint32_t so = (w >> 4) & 0x07070707u;                       // e1 e3 e5 e7
-  const uint32_t pe = ((w >> 1) & 0x04040404u) | 0x03020100u;       // bit 3 -> +4
-  const uint32_t po = ((w >> 5) & 0x04040404u) | 0x03020100u;
-  const uint32_t le = lut_plane4(t.lo, se, pe), he = lut_plane4(t.hi, se, pe);
-  const uint32_t lo = lut_plane4(t.lo, so, po), ho = lut_plane4(t.hi, so, po);
-  const uint32_t x = perm(he, le, 0x05010400u);  // e0 e2
-  const uint32_t y = perm(he, le, 0x07030602u);  // e4 e6
-  const uint32_t z = perm(ho, lo, 0x05010400u);  // e1 e3
-  const uint32_t v = perm(ho, lo, 0x07030602u);  // e5 e7
+  const uint32_t sl = w & 0x07070707u;                           // e0..e3, low 3 bits
+  const uint32_t sh = (w >> 4) & 0x07070707u;                    // e4..e7
+  const uint32_t pl = ((w >> 1) & 0x04040404u) | 0x03020100u;    // bit 3 -> +4
+  const uint32_t ph = ((w >> 5) & 0x04040404u) | 0x03020100u;
+  const uint32_t ll = lut_plane4(t.lo, sl, pl), hl = lut_plane4(t.hi, sl, pl);
+  const uint32_t lh = lut_plane4(t.lo, sh, ph), hh = lut_plane4(t.hi, sh, ph);
   u32x4 r;
-  r.x = perm(z, x, 0x05040100u);  // e0 e1
-  r.y = perm(z, x, 0x07060302u);  // e2 e3
-  r.z = perm(v, y, 0x05040100u);  // e4 e5
-  r.w = perm(v, y, 0x07060302u);  // e6 e7
-  return r;
-}
-
-// Same lookup with the elements delivered in the order 0 2 4 6 1 3 5 7
-// (four dwords: (e0,e2) (e4,e6) (e1,e3) (e5,e7)).  A matrix product over k is
-// unchanged when both operands use one permutation of k, so kernels that can
-// permute the other operand once (and reuse it many times) save four permutes
-// per eight weights.
-__device__ __forceinline__ u32x4 lut_decode8_eo(const Lut16& t, uint32_t w) {
-  const uint32_t se = w & 0x07070707u;
-  const uint32_t so = (w >> 4) & 0x07070707u;
-  const uint32_t pe = ((w >> 1) & 0x04040404u) | 0x03020100u;
-  const uint32_t po = ((w >> 5) & 0x04040404u) | 0x03020100u;
-  const uint32_t le = lut_plane4(t.lo, se, pe), he = lut_plane4(t.hi, se, pe);
-  const uint32_t lo = lut_plane4(t.lo, so, po), ho = lut_plane4(t.hi, so, po);
-  u32x4 r;
-  r.x = perm(he, le, 0x05010400u);
-  r.y = perm(he, le, 0x07030602u);
-  r.z = perm(ho, lo, 0x05010400u);
-  r.w = perm(ho, lo, 0x07030602u);
-  return r;
-}
-
-// The matching permutation of eight bf16 of the other operand.
-__device__ __forceinline__ u32x4 eo_permute(u32x4 d) {
-  u32x4 r;
-  r.x = perm(d.y, d.x, 0x05040100u);  // x0 x2
-  r.y = perm(d.w, d.z, 0x05040100u);  // x4 x6
-  r.z = perm(d.y, d.x, 0x07060302u);  // x1 x3
-  r.w = perm(d.w, d.z, 0x07060302u);  // x5 x7
+  r.x = perm(hl, ll, 0x05010400u);  // e0 e1
+  r.y = perm(hl, ll, 0x07030602u);  // e2 e3
+  r.z = perm(hh, lh, 0x05010400u);  // e4 e5
+  r.w = perm(hh, lh, 0x07030602u);  // e6 e7
   return r;
 }
 

@@ -45,8 +45,12 @@ __device__ __forceinline__ BlockParams load_piece_params(const WeightView& w, in
   p.b = 0u;
   return p;
 }
+// Table of a piece; a masked piece (ok false) gets all-zero constants, so
+// that it decodes to zeros (NF4: a zero scale; INT4: zero scale and offset).
 template <int FMT>
-__device__ __forceinline__ Lut16 piece_lut(const WeightView& w, BlockParams p) {
+__device__ __forceinline__ Lut16 piece_lut(const WeightView& w, BlockParams p, bool ok) {
+  p.a = ok ? p.a : 0u;
+  p.b = ok ? p.b : 0u;
   if (FMT == kFmtNF4) return lut_nf4(w.cb, nf4_params_scale(w, p));
   return lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.a & 0xFFFFu)),
                   half_bits_to_f32(static_cast<uint16_t>(p.a >> 16)));
@@ -157,8 +161,8 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     const int64_t last = M * r - 1;
     ur[i] = a.u[idx < last ? idx : last];
   }
-  // (4) weight codes and constants of all chunks, issued last so the loads
-  //     above complete first.  Thread (prow, pp) owns a 32-column piece of
+  // (4) weight codes and constants of all chunks, issued after the adapter
+  //     operands so that those complete first.  Thread (prow, pp) owns a 32-column piece of
   //     rows c*128 + q*64 + prow; four threads cover a row's 64 B, so each
   //     load instruction reads 16 row segments of 64 B.
   const int prow = tid >> 2, pp = tid & 3;
@@ -177,10 +181,23 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
       bp[c][q] = load_piece_params<FMT>(a.w, nrow, pcolc >> 5);
     }
 
+  // (5) the x tile and (narrow adapters) the A tile of this column tile, for
+  //     the fix-up that the tile's last workgroup runs; issued now so that
+  //     their latency is hidden (8 KB per workgroup, shared through L2 by
+  //     the tile's splits)
+  const int fm = tid >> 4;
+  const int fcl = (tid & 15) * 8;
+  const int64_t fkx = kc0 + fcl < K ? kc0 + fcl : K - 8;
+  const bool narrow = r <= 16 && a.pool == 1;  // one load of each kind per thread
+  const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (fm < M ? fm : M - 1) * K + fkx);
+  u32x4 av = u32x4{0u, 0u, 0u, 0u};
+  if (narrow)
+    av = *reinterpret_cast<const u32x4*>(a.A + static_cast<int64_t>(fm < r ? fm : r - 1) * K + fkx);
+
   // keep the staging below from being scheduled between the loads above
   __builtin_amdgcn_sched_barrier(0);
 
-  // (5) stage dY, the first B slice and u (masked here)
+  // (6) stage dY, the first B slice and u (masked here)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ch = i * 256 + tid;
@@ -196,7 +213,7 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
   }
   __syncthreads();
 
-  // (6) adapter partial du_p[m][j] = sum_{n in split} dY[m][n] B[n][j]
+  // (7) adapter partial du_p[m][j] = sum_{n in split} dY[m][n] B[n][j]
   float* du_part = a.du_part + (static_cast<int64_t>(tile) * a.splits + split) * (16 * r);
   for (int js = 0; js < jsub; ++js) {
     if (js > 0) {
@@ -226,47 +243,74 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     }
   }
 
-  // (7) dB[n][j] = s sum_m dY[m][n] u[m][j], rows [db0, db0 + db_rows) of the split
+  // (8) dB[n][j] = s sum_m dY[m][n] u[m][j], rows [db0, db0 + db_rows) of the split
   for (int idx = tid; idx < db_rows * r; idx += 256) {
     const int nn = db0 + idx / r, j = idx % r;
     if (nn >= nlen) break;
+    // all 32 operands are read before any is used (one LDS round trip)
+    float dv[16], uv[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      dv[m] = bf16_to_f32(s_dy[m * kGdRowsSplit + nn]);
+      uv[m] = s_u[m * r + j];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float t = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) t += bf16_to_f32(s_dy[m * kGdRowsSplit + nn]) * s_u[m * r + j];
+    for (int m = 0; m < 16; ++m) t += dv[m] * uv[m];
     a.dB[(nb0 + nn) * r + j] = f32_to_bf16(a.s * t);
   }
 
-  // (8) weight product dX_p[m][k] = sum_{n in split} dY[m][n] W[n][k]; chunk
+  // (9) weight product dX_p[m][k] = sum_{n in split} dY[m][n] W[n][k]; chunk
   //     c + 1 is decoded into the other buffer while chunk c feeds the MFMAs
   f32x4 acc[2];
   acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nchunks = static_cast<int>((nlen + kGdRowsChunk - 1) / kGdRowsChunk);
-  auto decode = [&](int c, uint8_t* wbuf) {
+  // Rows 2 apart start 16 banks apart: the store order alternates by row
+  // pair (store s writes 16-byte piece s ^ sw) so that the 16 lanes of a
+  // store hit distinct banks.  The pieces are swapped in registers with
+  // fixed indices, never by a run-time index into a register vector.
+  const uint32_t sw = (static_cast<uint32_t>(prow) >> 1) & 1u;
+  // All eight lookups are done before the first store: a store reads its
+  // data registers only when the LDS takes it, so a lookup that reuses them
+  // right after would wait for the store.
+  auto decode = [&](const u32x4 (&cwc)[2], const BlockParams (&bpc)[2], int c, uint8_t* wbuf) {
+    u32x4 d[2][4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int row = q * 64 + prow;
       const bool ok = do_dx && c * kGdRowsChunk + row < nlen && pcol_ok;
-      const Lut16 lut = piece_lut<FMT>(a.w, bp[c][q]);
-      uint8_t* dst = wbuf + row * kGdWStride + pp * 64;
-      // rows 2 apart start 16 banks apart: alternate the store order by row
-      // pair so that the 16 lanes of a store hit distinct banks
-      const int sw = (row >> 1) & 1;
+      const Lut16 lut = piece_lut<FMT>(a.w, bpc[q], ok);
+      const u32x4 cv = cwc[q];
+      d[q][0] = lut_decode8(lut, sw ? cv.y : cv.x);
+      d[q][1] = lut_decode8(lut, sw ? cv.x : cv.y);
+      d[q][2] = lut_decode8(lut, sw ? cv.w : cv.z);
+      d[q][3] = lut_decode8(lut, sw ? cv.z : cv.w);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ss = s ^ sw;
-        const u32x4 d = lut_decode8(lut, cw[c][q][ss]);
-        *reinterpret_cast<u32x4*>(dst + ss * 16) = ok ? d : u32x4{0, 0, 0, 0};
-      }
+    for (int q = 0; q < 2; ++q) {
+      uint8_t* dst = wbuf + (q * 64 + prow) * kGdWStride + pp * 64;
+      uint8_t* de = dst + (sw << 4);         // pieces 0, 2 (sw 0) or 1, 3 (sw 1)
+      uint8_t* dd = dst + ((sw ^ 1u) << 4);  // the other two
+      *reinterpret_cast<u32x4*>(de) = d[q][0];
+      *reinterpret_cast<u32x4*>(dd) = d[q][1];
+      *reinterpret_cast<u32x4*>(de + 32) = d[q][2];
+      *reinterpret_cast<u32x4*>(dd + 32) = d[q][3];
     }
   };
   if (do_dx) {
-    decode(0, s_lds);
+    decode(cw[0], bp[0], 0, s_lds);
     __syncthreads();
-#pragma unroll
-    for (int c = 0; c < kGdChunks; ++c) {
-      if (c >= nchunks) break;
+    // The chunk loop stays rolled.  A workgroup runs it once, so its
+    // instructions are fetched cold and code size costs about as much as
+    // the arithmetic; the rolled body is fetched once and then hits the
+    // instruction cache.  The codes of later chunks move down one slot per
+    // iteration so that every register index stays fixed.
+#pragma unroll 1
+    for (int c = 0; c < nchunks; ++c) {
       const uint8_t* wb = s_lds + (c & 1) * kWBuf;
-      if (c + 1 < nchunks) decode(c + 1, s_lds + ((c + 1) & 1) * kWBuf);
+      if (c + 1 < nchunks) decode(cw[1], bp[1], c + 1, s_lds + ((c + 1) & 1) * kWBuf);
       // D[k][m] += sum_n W[n][k] dY[m][n]; wave w owns columns [32w, 32w+32)
 #pragma unroll
       for (int ns = 0; ns < kGdRowsChunk / 32; ++ns) {
@@ -280,6 +324,13 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
         }
       }
       __syncthreads();
+#pragma unroll
+      for (int j = 1; j + 1 < kGdChunks; ++j) {
+        cw[j][0] = cw[j + 1][0];
+        cw[j][1] = cw[j + 1][1];
+        bp[j][0] = bp[j + 1][0];
+        bp[j][1] = bp[j + 1][1];
+      }
     }
     // D[16 k][16 m]: lane holds D[4g + v][l16]
     const rsrc_t pr = make_rsrc(a.partial);
@@ -303,16 +354,16 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
   const int64_t Ka = K >> ps;
   const int acols = a.pool == 1 ? ncol : ngrp;
   const int64_t ac0 = kc0 >> ps;
-  float* s_du = reinterpret_cast<float*>(s_lds);                 // [16][r]   8 KB max
+  float* s_du = reinterpret_cast<float*>(s_lds);                 // [r][16]   8 KB max
   float* s_px = reinterpret_cast<float*>(s_lds + 8192);          // [16][128] 8 KB
   uint16_t* s_a = reinterpret_cast<uint16_t*>(s_lds + 16384);    // [r][128] 32 KB max
-  const int m = tid >> 4;
-  const int cl = (tid & 15) * 8;
-  const int64_t kx = kc0 + cl < K ? kc0 + cl : K - 8;
-  const bool narrow = r <= 16 && a.pool == 1;  // one load of each kind per thread
+  const int m = fm;
+  const int cl = fcl;
+  const int64_t kx = fkx;
 
-  // issue every load before using any: split partials of dX, du partials,
-  // the x tile and (narrow adapters) the A tile
+  // issue every load before using any: split partials of dX and du.  Thread
+  // t reads du element (m = t % 16, j = t / 16), so that du lands in LDS
+  // transposed, [j][m].
   f32x4 pd[kGdPre][2];
   const rsrc_t pr = make_rsrc(a.partial);
 #pragma unroll
@@ -323,17 +374,12 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     pd[sp][1] = ld_sys16(pr, off + 16);
   }
   const float* dub = a.du_part + static_cast<int64_t>(tile) * S * (16 * r);
-  const int dlast = 16 * r - 1;
+  auto du_src = [&](int idx) { return (idx & 15) * r + (idx >> 4 < r ? idx >> 4 : r - 1); };
   float dv[kGdPre];
+  {
+    const int src = du_src(tid);
 #pragma unroll
-  for (int sp = 0; sp < kGdPre; ++sp)
-    dv[sp] = ld_sys(dub + (sp < S ? sp : S - 1) * (16 * r) + (tid < dlast ? tid : dlast));
-  const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (m < M ? m : M - 1) * K + kx);
-  u32x4 av = u32x4{0u, 0u, 0u, 0u};
-  if (narrow) {
-    const int j = tid >> 4;
-    av = *reinterpret_cast<const u32x4*>(a.A + static_cast<int64_t>(j < r ? j : r - 1) * Ka + ac0 +
-                                         (kc0 + cl < K ? cl : ncol - 8));
+    for (int sp = 0; sp < kGdPre; ++sp) dv[sp] = ld_sys(dub + (sp < S ? sp : S - 1) * (16 * r) + src);
   }
 
   // stage du (all splits), x (as fp32) and A
@@ -342,11 +388,11 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
 #pragma unroll
     for (int sp = 0; sp < kGdPre; ++sp)
       if (sp < S) v += dv[sp];
-    for (int sp = kGdPre; sp < S; ++sp) v += ld_sys(dub + sp * (16 * r) + (tid < dlast ? tid : dlast));
+    for (int sp = kGdPre; sp < S; ++sp) v += ld_sys(dub + sp * (16 * r) + du_src(tid));
     if (tid < 16 * r) s_du[tid] = a.s * v;
     for (int idx = tid + 256; idx < 16 * r; idx += 256) {
       float w = 0.0f;
-      for (int sp = 0; sp < S; ++sp) w += ld_sys(dub + sp * (16 * r) + idx);
+      for (int sp = 0; sp < S; ++sp) w += ld_sys(dub + sp * (16 * r) + du_src(idx));
       s_du[idx] = a.s * w;
     }
   }
@@ -359,8 +405,7 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     }
   }
   if (narrow) {
-    const int j = tid >> 4;
-    if (j < r) *reinterpret_cast<u32x4*>(&s_a[j * kGdCols + cl]) = av;
+    if (m < r) *reinterpret_cast<u32x4*>(&s_a[m * kGdCols + cl]) = av;
   } else {
     for (int idx = tid; idx < r * acols; idx += 256) {
       const int j = idx / acols, c = idx % acols;
@@ -378,14 +423,27 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     if (gg < ngrp) s_px[mm * kGdCols + gg] = pv;
     __syncthreads();
   }
-  // dA[j][c] = sum_m du[m][j] P[m][c]
-#pragma unroll 2
-  for (int idx = tid; idx < r * acols; idx += 256) {
-    const int j = idx / acols, c = idx % acols;
-    float t = 0.0f;
+  // dA[j][c] = sum_m du[m][j] P[m][c]: thread (c = t % 128) holds column c of
+  // P and forms rows j = t / 128, + 2, ... of dA
+  {
+    const int c = tid & (kGdCols - 1);
+    if (c < acols) {
+      float pc[16];
 #pragma unroll
-    for (int mm = 0; mm < 16; ++mm) t += s_du[mm * r + j] * s_px[mm * kGdCols + c];
-    a.dA[static_cast<int64_t>(j) * Ka + ac0 + c] = f32_to_bf16(t);
+      for (int mm = 0; mm < 16; ++mm) pc[mm] = s_px[mm * kGdCols + c];
+#pragma unroll 4
+      for (int j = tid >> 7; j < r; j += 2) {
+        const f32x4* dj = reinterpret_cast<const f32x4*>(s_du + j * 16);
+        float t = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 d = dj[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t += d[e] * pc[4 * q + e];
+        }
+        a.dA[static_cast<int64_t>(j) * Ka + ac0 + c] = f32_to_bf16(t);
+      }
+    }
   }
   if (do_dx && m < M && kc0 + cl < K) {
     float sum[8];
@@ -416,7 +474,7 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     if (a.pool == 1) {
 #pragma unroll 4
       for (int j = 0; j < r; ++j) {
-        const float d = s_du[m * r + j];
+        const float d = s_du[j * 16 + m];
         const u32x4 av8 = *reinterpret_cast<const u32x4*>(&s_a[j * kGdCols + cl]);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -429,7 +487,7 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int c = (cl + e) >> ps;
         float te = 0.0f;
-        for (int j = 0; j < r; ++j) te += s_du[m * r + j] * bf16_to_f32(s_a[j * kGdCols + c]);
+        for (int j = 0; j < r; ++j) te += s_du[j * 16 + m] * bf16_to_f32(s_a[j * kGdCols + c]);
         t[e] = te;
       }
     }

@@ -72,10 +72,13 @@ __global__ __launch_bounds__(256) void k_quant_nf4(const float* __restrict__ W, 
       for (int k = 0; k < 15; ++k) idx += (wd > thr[k]) ? 1u : 0u;
       nib[e] = (a == 0.0f) ? 7u : idx;
     }
+    // packed layout: byte j of each run of 8 elements holds element j in
+    // its low nibble and element j + 4 in its high nibble; lanes 2i and
+    // 2i + 1 hold elements 0..3 and 4..7 of run i
+    const uint32_t part = (nib[0] | (nib[1] << 8) | (nib[2] << 16) | (nib[3] << 24)) << ((li & 1) * 4);
+    const uint32_t word = part | static_cast<uint32_t>(__shfl_xor(static_cast<int>(part), 1, 64));
     if (b < n_blocks) {
-      const uint16_t packed =
-          static_cast<uint16_t>(nib[0] | (nib[1] << 4) | (nib[2] << 8) | (nib[3] << 12));
-      reinterpret_cast<uint16_t*>(codes + b * 32)[li] = packed;
+      if ((li & 1) == 0) reinterpret_cast<uint32_t*>(codes + b * 32)[li >> 1] = word;
       if (li == 0) {
         s_abs[local] = a;
         s_bad[local] = bad;
@@ -154,9 +157,12 @@ __global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ W,
     }
     nib[e] = static_cast<uint32_t>(q);
   }
+  // the packed layout of the NF4 quantizer: byte j of each run of 8 holds
+  // elements j (low nibble) and j + 4 (high nibble)
+  const uint32_t part = (nib[0] | (nib[1] << 8) | (nib[2] << 16) | (nib[3] << 24)) << ((li & 1) * 4);
+  const uint32_t word = part | static_cast<uint32_t>(__shfl_xor(static_cast<int>(part), 1, 64));
   if (grp < n_groups) {
-    reinterpret_cast<uint16_t*>(codes + grp * 16)[li] =
-        static_cast<uint16_t>(nib[0] | (nib[1] << 4) | (nib[2] << 8) | (nib[3] << 12));
+    if ((li & 1) == 0) reinterpret_cast<uint32_t*>(codes + grp * 16)[li >> 1] = word;
     if (li == 0) {
       scale[grp] = bad ? static_cast<uint16_t>(0x7E00u) : __builtin_bit_cast(uint16_t, alpha_h);
       zero[grp] = __builtin_bit_cast(uint16_t, beta_h);

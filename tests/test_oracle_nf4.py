@@ -180,10 +180,20 @@ def test_quantizer_tie_goes_to_lower_index(oracle):
 
 
 def test_nibble_packing_order(oracle):
-    idx = np.array([[1, 2, 3, 4, 15, 0]], np.uint8)
+    # byte j of each run of 8 holds element j (low nibble) and j + 4 (high)
+    idx = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 0]], np.uint8)
     packed = oracle.pack_nibbles(idx)
-    assert packed.tolist() == [[0x21, 0x43, 0x0F]]
+    assert packed.tolist() == [[0x51, 0x62, 0x73, 0x84, 0xD9, 0xEA, 0xFB, 0x0C]]
     assert np.array_equal(oracle.unpack_nibbles(packed), idx)
+    # the column sampler reads the same layout
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 16, size=(3, 64), dtype=np.uint8)
+    codes = oracle.pack_nibbles(q)
+    absmax = np.ones(3, np.float32)
+    cols = np.arange(64)
+    got = oracle.dequant_nf4_cols(codes, absmax, None, cols, block=64, dq_block=0)
+    c = oracle.nf4_codebook()
+    assert np.array_equal(got, oracle.bf16_bits_to_f64(oracle.f32_to_bf16_bits(c[q].astype(np.float32))))
 
 
 def test_quantizer_rejects_nonfinite_and_bad_shape(oracle):
