@@ -30,30 +30,23 @@ constexpr int kGdCols = 128;
 constexpr int kGdRowsChunk = 128;
 constexpr int kGdRowsSplit = 512;
 constexpr int kGdChunks = kGdRowsSplit / kGdRowsChunk;
-constexpr int kGdWStride = kGdCols * 2 + 32;  // 288 B: rows land 8 banks apart
-constexpr int kGdPre = 8;                     // split partials prefetched per thread
+constexpr int kGdCodeChunk = kGdRowsChunk * 64;  // packed codes of a chunk in LDS: 8 KB
+constexpr int kGdWStride = 64 * 2 + 16;          // wave tile row: 64 bf16 + 16 B pad (144 B)
+constexpr int kGdWTile = 64 * kGdWStride;        // one wave tile: 64 rows, 9 KB
+constexpr int kGdPre = 8;                        // split partials prefetched per thread
+
 
 // Raw decode constants of a 32-column piece of one row: NF4 -> its 64-block,
 // INT4 -> its group (a = scale | zero << 16).
+// Tables of one 64-column block; a masked block (ok false) gets all-zero
+// constants, so that it decodes to zeros (NF4: a zero scale; INT4: zero
+// scale and offset).
 template <int FMT>
-__device__ __forceinline__ BlockParams load_piece_params(const WeightView& w, int64_t row,
-                                                         int64_t col32) {
-  if (FMT == kFmtNF4) return load_block_params<kFmtNF4>(w, row, col32 >> 1, true);
-  const int64_t gi = row * (w.K >> 5) + col32;
-  BlockParams p;
-  p.a = static_cast<uint32_t>(w.scale[gi]) | (static_cast<uint32_t>(w.zero[gi]) << 16);
-  p.b = 0u;
-  return p;
-}
-// Table of a piece; a masked piece (ok false) gets all-zero constants, so
-// that it decodes to zeros (NF4: a zero scale; INT4: zero scale and offset).
-template <int FMT>
-__device__ __forceinline__ Lut16 piece_lut(const WeightView& w, BlockParams p, bool ok) {
+__device__ __forceinline__ void block_luts(const WeightView& w, BlockParams p, bool ok,
+                                           Lut16 (&lut)[2]) {
   p.a = ok ? p.a : 0u;
   p.b = ok ? p.b : 0u;
-  if (FMT == kFmtNF4) return lut_nf4(w.cb, nf4_params_scale(w, p));
-  return lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.a & 0xFFFFu)),
-                  half_bits_to_f32(static_cast<uint16_t>(p.a >> 16)));
+  luts_from_params<FMT>(w, p, lut);
 }
 
 // Bijection of workgroup ids: XCD x = id % 8 receives the x-th contiguous
@@ -66,14 +59,16 @@ __device__ __forceinline__ int gd_xcd_order(int bid, int n) {
 
 template <int FMT>
 __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
-  // LDS: two decoded-weight buffers 2 x 36 KB | dY slice 16 KB | B slice 16 KB |
-  // wave partials 4 KB | u 8 KB.  The fix-up reuses the first 48 KB.
-  constexpr int kWBuf = kGdRowsChunk * kGdWStride;        // 36864
-  constexpr int kOffDy = 2 * kWBuf;
+  // LDS: wave tiles 4 x 2 x 9 KB | dY slice 16 KB | B slice 16 KB | wave
+  // partials 4 KB | u 8 KB, and the packed codes 4 x 8 KB.  The fix-up
+  // reuses the first 48 KB.
+  constexpr int kOffW = 0;
+  constexpr int kOffDy = kOffW + 4 * 2 * kGdWTile;
   constexpr int kOffB = kOffDy + 16 * kGdRowsSplit * 2;
   constexpr int kOffF = kOffB + kGdRowsSplit * 16 * 2;
   constexpr int kOffU = kOffF + 4096;
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[kOffU + 16 * 128 * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_code[kGdChunks * kGdCodeChunk];
   __shared__ uint32_t s_ticket;
   uint16_t* s_dy = reinterpret_cast<uint16_t*>(s_lds + kOffDy);   // [16][512]
   uint8_t* s_b = s_lds + kOffB;                                   // [512][16] bf16, 32 B rows
@@ -161,25 +156,35 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     const int64_t last = M * r - 1;
     ur[i] = a.u[idx < last ? idx : last];
   }
-  // (4) weight codes and constants of all chunks, issued after the adapter
-  //     operands so that those complete first.  Thread (prow, pp) owns a 32-column piece of
-  //     rows c*128 + q*64 + prow; four threads cover a row's 64 B, so each
-  //     load instruction reads 16 row segments of 64 B.
-  const int prow = tid >> 2, pp = tid & 3;
-  const int64_t pcol = kc0 + pp * 32;
-  const bool pcol_ok = pcol < K;
-  const int64_t pcolc = pcol_ok ? pcol : kc0;
+  // (4) packed codes of all chunks, issued after the adapter operands so
+  //     that those complete first.  For chunk c and row half q, lane L of
+  //     wave w loads a 16-byte piece of row q*64 + 16w + L/4 of the chunk:
+  //     four lanes cover a row's 64 bytes, so every load instruction reads
+  //     whole row segments.  They go to LDS (s_code[c][row][64 B]) just
+  //     before the weight product, which reads them in another pattern.
+  const int hcol = wave & 1;   // this wave's 64 columns of the tile
+  const int vrow = wave >> 1;  // and 64 rows of each chunk
   u32x4 cw[kGdChunks][2];
-  BlockParams bp[kGdChunks][2];
 #pragma unroll
   for (int c = 0; c < kGdChunks; ++c)
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int64_t nl = c * kGdRowsChunk + q * 64 + prow;
+      const int rl = q * 64 + 16 * wave + (lane >> 2);
+      const int64_t nl = c * kGdRowsChunk + rl;
       const int64_t nrow = nb0 + (nl < nlen ? nl : nlen - 1);
-      cw[c][q] = *reinterpret_cast<const u32x4*>(a.w.codes + nrow * (K >> 1) + (pcolc >> 1));
-      bp[c][q] = load_piece_params<FMT>(a.w, nrow, pcolc >> 5);
+      int64_t bc = (kc0 >> 1) + (lane & 3) * 16;
+      bc = bc + 16 <= (K >> 1) ? bc : (K >> 1) - 16;
+      cw[c][q] = *reinterpret_cast<const u32x4*>(a.w.codes + nrow * (K >> 1) + bc);
     }
+  // decode constants of this lane's row of each chunk, in its 64-column block
+  const bool blk_ok = kc0 + 64 * hcol < K;
+  const int64_t blk = (kc0 >> 6) + (blk_ok ? hcol : 0);
+  BlockParams bp[kGdChunks];
+#pragma unroll
+  for (int c = 0; c < kGdChunks; ++c) {
+    const int64_t nl = c * kGdRowsChunk + vrow * 64 + lane;
+    bp[c] = load_block_params<FMT>(a.w, nb0 + (nl < nlen ? nl : nlen - 1), blk, true);
+  }
 
   // (5) the x tile and (narrow adapters) the A tile of this column tile, for
   //     the fix-up that the tile's last workgroup runs; issued now so that
@@ -261,85 +266,103 @@ __global__ __launch_bounds__(256) void k_gemv_dx(GemvDxArgs a) {
     a.dB[(nb0 + nn) * r + j] = f32_to_bf16(a.s * t);
   }
 
-  // (9) weight product dX_p[m][k] = sum_{n in split} dY[m][n] W[n][k]; chunk
-  //     c + 1 is decoded into the other buffer while chunk c feeds the MFMAs
-  f32x4 acc[2];
-  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // (9) weight product dX_p[m][k] = sum_{n in split} dY[m][n] W[n][k].
+  //     Wave (hcol, vrow) owns columns 64 hcol .. +63 of the tile and rows
+  //     64 vrow .. +63 of each chunk: every lane decodes one row of 64 into the
+  //     wave's own LDS tile, and the transposed LDS read turns 8 consecutive
+  //     rows of one column into an MFMA operand.  No other wave reads the
+  //     tile, so the chunk loop has no barrier; it is software pipelined
+  //     (the operands of chunk c are read before chunk c + 1 is decoded into
+  //     the other tile) and kept rolled, with the next chunk's constants
+  //     moving down one slot per iteration so that register indices stay
+  //     fixed.
+  f32x4 acc[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nchunks = static_cast<int>((nlen + kGdRowsChunk - 1) / kGdRowsChunk);
-  // Rows 2 apart start 16 banks apart: the store order alternates by row
-  // pair (store s writes 16-byte piece s ^ sw) so that the 16 lanes of a
-  // store hit distinct banks.  The pieces are swapped in registers with
-  // fixed indices, never by a run-time index into a register vector.
-  const uint32_t sw = (static_cast<uint32_t>(prow) >> 1) & 1u;
-  // All eight lookups are done before the first store: a store reads its
-  // data registers only when the LDS takes it, so a lookup that reuses them
-  // right after would wait for the store.
-  auto decode = [&](const u32x4 (&cwc)[2], const BlockParams (&bpc)[2], int c, uint8_t* wbuf) {
-    u32x4 d[2][4];
+  uint8_t* wtile = s_lds + kOffW + wave * 2 * kGdWTile;
+  const int rloc = vrow * 64 + lane;  // this lane's row within a chunk
+  const int csw = (rloc >> 1) & 3;    // rotation of its code pieces
+  auto read_codes = [&](int c, u32x4& c0, u32x4& c1) {
+    const uint8_t* crow = s_code + c * kGdCodeChunk + rloc * 64;
+    c0 = *reinterpret_cast<const u32x4*>(crow + (((2 * hcol) ^ csw) << 4));
+    c1 = *reinterpret_cast<const u32x4*>(crow + (((2 * hcol + 1) ^ csw) << 4));
+  };
+  auto decode = [&](int c, BlockParams p, const u32x4& c0, const u32x4& c1, uint8_t* dst_tile) {
+    const bool ok = do_dx && c * kGdRowsChunk + rloc < nlen && blk_ok;
+    Lut16 lut[2];
+    block_luts<FMT>(a.w, p, ok, lut);
+    u32x4 d[8];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = q * 64 + prow;
-      const bool ok = do_dx && c * kGdRowsChunk + row < nlen && pcol_ok;
-      const Lut16 lut = piece_lut<FMT>(a.w, bpc[q], ok);
-      const u32x4 cv = cwc[q];
-      d[q][0] = lut_decode8(lut, sw ? cv.y : cv.x);
-      d[q][1] = lut_decode8(lut, sw ? cv.x : cv.y);
-      d[q][2] = lut_decode8(lut, sw ? cv.w : cv.z);
-      d[q][3] = lut_decode8(lut, sw ? cv.z : cv.w);
+    for (int e = 0; e < 4; ++e) {
+      d[e] = lut_decode8(lut[0], c0[e]);
+      d[4 + e] = lut_decode8(lut[1], c1[e]);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* dst = dst_tile + lane * kGdWStride;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      uint8_t* dst = wbuf + (q * 64 + prow) * kGdWStride + pp * 64;
-      uint8_t* de = dst + (sw << 4);         // pieces 0, 2 (sw 0) or 1, 3 (sw 1)
-      uint8_t* dd = dst + ((sw ^ 1u) << 4);  // the other two
-      *reinterpret_cast<u32x4*>(de) = d[q][0];
-      *reinterpret_cast<u32x4*>(dd) = d[q][1];
-      *reinterpret_cast<u32x4*>(de + 32) = d[q][2];
-      *reinterpret_cast<u32x4*>(dd + 32) = d[q][3];
-    }
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(dst + e * 16) = d[e];
   };
   if (do_dx) {
-    decode(cw[0], bp[0], 0, s_lds);
+    // stage the codes; the 16-byte pieces of a row are stored rotated by
+    // bits 1..2 of the row, so that the decode's reads (one piece of each of
+    // 64 consecutive rows) spread over all banks
+#pragma unroll
+    for (int c = 0; c < kGdChunks; ++c)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rl = q * 64 + 16 * wave + (lane >> 2);
+        const int slot = (lane & 3) ^ ((rl >> 1) & 3);
+        *reinterpret_cast<u32x4*>(s_code + c * kGdCodeChunk + rl * 64 + slot * 16) = cw[c][q];
+      }
     __syncthreads();
-    // The chunk loop stays rolled.  A workgroup runs it once, so its
-    // instructions are fetched cold and code size costs about as much as
-    // the arithmetic; the rolled body is fetched once and then hits the
-    // instruction cache.  The codes of later chunks move down one slot per
-    // iteration so that every register index stays fixed.
+    {
+      u32x4 c0, c1;
+      read_codes(0, c0, c1);
+      decode(0, bp[0], c0, c1, wtile);
+    }
 #pragma unroll 1
     for (int c = 0; c < nchunks; ++c) {
-      const uint8_t* wb = s_lds + (c & 1) * kWBuf;
-      if (c + 1 < nchunks) decode(cw[1], bp[1], c + 1, s_lds + ((c + 1) & 1) * kWBuf);
-      // D[k][m] += sum_n W[n][k] dY[m][n]; wave w owns columns [32w, 32w+32)
+      const uint8_t* wt = wtile + (c & 1) * kGdWTile;
+      // the next chunk's codes first (LDS returns in order), then the
+      // operands of chunk c: dY (B operand) and the transposed weights
+      u32x4 nc0, nc1;
+      read_codes(c + 1 < nchunks ? c + 1 : c, nc0, nc1);
+      u32x4 bfr[2], af[2][4];
 #pragma unroll
-      for (int ns = 0; ns < kGdRowsChunk / 32; ++ns) {
-        const int nbase = ns * 32 + g * 8;
-        const u32x4 bfr =
-            *reinterpret_cast<const u32x4*>(&s_dy[l16 * kGdRowsSplit + c * kGdRowsChunk + nbase]);
+      for (int ns = 0; ns < 2; ++ns) {
+        bfr[ns] = *reinterpret_cast<const u32x4*>(
+            &s_dy[l16 * kGdRowsSplit + c * kGdRowsChunk + vrow * 64 + ns * 32 + g * 8]);
 #pragma unroll
-        for (int ksub = 0; ksub < 2; ++ksub) {
-          const u32x4 af = tr16_operand(wb, kGdWStride, nbase, wave * 32 + ksub * 16, l16);
-          acc[ksub] = mfma16(af, bfr, acc[ksub]);
-        }
+        for (int kt = 0; kt < 4; ++kt) af[ns][kt] = tr16_operand(wt, kGdWStride, ns * 32 + g * 8, kt * 16, l16);
       }
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 1 < nchunks) decode(c + 1, bp[1], nc0, nc1, wtile + ((c + 1) & 1) * kGdWTile);
 #pragma unroll
-      for (int j = 1; j + 1 < kGdChunks; ++j) {
-        cw[j][0] = cw[j + 1][0];
-        cw[j][1] = cw[j + 1][1];
-        bp[j][0] = bp[j + 1][0];
-        bp[j][1] = bp[j + 1][1];
-      }
+      for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acc[kt] = mfma16(af[ns][kt], bfr[ns], acc[kt]);
+#pragma unroll
+      for (int j = 1; j + 1 < kGdChunks; ++j) bp[j] = bp[j + 1];
     }
-    // D[16 k][16 m]: lane holds D[4g + v][l16]
-    const rsrc_t pr = make_rsrc(a.partial);
+    // add the two row halves (waves 2, 3 hand theirs to waves 0, 1 through
+    // the B slice, unused since du) and publish.  D[16 k][16 m]: lane
+    // holds D[4g + v][l16].
+    float* s_comb = reinterpret_cast<float*>(s_b);  // [2][64][4][4]
+    if (vrow == 1)
 #pragma unroll
-    for (int ksub = 0; ksub < 2; ++ksub) {
-      const int64_t k = kc0 + wave * 32 + ksub * 16 + 4 * g;
-      if (k < K)
-        st_sys16(pr, static_cast<uint32_t>(((static_cast<int64_t>(split) * 16 + l16) * K + k) * 4),
-                 acc[ksub]);
+      for (int kt = 0; kt < 4; ++kt)
+        *reinterpret_cast<f32x4*>(s_comb + ((hcol * 64 + lane) * 4 + kt) * 4) = acc[kt];
+    __syncthreads();
+    if (vrow == 0) {
+      const rsrc_t pr = make_rsrc(a.partial);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(s_comb + ((hcol * 64 + lane) * 4 + kt) * 4);
+        const f32x4 v = acc[kt] + o;
+        const int64_t k = kc0 + hcol * 64 + kt * 16 + 4 * g;
+        if (k < K)
+          st_sys16(pr, static_cast<uint32_t>(((static_cast<int64_t>(split) * 16 + l16) * K + k) * 4), v);
+      }
     }
   }
 
