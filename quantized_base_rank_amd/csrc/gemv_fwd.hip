@@ -8,8 +8,8 @@
 //
 // A workgroup owns 16 output features over a share of K of at most 4096
 // (the whole K for K <= 4096, so no cross-workgroup reduction at all).  Its
-// 8 waves (two per SIMD) take interleaved 256-wide K chunks, at most two
-// each.  Token (and adapter) chunks are staged through per-wave LDS slots
+// 16 waves (four per SIMD; 8 with u fused) take interleaved 256-wide K
+// chunks, one each (two with u fused).  Token (and adapter) chunks are staged through per-wave LDS slots
 // with whole-line direct-to-LDS loads; packed codes are read as whole row
 // segments and routed to their MFMA lanes with ds_bpermute; every lane
 // decodes one 64-element block of one row per chunk.  The plain adapter's
@@ -30,8 +30,16 @@ namespace {
 constexpr int kGfRows = 16;
 constexpr int kGfChunk = 256;
 constexpr int kGfKShare = 4096;  // K per workgroup at most (bounds activation re-reads)
-constexpr int kGfWaves = 8;
-constexpr int kGfPerWave = kGfKShare / kGfChunk / kGfWaves;  // chunks per wave (2)
+// Waves per workgroup: 16 for the plain product (one chunk each: a wave
+// starts as soon as its own chunk has landed, while later chunks still
+// stream in), 8 with u fused (two rounds of a token and an adapter chunk).
+template <bool FUSE_U>
+struct GfShape {
+  static constexpr int kWaves = FUSE_U ? 8 : 16;
+  static constexpr int kPerWave = kGfKShare / kGfChunk / kWaves;  // chunks per wave
+  static constexpr int kSlots = FUSE_U ? 2 : kPerWave;            // LDS slots per wave
+  static constexpr int kThreads = 64 * kWaves;
+};
 constexpr int kGfSlot = kGfRows * kGfChunk * 2;               // one staged chunk: 8 KB
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -54,6 +62,28 @@ __device__ __forceinline__ void stage_chunk(const uint16_t* src, int64_t ld, int
     k = k < kmax ? k : kmax - 8;
     __builtin_amdgcn_global_load_lds(src + rc * ld + k, (lds_ptr_t)(slot + t * 1024), 16, 0, 0);
   }
+}
+
+// The same chunk through registers: load_chunk_regs reads the pieces that
+// stage_chunk would place, store_chunk_regs writes them to the same slot
+// positions.  (Ordinary loads let the wave wait for exactly the data it
+// needs; after a direct-to-LDS load the compiler waits for every load
+// before any LDS access.)
+__device__ __forceinline__ void load_chunk_regs(const uint16_t* src, int64_t ld, int rows, int64_t k0,
+                                                int64_t kmax, int lane, u32x4 (&xr)[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int row = 2 * t + (lane >> 5);
+    const int q = (lane & 31) ^ (row & 15);
+    const int64_t rc = row < rows ? row : rows - 1;
+    int64_t k = k0 + q * 8;
+    k = k < kmax ? k : kmax - 8;
+    xr[t] = *reinterpret_cast<const u32x4*>(src + rc * ld + k);
+  }
+}
+__device__ __forceinline__ void store_chunk_regs(const u32x4 (&xr)[8], uint8_t* slot, int lane) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) *reinterpret_cast<u32x4*>(slot + t * 1024 + lane * 16) = xr[t];
 }
 
 // MFMA fragment of a staged chunk: row l16, logical piece q (8 bf16).
@@ -92,11 +122,15 @@ __device__ __forceinline__ void route_chunk_codes(const u32x4 (&raw)[2], int l16
 }
 
 template <int FMT, bool FUSE_U>
-__global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
+__global__ __launch_bounds__(GfShape<FUSE_U>::kThreads) void k_gemv_fwd(GemvFwdArgs a) {
+  constexpr int kGfWaves = GfShape<FUSE_U>::kWaves;
+  constexpr int kGfPerWave = GfShape<FUSE_U>::kPerWave;
+  constexpr int kNT = GfShape<FUSE_U>::kThreads;
+  constexpr int kAdapterIters = 2048 / kNT;  // 16 x 128 adapter elements at most
   // per wave: two 8 KB slots (token chunks i = 0, 1; or, with u fused, the
   // token and adapter chunk of one round); after the products the first
   // 2 KB of a wave's slots hold its partial y and u
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kGfWaves][2 * kGfSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kGfWaves][GfShape<FUSE_U>::kSlots * kGfSlot];
   __shared__ float s_fu[16 * 128];       // final u [16][r]
   __shared__ uint16_t s_b[16 * 128];     // B rows of this tile [16][r]
   __shared__ uint32_t s_ticket;
@@ -113,7 +147,7 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
   const int nch = static_cast<int>((krlen + kGfChunk - 1) / kGfChunk);
   const int64_t n0 = static_cast<int64_t>(tile) * kGfRows;
   uint8_t* slot0 = s_stage[wave];
-  uint8_t* slot1 = s_stage[wave] + kGfSlot;
+  uint8_t* slot1 = s_stage[wave] + (GfShape<FUSE_U>::kSlots > 1 ? kGfSlot : 0);
 
   // chunks of this wave (clamped; a chunk past the share is fully masked)
   int cc[kGfPerWave];
@@ -127,12 +161,12 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
   auto chunk_k0 = [&](int i) { return kr0 + static_cast<int64_t>(cc[i]) * kGfChunk; };
 
   // (1) adapter operands of the epilogue (small, L2-resident)
-  uint32_t breg[4];
-  float ureg[4];
+  uint32_t breg[kAdapterIters];
+  float ureg[kAdapterIters];
   if (a.adapter) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = i * 512 + tid;
+    for (int i = 0; i < kAdapterIters; ++i) {
+      const int idx = i * kNT + tid;
       const int nn = idx / r;
       const int64_t n = n0 + (nn < 16 ? nn : 15);
       breg[i] = a.B[(n < N ? n : N - 1) * r + idx % r];
@@ -142,15 +176,7 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
       }
     }
   }
-  // (2) token (and adapter) chunks straight into LDS
-  const int mrows = static_cast<int>(M < 16 ? M : 16);
-  const int arows = r < 16 ? r : 16;
-  stage_chunk(a.x, K, mrows, chunk_k0(0), K, slot0, lane);
-  if (FUSE_U)
-    stage_chunk(a.A, K, arows, chunk_k0(0), K, slot1, lane);
-  else
-    stage_chunk(a.x, K, mrows, chunk_k0(1), K, slot1, lane);
-  // (3) packed codes and block constants of both chunks (HBM stream)
+  // (2) packed codes and block constants of this wave's chunks (HBM stream)
   const int64_t rowc = n0 + l16 < N ? n0 + l16 : N - 1;
   u32x4 raw[kGfPerWave][2];
   BlockParams bp[kGfPerWave];
@@ -163,6 +189,23 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
     const int64_t kb = kr0 + (kl < krlen ? kl : 0);
     bp[i] = load_block_params<FMT>(a.w, rowc, kb >> 6, true);
   }
+  // (3) token (and adapter) chunks straight into LDS, issued after the codes
+  //     so that the decode (which needs only the codes) can start while the
+  //     chunks still stream in
+  //     (plain product, one chunk per wave: through registers)
+  const int mrows = static_cast<int>(M < 16 ? M : 16);
+  const int arows = r < 16 ? r : 16;
+  constexpr bool kRegX = !FUSE_U && kGfPerWave == 1;
+  u32x4 xr[8];
+  if (kRegX) {
+    load_chunk_regs(a.x, K, mrows, chunk_k0(0), K, lane, xr);
+  } else {
+    stage_chunk(a.x, K, mrows, chunk_k0(0), K, slot0, lane);
+    if (FUSE_U)
+      stage_chunk(a.A, K, arows, chunk_k0(0), K, slot1, lane);
+    else if (kGfPerWave > 1)
+      stage_chunk(a.x, K, mrows, chunk_k0(kGfPerWave - 1), K, slot1, lane);
+  }
   // keep every load above ahead of the first use (the scheduler would
   // otherwise sink some next to their use, one round trip each)
   __builtin_amdgcn_sched_barrier(0);
@@ -171,7 +214,25 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
   f32x4 accu = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kGfPerWave; ++i) {
-    // token (and adapter) fragments of this chunk
+    // the weights first: they need only the codes.  A chunk past the share
+    // decodes through an all-zero table.
+    u32x4 cw[2];
+    route_chunk_codes(raw[i], l16, g, cw);
+    Lut16 lut[2];
+    BlockParams p = bp[i];
+    p.a = vblk[i] ? p.a : 0u;
+    p.b = vblk[i] ? p.b : 0u;
+    luts_from_params<FMT>(a.w, p, lut);
+    u32x4 wf[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) wf[t] = lut_decode8(lut[t >> 2], cw[t >> 2][t & 3]);
+    // token (and adapter) fragments of this chunk.  Slots filled by
+    // direct-to-LDS loads are read only after an explicit wait for them: the
+    // compiler's own wait for such loads can be placed after the first read.
+    if (kRegX)
+      store_chunk_regs(xr, slot0, lane);
+    else
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint8_t* xs = (FUSE_U || i == 0) ? slot0 : slot1;
     u32x4 xf[8], af[8];
 #pragma unroll
@@ -186,14 +247,9 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
         stage_chunk(a.A, K, arows, chunk_k0(i + 1), K, slot1, lane);
       }
     }
-    u32x4 cw[2];
-    route_chunk_codes(raw[i], l16, g, cw);
-    Lut16 lut[2];
-    luts_from_params<FMT>(a.w, bp[i], lut);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const u32x4 wf = lut_decode8(lut[t >> 2], cw[t >> 2][t & 3]);
-      accy = mfma16(vblk[i] ? wf : u32x4{0, 0, 0, 0}, xf[t], accy);
+      accy = mfma16(wf[t], xf[t], accy);
       if (FUSE_U) accu = mfma16(xf[t], vblk[i] ? af[t] : u32x4{0, 0, 0, 0}, accu);
     }
   }
@@ -208,8 +264,8 @@ __global__ __launch_bounds__(512) void k_gemv_fwd(GemvFwdArgs a) {
   }
   if (a.adapter) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = i * 512 + tid;
+    for (int i = 0; i < kAdapterIters; ++i) {
+      const int idx = i * kNT + tid;
       if (idx < 16 * r) {
         s_b[idx] = static_cast<uint16_t>(breg[i]);
         if (!FUSE_U) s_fu[idx] = ureg[i];
@@ -296,7 +352,7 @@ int64_t gemv_fwd_partial_floats(int64_t N, int64_t K) {
 
 hipError_t launch_gemv_fwd(const GemvFwdArgs& a, int fmt, hipStream_t stream) {
   const int grid = gemv_fwd_tiles(a.w.N) * a.splits;
-  const dim3 block(64 * kGfWaves);
+  const dim3 block(a.fuse_u ? GfShape<true>::kThreads : GfShape<false>::kThreads);
   if (fmt == kFmtNF4) {
     if (a.fuse_u)
       hipLaunchKernelGGL((k_gemv_fwd<kFmtNF4, true>), dim3(grid), block, 0, stream, a);

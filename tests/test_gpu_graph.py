@@ -58,6 +58,6 @@ def test_graph_replays_match_eager(d_out, d_in, M, r):
         torch.cuda.synchronize()
         g.replay()
         got = snap()
-        for a, b in zip(eager, got):
-            assert np.array_equal(a, b), f"replay {rep} differs from eager"
+        for name, a, b in zip(("y", "dx", "dA", "dB", "u"), eager, got):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs from eager"
         del scratch
