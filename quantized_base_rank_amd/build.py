@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libqlin.so")
 
-SOURCES = ["api.hip", "quant.hip", "adapter.hip", "adapter_tn.hip", "fwd_gemm.hip", "dx_gemm.hip", "gemv_fwd.hip", "gemv_dx.hip",
+SOURCES = ["api.hip", "quant.hip", "adapter.hip", "adapter_qa.hip", "adapter_tn.hip", "fwd_gemm.hip", "dx_gemm.hip", "gemv_fwd.hip", "gemv_dx.hip",
            "codebook.cpp"]
 
 ARCH = "gfx950"

@@ -138,55 +138,6 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* __restrict_
   }
 }
 
-// ------------------------------------------------------ QA-LoRA (pooled) ops
-// P[m][g] = sum of x[m][32g .. 32g+31] (fp32); u[m][j] = sum_g P[m][g] A[j][g].
-// One workgroup per token row; the pooled row stays in LDS.
-__global__ __launch_bounds__(256) void k_qa_pool_u(QaArgs a) {
-  extern __shared__ float s_p[];  // [G]
-  const int64_t m = blockIdx.x;
-  const int tid = threadIdx.x;
-  const uint16_t* xr = a.x + m * a.K;
-  for (int64_t g = tid; g < a.G; g += 256) {
-    const uint16_t* xs = xr + g * a.pool;
-    float acc = 0.0f;
-    for (int i = 0; i < a.pool; ++i) acc += bf16_to_f32(xs[i]);
-    s_p[g] = acc;
-    if (a.P_out) a.P_out[m * a.G + g] = acc;
-  }
-  __syncthreads();
-  if (!a.u_out) return;
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int j = wave; j < a.r; j += 4) {
-    const uint16_t* ar = a.A + static_cast<int64_t>(j) * a.G;
-    float acc = 0.0f;
-    for (int64_t g = lane; g < a.G; g += 64) acc += s_p[g] * bf16_to_f32(ar[g]);
-    acc = warp_sum(acc);
-    if (lane == 0) a.u_out[m * a.r + j] = acc;
-  }
-}
-
-// Gq[m][g] = sum_j du[m][j] A[j][g]  (the pooled adapter's input gradient
-// before it is repeated over the group).
-__global__ __launch_bounds__(256) void k_qa_grad_in(QaArgs a) {
-  const int64_t m = blockIdx.y;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (g >= a.G) return;
-  const float* dur = a.du + m * a.r;
-  float acc = 0.0f;
-  for (int j = 0; j < a.r; ++j) acc += dur[j] * bf16_to_f32(a.A[static_cast<int64_t>(j) * a.G + g]);
-  a.Gq_out[m * a.G + g] = acc;
-}
-
-// dA[j][g] = sum_m du[m][j] P[m][g], fixed summation order over m.
-__global__ __launch_bounds__(256) void k_qa_dA(QaArgs a) {
-  const int j = blockIdx.y;
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (g >= a.G) return;
-  float acc = 0.0f;
-  for (int64_t m = 0; m < a.M; ++m) acc += a.du[m * a.r + j] * a.P_in[m * a.G + g];
-  a.dA_out[static_cast<int64_t>(j) * a.G + g] = f32_to_bf16(acc);
-}
-
 }  // namespace
 
 hipError_t launch_nt_skinny(const NtArgs& a, hipStream_t stream) {
@@ -204,24 +155,6 @@ hipError_t launch_transpose16(const uint16_t* in, int64_t rows, int64_t cols, ui
                               hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>((cols + 31) / 32), static_cast<uint32_t>((rows + 31) / 32));
   hipLaunchKernelGGL(k_transpose16, grid, dim3(256), 0, stream, in, rows, cols, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_qa_pool_u(const QaArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_qa_pool_u, dim3(static_cast<uint32_t>(a.M)), dim3(256),
-                     static_cast<uint32_t>(a.G * sizeof(float)), stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_qa_grad_in(const QaArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<uint32_t>((a.G + 255) / 256), static_cast<uint32_t>(a.M));
-  hipLaunchKernelGGL(k_qa_grad_in, grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_qa_dA(const QaArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<uint32_t>((a.G + 255) / 256), static_cast<uint32_t>(a.r));
-  hipLaunchKernelGGL(k_qa_dA, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

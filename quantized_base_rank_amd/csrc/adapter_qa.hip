@@ -1,0 +1,303 @@
+// Pooled-adapter products of the group-wise INT4 variant.  [QA-LoRA
+// abstract: the adapter of the group-wise variant sees the input summed over
+// each quantization group, so its rank-r products run on G = K / 32 pooled
+// features.]
+//
+//   P[m][g]  = sum_{i < 32} x[m][32 g + i]     u[m][j]  = sum_g P[m][g] A[j][g]
+//   dA[j][g] = sum_m du[m][j] P[m][g]          Gq[m][g] = sum_j du[m][j] A[j][g]
+//
+// The pool is the INT4 group (32), the only pooled case.  Every sum is taken
+// in a fixed order, so results are bit-identical from run to run.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace qlin {
+
+namespace {
+
+constexpr int kQaPool = 32;
+constexpr int kQaTokMax = 8;  // tokens per workgroup (pooling, input gradient)
+constexpr int kQaDaTile = 64;  // dA tile: 64 adapter rows x 64 groups
+constexpr int kQaDaBlk = 32;   // tokens staged per step of a dA partial
+constexpr int kQaMaxRank = 128;
+constexpr int kQaGiRows = 32;  // rows of A staged per step of the input gradient
+
+// P and u for a block of tokens.  In a pass, lane c loads the 16-byte piece
+// c of every token row of the block (a wave reads 1 KB contiguous per row)
+// and adds its 8 elements in order; the four neighbouring lanes that hold one group add
+// their sums pairwise in lane order.  u then reads each row of A once for all
+// tokens of the block: lanes run across groups and the lane sums are added
+// with a fixed butterfly (lane 0's result is stored).
+__global__ __launch_bounds__(256) void k_qa_pool_u(QaArgs a) {
+  extern __shared__ float s_p[];  // [tok][G]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tok = a.tok;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * tok;
+  const int64_t G = a.G, K = a.K;
+  const int64_t npiece = K / 8;
+  // one pass reads piece c of every token of the block (all loads issued
+  // before any is used), then reduces them
+  for (int64_t c0 = 0; c0 < npiece; c0 += 256) {
+    const int64_t c = c0 + tid;
+    const int64_t cc = c < npiece ? c : npiece - 1;
+    u32x4 w[kQaTokMax];
+#pragma unroll
+    for (int t = 0; t < kQaTokMax; ++t) {
+      const int64_t m = m0 + t;
+      const int64_t mc = t < tok && m < a.M ? m : a.M - 1;
+      w[t] = *reinterpret_cast<const u32x4*>(a.x + mc * K + cc * 8);
+    }
+#pragma unroll
+    for (int t = 0; t < kQaTokMax; ++t) {
+      if (t >= tok) break;
+      float v = bf16_lo(w[t].x);
+      v += bf16_hi(w[t].x);
+      v += bf16_lo(w[t].y);
+      v += bf16_hi(w[t].y);
+      v += bf16_lo(w[t].z);
+      v += bf16_hi(w[t].z);
+      v += bf16_lo(w[t].w);
+      v += bf16_hi(w[t].w);
+      // (lane 4q + 0 + lane 4q + 1) + (lane 4q + 2 + lane 4q + 3), the same
+      // value in all four lanes
+      const float v1 = __shfl_xor(v, 1, 64);
+      const float p = (lane & 1) ? v1 + v : v + v1;
+      const float p2 = __shfl_xor(p, 2, 64);
+      const float q = (lane & 2) ? p2 + p : p + p2;
+      const int64_t m = m0 + t;
+      if ((lane & 3) == 0 && c < npiece) {
+        const int64_t g = c >> 2;
+        s_p[t * G + g] = q;
+        if (a.P_out != nullptr && m < a.M) a.P_out[m * G + g] = q;
+      }
+    }
+  }
+  if (a.u_out == nullptr) return;
+  // A itself goes to LDS after the pooled block when it fits (rows 16-byte
+  // aligned), so that the loop below reads no global memory
+  uint16_t* s_A = reinterpret_cast<uint16_t*>(s_p + tok * G);
+  if (a.stage_a) {
+    const int64_t n16 = static_cast<int64_t>(a.r) * G / 8;
+#pragma unroll 4
+    for (int64_t i = tid; i < n16; i += 256)
+      reinterpret_cast<u32x4*>(s_A)[i] = reinterpret_cast<const u32x4*>(a.A)[i];
+  }
+  __syncthreads();
+  for (int j = wave; j < a.r; j += 4) {
+    const uint16_t* ar = a.stage_a ? s_A + static_cast<int64_t>(j) * G : a.A + static_cast<int64_t>(j) * G;
+    float acc[kQaTokMax];
+#pragma unroll
+    for (int t = 0; t < kQaTokMax; ++t) acc[t] = 0.0f;
+    for (int64_t g = lane; g < G; g += 64) {
+      const float av = bf16_to_f32(ar[g]);
+#pragma unroll
+      for (int t = 0; t < kQaTokMax; ++t)
+        if (t < tok) acc[t] += s_p[t * G + g] * av;
+    }
+#pragma unroll
+    for (int t = 0; t < kQaTokMax; ++t) {
+      if (t >= tok) break;
+      const float sum = warp_sum(acc[t]);
+      if (lane == 0 && m0 + t < a.M) a.u_out[(m0 + t) * a.r + j] = sum;
+    }
+  }
+}
+
+// Partial dA over one slice of tokens: workgroup (group tile, adapter-row
+// tile, slice) adds du[m][j] P[m][g] over the slice's tokens in increasing m
+// into part[slice][j][g].  The operands of 32 tokens at a time are staged
+// in LDS; each thread owns a 4 x 4 block of the 64 x 64 tile.
+__global__ __launch_bounds__(256) void k_qa_dA_part(QaArgs a) {
+  __shared__ __attribute__((aligned(16))) float s_du[kQaDaBlk][kQaDaTile];
+  __shared__ __attribute__((aligned(16))) float s_pp[kQaDaBlk][kQaDaTile];
+  const int tid = threadIdx.x;
+  const int64_t G = a.G;
+  const int r = a.r;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * kQaDaTile;
+  const int j0 = static_cast<int>(blockIdx.y) * kQaDaTile;
+  const int slice = static_cast<int>(blockIdx.z);
+  const int64_t per = (a.M + a.splits - 1) / a.splits;
+  const int64_t mb0 = slice * per;
+  const int64_t mb1 = mb0 + per < a.M ? mb0 + per : a.M;
+  const int tj = tid >> 4, tg = tid & 15;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[i][k] = 0.0f;
+  for (int64_t mb = mb0; mb < mb1; mb += kQaDaBlk) {
+#pragma unroll
+    for (int e = 0; e < (kQaDaBlk * kQaDaTile) / 256; ++e) {
+      const int idx = e * 256 + tid;
+      const int mm = idx / kQaDaTile, cc = idx % kQaDaTile;
+      const int64_t m = mb + mm;
+      const bool mok = m < mb1;
+      s_du[mm][cc] = mok && j0 + cc < r ? a.du[m * r + j0 + cc] : 0.0f;
+      s_pp[mm][cc] = mok && g0 + cc < G ? a.P_in[m * G + g0 + cc] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int mm = 0; mm < kQaDaBlk; ++mm) {
+      const f32x4 d = *reinterpret_cast<const f32x4*>(&s_du[mm][tj * 4]);
+      const f32x4 p = *reinterpret_cast<const f32x4*>(&s_pp[mm][tg * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] += d[i] * p[k];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = j0 + tj * 4 + i;
+    if (j >= r) continue;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t g = g0 + tg * 4 + k;
+      if (g < G) a.part[(static_cast<int64_t>(slice) * r + j) * G + g] = acc[i][k];
+    }
+  }
+}
+
+// dA[j][g] = the slices' partial sums, added in a fixed order: four
+// neighbouring lanes each add a quarter of the slices in slice order (loads
+// issued eight at a time), then the quarters are added pairwise in lane
+// order.
+__global__ __launch_bounds__(256) void k_qa_dA_sum(QaArgs a) {
+  const int64_t n = static_cast<int64_t>(a.r) * a.G;
+  const int lane = threadIdx.x & 63, qq = threadIdx.x & 3;
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 2;
+  const int64_t e = e0 < n ? e0 : n - 1;
+  const int per = (a.splits + 3) / 4;
+  const int s0 = qq * per;
+  const int s1 = s0 + per < a.splits ? s0 + per : a.splits;
+  float v = 0.0f;
+  for (int sp = s0; sp < s1; sp += 8) {
+    float t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = sp + i < s1 ? a.part[(sp + i) * n + e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (sp + i < s1) v += t[i];
+  }
+  const float v1 = __shfl_xor(v, 1, 64);
+  const float p = (lane & 1) ? v1 + v : v + v1;
+  const float p2 = __shfl_xor(p, 2, 64);
+  const float q = (lane & 2) ? p2 + p : p + p2;
+  if (qq == 0 && e0 < n) a.dA_out[e0] = f32_to_bf16(q);
+}
+
+// Gq[m][g] = sum_j du[m][j] A[j][g] (the pooled adapter's input gradient
+// before it is repeated over the group), for a block of 8 tokens and 256
+// groups: du of the block and the A tile (read with 16-byte loads, all issued
+// before use) are staged in LDS; one thread per group.
+__global__ __launch_bounds__(256) void k_qa_grad_in(QaArgs a) {
+  __shared__ float s_du[kQaTokMax * kQaMaxRank];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[kQaGiRows * 256];
+  const int tid = threadIdx.x;
+  const int tok = a.tok;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * tok;
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * 256;
+  const int64_t G = a.G;
+  const int r = a.r;
+  for (int idx = tid; idx < tok * r; idx += 256) {
+    const int t = idx / r, j = idx % r;
+    s_du[idx] = m0 + t < a.M ? a.du[(m0 + t) * r + j] : 0.0f;
+  }
+  const int64_t g = g0 + tid;
+  float acc[kQaTokMax];
+#pragma unroll
+  for (int t = 0; t < kQaTokMax; ++t) acc[t] = 0.0f;
+  // rows of A in blocks of 32: thread (row j, piece q) loads 8 groups, as
+  // one 16-byte load when rows are 16-byte aligned (G a multiple of 8)
+  const bool vec = (G & 7) == 0;
+  for (int jb = 0; jb < r; jb += kQaGiRows) {
+    u32x4 av[kQaGiRows * 32 / 256];
+#pragma unroll
+    for (int i = 0; i < kQaGiRows * 32 / 256; ++i) {
+      const int idx = i * 256 + tid;
+      const int j = jb + (idx >> 5), q = idx & 31;
+      const uint16_t* arow = a.A + static_cast<int64_t>(j < r ? j : r - 1) * G;
+      const int64_t gq = g0 + q * 8;
+      if (vec && gq + 8 <= G) {
+        av[i] = *reinterpret_cast<const u32x4*>(arow + gq);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = gq + e < G ? arow[gq + e] : 0u;
+        av[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      }
+    }
+    __syncthreads();  // the previous block's rows are consumed
+#pragma unroll
+    for (int i = 0; i < kQaGiRows * 32 / 256; ++i) {
+      const int idx = i * 256 + tid;
+      *reinterpret_cast<u32x4*>(&s_a[(idx >> 5) * 256 + (idx & 31) * 8]) = av[i];
+    }
+    __syncthreads();
+    const int jn = r - jb < kQaGiRows ? r - jb : kQaGiRows;
+    for (int jj = 0; jj < jn; ++jj) {
+      const float w = bf16_to_f32(s_a[jj * 256 + tid]);
+#pragma unroll
+      for (int t = 0; t < kQaTokMax; ++t)
+        if (t < tok) acc[t] += s_du[t * r + jb + jj] * w;
+    }
+  }
+  if (g >= G) return;
+#pragma unroll
+  for (int t = 0; t < kQaTokMax; ++t)
+    if (t < tok && m0 + t < a.M) a.Gq_out[(m0 + t) * G + g] = acc[t];
+}
+
+// Tokens per workgroup of the pooling kernel: the P block of all its tokens
+// sits in LDS (at most 64 KB).
+int qa_tokens(int64_t G) {
+  const int64_t t = 16384 / G;
+  return static_cast<int>(t < 1 ? 1 : (t > kQaTokMax ? kQaTokMax : t));
+}
+
+}  // namespace
+
+int qa_dA_splits(int64_t M) {
+  const int64_t s = (M + kQaDaBlk - 1) / kQaDaBlk;
+  return static_cast<int>(s < 1 ? 1 : (s > 64 ? 64 : s));
+}
+int64_t qa_dA_partial_floats(int64_t M, int32_t r, int64_t G) {
+  return static_cast<int64_t>(qa_dA_splits(M)) * r * G;
+}
+
+hipError_t launch_qa_pool_u(const QaArgs& in, hipStream_t stream) {
+  if (in.pool != kQaPool || in.K % kQaPool != 0) return hipErrorInvalidValue;
+  QaArgs a = in;
+  a.tok = qa_tokens(a.G);
+  size_t lds = static_cast<size_t>(a.tok) * a.G * sizeof(float);
+  if (lds > 65536) return hipErrorInvalidValue;
+  const size_t a_bytes = static_cast<size_t>(a.r) * a.G * sizeof(uint16_t);
+  a.stage_a = a.u_out != nullptr && a.G % 8 == 0 && lds + a_bytes <= 65536;
+  if (a.stage_a) lds += a_bytes;
+  const uint32_t grid = static_cast<uint32_t>((a.M + a.tok - 1) / a.tok);
+  hipLaunchKernelGGL(k_qa_pool_u, dim3(grid), dim3(256), static_cast<uint32_t>(lds), stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qa_dA(const QaArgs& in, hipStream_t stream) {
+  QaArgs a = in;
+  a.splits = qa_dA_splits(a.M);
+  dim3 grid(static_cast<uint32_t>((a.G + kQaDaTile - 1) / kQaDaTile),
+            static_cast<uint32_t>((a.r + kQaDaTile - 1) / kQaDaTile), static_cast<uint32_t>(a.splits));
+  hipLaunchKernelGGL(k_qa_dA_part, grid, dim3(256), 0, stream, a);
+  const int64_t n = static_cast<int64_t>(a.r) * a.G;
+  hipLaunchKernelGGL(k_qa_dA_sum, dim3(static_cast<uint32_t>((4 * n + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qa_grad_in(const QaArgs& in, hipStream_t stream) {
+  if (in.r > kQaMaxRank) return hipErrorInvalidValue;
+  QaArgs a = in;
+  a.tok = kQaTokMax;
+  dim3 grid(static_cast<uint32_t>((a.G + 255) / 256), static_cast<uint32_t>((a.M + a.tok - 1) / a.tok));
+  hipLaunchKernelGGL(k_qa_grad_in, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace qlin

@@ -138,6 +138,7 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
                                  gemv_dx_partial_floats(N, K) + gemv_dx_dupart_floats(N, K, r)});
   } else {
     partial = std::max<int64_t>(partial, fwd_gemm_partial_floats(M, N, p.fwd_splits));
+    if (pool > 1) partial = std::max<int64_t>(partial, qa_dA_partial_floats(M, r, G));
   }
   size_t off = 0;
   p.off_counters = off; off = align256(off + counters * sizeof(uint32_t));
@@ -386,6 +387,7 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     QLIN_TRY(launch_qa_pool_u(q, stream));
     q.P_in = q.P_out;
     q.dA_out = dA;
+    q.part = partial;
     QLIN_TRY(launch_qa_dA(q, stream));
     if (dx != nullptr) {
       Gq = ws_at<float>(workspace, p.off_Gq);

@@ -63,10 +63,14 @@ struct QaArgs {  // pooled-adapter helpers (QA-LoRA)
   float* u_out;       // [M][r]
   float* Gq_out;      // [M][G]
   uint16_t* dA_out;   // [r][G]
+  float* part;        // dA partial sums [splits][r][G]
   int64_t M, K, G;
   int32_t r, pool;
+  int32_t splits, tok, stage_a;  // set by the launchers
 };
 hipError_t launch_qa_pool_u(const QaArgs& a, hipStream_t stream);
+int qa_dA_splits(int64_t M);
+int64_t qa_dA_partial_floats(int64_t M, int32_t r, int64_t G);
 hipError_t launch_qa_grad_in(const QaArgs& a, hipStream_t stream);
 hipError_t launch_qa_dA(const QaArgs& a, hipStream_t stream);
 

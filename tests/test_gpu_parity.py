@@ -178,7 +178,8 @@ def test_layer_nf4(qb, oracle, d_out, d_in, M, r):
     (256, 1024, 8, 16, 1),
     (272, 1088, 300, 64, 1),
     (256, 1024, 16, 16, 32),    # QA-LoRA pooled adapter, weight-streaming
-    (528, 1088, 300, 64, 32),   # QA-LoRA pooled adapter, MFMA path
+    (528, 1088, 300, 64, 32),   # QA-LoRA pooled adapter, MFMA path (34 groups)
+    (272, 2048, 260, 16, 32),   # pooled, MFMA path, group count a multiple of 8
 ])
 def test_layer_int4(qb, oracle, d_out, d_in, M, r, pool):
     _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r, fmt="int4", pool=pool)
