@@ -11,8 +11,9 @@
 // 8 consecutive n of one column as one 16-byte MFMA operand.
 //
 // Tile: 256 columns of dX x 256 tokens per workgroup, 4 waves as 2 x 2 of
-// 128 x 128.  dY tiles stream into LDS with direct-to-LDS loads; both LDS
-// stages are double buffered.  The adapter term du A is 2*ceil(r/16) extra
+// 128 x 128.  The next step's dY tile and codes are loaded into registers
+// while the current step's products run and are written to LDS after them;
+// both LDS stages are double buffered.  The adapter term du A is 2*ceil(r/16) extra
 // MFMA k-steps (du split hi + lo), read from A^T [K][r].
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -62,7 +63,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   const int tiles_m = static_cast<int>((M + kTMx - 1) / kTMx);
   const int tiles_k = static_cast<int>((K + kTK - 1) / kTK);
   const int t = remap_xcd(static_cast<int>(blockIdx.x), tiles_m * tiles_k);
-  const int tm = t / tiles_k, tk = t % tiles_k;
+  // (uniform; said so, so that the buffer resource below stays scalar)
+  const int tm = __builtin_amdgcn_readfirstlane(t / tiles_k);
+  const int tk = __builtin_amdgcn_readfirstlane(t % tiles_k);
   const int64_t m0 = static_cast<int64_t>(tm) * kTMx, k0 = static_cast<int64_t>(tk) * kTK;
   const int64_t nsteps = (N + kNS - 1) / kNS;
 
@@ -77,19 +80,35 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  auto load_dy = [&](int64_t st, int buf) {
-    const int64_t nb = st * kNS;
+  // dY tile of a step (256 tokens x 64 rows of dY^T) through registers:
+  // lane L of wave w, instruction i holds 16 bytes of token row
+  // (4i + w) * 8 + L / 8, chunk (L % 8) XOR-swizzled by the row, and writes
+  // them where a whole-line direct-to-LDS load would have put them.  (After
+  // a direct-to-LDS load the compiler holds every later LDS read until the
+  // load lands, which would expose the next step's load latency.)
+  // The rows go through a buffer resource over the tile's tokens: one 32-bit
+  // offset per lane and a scalar offset per instruction (rows past M read as
+  // zero; their outputs are never stored).  A chunk past N reads the row's
+  // last 8 columns (those weight rows are masked to zero).
+  const int64_t dy_rows = M - m0 < kTMx ? M - m0 : kTMx;
+  const rsrc_t dyr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.dy + m0 * N), 0, static_cast<int>(dy_rows * N * 2), 0x00020000);
+  const int dy_lrow = wave * 8 + (lane >> 3);   // row in instruction 0; + 32 per instruction
+  const int dy_c = (lane & 7) ^ (dy_lrow & 7);  // this lane's chunk (32 rows keep row & 7)
+  u32x4 dyv[8];
+  auto load_dy = [&](int64_t st) {
+    int64_t n = st * kNS + dy_c * 8;
+    n = n < N ? n : N - 8;
+    const uint32_t voff = static_cast<uint32_t>((dy_lrow * N + n) * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = (i * 4 + wave) * 8 + (lane >> 3);  // 8 rows of 128 B per wave-instr
-      const int c = (lane & 7) ^ (row & 7);
-      int64_t m = m0 + row;
-      m = m < M ? m : M - 1;
-      int64_t n = nb + c * 8;
-      n = n < N ? n : N - 8;
-      __builtin_amdgcn_global_load_lds(a.dy + m * N + n,
-                                       (lds_ptr_t)(&s_dy[buf][(i * 4 + wave) * 1024]), 16, 0, 0);
-    }
+    for (int i = 0; i < 8; ++i)
+      dyv[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(dyr, voff, static_cast<int>(i * 32 * N * 2), 0));
+  };
+  auto store_dy = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(&s_dy[buf][(i * 4 + wave) * 1024 + lane * 16]) = dyv[i];
   };
 
   u32x4 cw[2];
@@ -143,9 +162,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     }
   };
 
-  load_dy(0, 0);
+  load_dy(0);
   load_codes(0);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  store_dy(0);
   decode_store(0);
   __syncthreads();
 
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     const int buf = static_cast<int>(st & 1);
     const bool more = st + 1 < nsteps;
     if (more) {
-      load_dy(st + 1, buf ^ 1);
+      load_dy(st + 1);
       load_codes(st + 1);
     }
     const uint8_t* wb = s_w[buf];
@@ -175,7 +194,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      store_dy(buf ^ 1);
       decode_store(buf ^ 1);
     }
     __syncthreads();
