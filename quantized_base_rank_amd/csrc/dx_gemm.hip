@@ -4,17 +4,21 @@
 //  dequantized weight; W itself receives no gradient.]
 //
 // The reduction runs over the output features n, i.e. across rows of the
-// packed weight, while every row decodes with its own per-block table.  So
-// each 64 x 256 weight slab is decoded cooperatively in its natural row
-// orientation (every thread: two rows x 32 columns, one table per row) and
-// written to LDS transposed as bf16 pairs [k][n, n+1]; the waves then read
-// 8 consecutive n of one column as one 16-byte MFMA operand.
+// packed weight.  Each 64 x 256 weight slab of a step is decoded in its
+// natural row orientation (wave w: columns [32 w, 32 w + 32) of the tile,
+// lane l: row l, one table per lane) and written to LDS row-major; the
+// transposing LDS read turns 8 consecutive rows of one column into an MFMA
+// operand.
 //
-// Tile: 256 columns of dX x 256 tokens per workgroup, 4 waves as 2 x 2 of
-// 128 x 128.  The next step's dY tile and codes are loaded into registers
-// while the current step's products run and are written to LDS after them;
-// both LDS stages are double buffered.  The adapter term du A is 2*ceil(r/16) extra
-// MFMA k-steps (du split hi + lo), read from A^T [K][r].
+// Tile: 256 columns of dX x 256 tokens per workgroup, 8 waves (two per SIMD)
+// each owning 128 columns x 64 tokens.  The two waves that share a SIMD work
+// in opposite order within a step (products then the next step's decode, or
+// the reverse), so that one wave's lookups overlap the other's products.
+// The next step's dY tile (buffer loads into registers) and the codes two
+// steps ahead load during the step; the dY tile goes to LDS at its end.  Both
+// LDS stages are double buffered, one barrier per step.  The adapter term
+// du A is 2*ceil(r/16) extra MFMA k-steps (du split hi + lo), read from A^T
+// [K][r].
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -22,16 +26,25 @@ namespace qlin {
 
 namespace {
 
-constexpr int kTK = 256;    // dX columns per tile
-constexpr int kTMx = 256;   // tokens per tile
-constexpr int kNS = 64;     // reduction rows per step
-constexpr int kStage = kTK * kNS * 2;  // 32 KB per operand per stage
+constexpr int kTK = 256;                  // dX columns per tile
+constexpr int kTMx = 256;                 // tokens per tile
+constexpr int kNS = 64;                   // reduction rows per step
+constexpr int kWRow = kTK * 2;            // one W row of the tile in LDS: 512 B
+constexpr int kWStage = kNS * kWRow;      // 32 KB
+constexpr int kDyStage = kTMx * kNS * 2;  // 32 KB
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// [row][64 bf16] rows of 128 B, 16-byte chunks XOR-swizzled by row
+// dY tile [m][64 bf16]: rows of 128 B, 16-byte chunks XOR-swizzled by row
 __device__ __forceinline__ uint32_t off64(int row, int chunk) {
   return static_cast<uint32_t>(row * 128 + ((chunk ^ (row & 7)) << 4));
+}
+
+// Position of the 16-byte piece c (columns 8c .. 8c+7) of W row r.  The
+// row term spreads the 16 consecutive rows that one write instruction covers
+// over 16 positions; the column term puts the two column halves read by one
+// transposing read (pieces 4j, 4j+1 and 4j+2, 4j+3) in different 128-byte
+// halves.
+__device__ __forceinline__ int wpos(int c, int r) {
+  return c ^ (((c >> 1) & 1) << 3) ^ (((r & 7) << 1) | ((r >> 3) & 1));
 }
 
 __device__ __forceinline__ int remap_xcd(int bid, int n) {
@@ -40,25 +53,33 @@ __device__ __forceinline__ int remap_xcd(int bid, int n) {
   return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
+// Codes and raw decode constants of one lane's 32-column piece of a step.
 template <int FMT>
-struct DxParams;
+struct StepCodes;
 template <>
-struct DxParams<kFmtNF4> {
-  BlockParams bp[2];  // raw: the scale is formed when the table is built
+struct StepCodes<kFmtNF4> {
+  u32x4 cw;
+  BlockParams bp;
+  bool valid;
 };
 template <>
-struct DxParams<kFmtINT4> {
-  uint32_t sz[2];
+struct StepCodes<kFmtINT4> {
+  u32x4 cw;
+  uint32_t sz;  // scale | zero << 16 of the piece's group
+  bool valid;
 };
 
 template <int FMT>
-__global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kStage];   // [k][n] bf16
-  __shared__ __attribute__((aligned(16))) uint8_t s_dy[2][kStage];  // [m][n] bf16
+__global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kWStage];    // [n][k] bf16, pieces at wpos
+  __shared__ __attribute__((aligned(16))) uint8_t s_dy[2][kDyStage];  // [m][n] bf16
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int wk = wave & 1, wm = wave >> 1;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, h = lane >> 5, l16 = lane & 15;
+  const int wk = wave & 1, wm = (wave >> 1) & 3;  // products: columns wk*128.., tokens wm*64..
+  const bool mfma_first = wave < 4;              // waves w and w + 4 share a SIMD
   const int64_t M = a.M, N = a.w.N, K = a.w.K;
   const int tiles_m = static_cast<int>((M + kTMx - 1) / kTMx);
   const int tiles_k = static_cast<int>((K + kTK - 1) / kTK);
@@ -69,134 +90,150 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   const int64_t m0 = static_cast<int64_t>(tm) * kTMx, k0 = static_cast<int64_t>(tk) * kTK;
   const int64_t nsteps = (N + kNS - 1) / kNS;
 
-  // decode assignment: rows 2p, 2p+1 of the step, columns [32 kq, 32 kq + 32)
-  const int p = tid & 31, kq = tid >> 5;
-  const int64_t kcol = k0 + kq * 32;
+  // decode assignment: row `lane` of each step, columns [32 wave, +32)
+  const int64_t kcol = k0 + wave * 32;
   const bool kvalid = kcol < K;
+  const int64_t kcc = kvalid ? kcol : k0;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  // dY tile of a step (256 tokens x 64 rows of dY^T) through registers:
-  // lane L of wave w, instruction i holds 16 bytes of token row
-  // (4i + w) * 8 + L / 8, chunk (L % 8) XOR-swizzled by the row, and writes
-  // them where a whole-line direct-to-LDS load would have put them.  (After
-  // a direct-to-LDS load the compiler holds every later LDS read until the
-  // load lands, which would expose the next step's load latency.)
-  // The rows go through a buffer resource over the tile's tokens: one 32-bit
-  // offset per lane and a scalar offset per instruction (rows past M read as
-  // zero; their outputs are never stored).  A chunk past N reads the row's
-  // last 8 columns (those weight rows are masked to zero).
+  // dY tile of a step (256 tokens x 64 rows of dY^T) through registers from a
+  // buffer resource over the tile's tokens: instruction i of lane L, wave w
+  // holds 16 bytes of token row 64 i + 8 w + L / 8, chunk (L % 8) XOR the row,
+  // and writes them where a whole-line direct-to-LDS load would put them.
+  // Rows past M read as zero (their outputs are never stored); a chunk past
+  // N reads the row's last 8 columns (those weight rows decode to zero).
   const int64_t dy_rows = M - m0 < kTMx ? M - m0 : kTMx;
   const rsrc_t dyr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.dy + m0 * N), 0, static_cast<int>(dy_rows * N * 2), 0x00020000);
-  const int dy_lrow = wave * 8 + (lane >> 3);   // row in instruction 0; + 32 per instruction
-  const int dy_c = (lane & 7) ^ (dy_lrow & 7);  // this lane's chunk (32 rows keep row & 7)
-  u32x4 dyv[8];
+  const int dy_lrow = wave * 8 + (lane >> 3);
+  const int dy_c = (lane & 7) ^ (dy_lrow & 7);
+  u32x4 dyv[4];
   auto load_dy = [&](int64_t st) {
     int64_t n = st * kNS + dy_c * 8;
-    n = n < N ? n : N - 8;
+    n = n < N ? n : N - 8;  // also clamps a step past the last
     const uint32_t voff = static_cast<uint32_t>((dy_lrow * N + n) * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       dyv[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(dyr, voff, static_cast<int>(i * 32 * N * 2), 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(dyr, voff, static_cast<int>(i * 64 * N * 2), 0));
   };
   auto store_dy = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(&s_dy[buf][(i * 4 + wave) * 1024 + lane * 16]) = dyv[i];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&s_dy[buf][(i * 8 + wave) * 1024 + lane * 16]) = dyv[i];
   };
 
-  u32x4 cw[2];
-  DxParams<FMT> prm;
-  bool rvalid[2];
-  auto load_codes = [&](int64_t st) {
+  auto load_codes = [&](int64_t st, StepCodes<FMT>& sc) {
+    const int64_t n = st * kNS + lane;
+    sc.valid = kvalid && n < N;
+    // unconditional loads from clamped addresses; invalid rows decode to zero
+    const int64_t nc = n < N ? n : N - 1;
+    sc.cw = *reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (kcc >> 1));
+    if constexpr (FMT == kFmtNF4) {
+      sc.bp = load_block_params<kFmtNF4>(a.w, nc, kcc >> 6, true);
+    } else {
+      const int64_t gi = nc * (K >> 5) + (kcc >> 5);
+      sc.sz = static_cast<uint32_t>(a.w.scale[gi]) | (static_cast<uint32_t>(a.w.zero[gi]) << 16);
+    }
+  };
+  // one table per lane (an invalid row gets all-zero constants), 4 lookups
+  // of 8, 16-byte writes to the lane's row
+  auto decode = [&](const StepCodes<FMT>& sc, uint8_t* wt) {
+    Lut16 lut;
+    if constexpr (FMT == kFmtNF4) {
+      BlockParams bp = sc.bp;
+      bp.a = sc.valid ? bp.a : 0u;
+      bp.b = sc.valid ? bp.b : 0u;
+      lut = lut_nf4(a.w.cb, nf4_params_scale(a.w, bp));
+    } else {
+      const uint32_t sz = sc.valid ? sc.sz : 0u;
+      lut = lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
+                     half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
+    }
+    u32x4 d[4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int64_t n = st * kNS + 2 * p + r;
-      rvalid[r] = kvalid && n < N;
-      // unconditional loads from clamped addresses; invalid rows are masked at decode
-      const int64_t nc = n < N ? n : N - 1;
-      const int64_t kc = kvalid ? kcol : 0;
-      cw[r] = *reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (kc >> 1));
-      if constexpr (FMT == kFmtNF4) {
-        prm.bp[r] = load_block_params<kFmtNF4>(a.w, nc, kc >> 6, true);
-      } else {
-        const int64_t gi = nc * (K >> 5) + (kc >> 5);
-        prm.sz[r] = static_cast<uint32_t>(a.w.scale[gi]) | (static_cast<uint32_t>(a.w.zero[gi]) << 16);
-      }
+    for (int q = 0; q < 4; ++q) d[q] = lut_decode8(lut, sc.cw[q]);
+    uint8_t* row = wt + lane * kWRow;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4*>(row + (wpos(4 * wave + q, lane) << 4)) = d[q];
+  };
+
+  // MFMA operand: rows nb .. nb+7 of column col0 + (lane % 16) of a W tile,
+  // two transposing reads of 4 rows.  Within a step, rows nb = 16 nn + 8 h +
+  // (lane % 16) / 4 (+ 4) keep their row bits 0..3 for every nn, so the
+  // positions depend on nn only through an immediate offset of nn * 16 rows:
+  // the byte offsets for nn = 0 are formed once.
+  uint32_t wofs[2][4];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = wk * 128 + i * 32 + (l32 & 16) + 4 * (l16 & 3);
+      const int c = col >> 3, half8 = ((col >> 2) & 1) * 8;
+      const int r = 8 * h + (l16 >> 2) + 4 * x;
+      wofs[x][i] = static_cast<uint32_t>(r * kWRow + (wpos(c, r) << 4) + half8);
+    }
+  // D[k][m] += sum_n W^T[k][n] dY^T[n][m] over a step: lane (l32, h) of the
+  // A operand holds 8 rows of column k, of the B operand 8 rows of token m
+  const int dyx = h ^ (l32 & 7);  // chunk 2 nn + h of row ... + l32 sits at (2 nn) ^ dyx
+  // The operands of sub-step nn + 1 are read before the products of nn, so
+  // that their LDS latency overlaps those products.
+  auto read_ops = [&](const uint8_t* wt, const uint8_t* db, int nn, u32x4 (&af)[4], u32x4 (&bf)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x2 lo = ds_read_tr16(wt + nn * 16 * kWRow + wofs[0][i]);
+      const u32x2 hi = ds_read_tr16(wt + nn * 16 * kWRow + wofs[1][i]);
+      af[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      bf[j] = *reinterpret_cast<const u32x4*>(db + (wm * 64 + j * 32 + l32) * 128 + (((2 * nn) ^ dyx) << 4));
+  };
+  auto products = [&](int buf) {
+    const uint8_t* wt = s_w[buf];
+    const uint8_t* db = s_dy[buf];
+    u32x4 af[2][4], bf[2][2];
+    read_ops(wt, db, 0, af[0], bf[0]);
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int cur = nn & 1;
+      if (nn + 1 < 4) read_ops(wt, db, nn + 1, af[cur ^ 1], bf[cur ^ 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  auto decode_store = [&](int buf) {
-    Lut16 lut[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      if constexpr (FMT == kFmtNF4)
-        lut[r] = lut_nf4(a.w.cb, nf4_params_scale(a.w, prm.bp[r]));
-      else
-        lut[r] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(prm.sz[r] & 0xFFFFu)),
-                          half_bits_to_f32(static_cast<uint16_t>(prm.sz[r] >> 16)));
-    }
-    uint8_t* wb = s_w[buf];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 d0 = lut_decode8(lut[0], cw[0][q]);
-      u32x4 d1 = lut_decode8(lut[1], cw[1][q]);
-      if (!rvalid[0]) d0 = u32x4{0, 0, 0, 0};
-      if (!rvalid[1]) d1 = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // columns kq*32 + 8q + 2e and +1: pairs (row 2p, row 2p+1)
-        const uint32_t lo = perm(d1[e], d0[e], 0x05040100u);
-        const uint32_t hi = perm(d1[e], d0[e], 0x07060302u);
-        const int kr = kq * 32 + 8 * q + 2 * e;
-        const int chunk = p >> 2, within = (p & 3) * 4;
-        *reinterpret_cast<uint32_t*>(wb + off64(kr, chunk) + within) = lo;
-        *reinterpret_cast<uint32_t*>(wb + off64(kr + 1, chunk) + within) = hi;
-      }
-    }
-  };
-
+  StepCodes<FMT> sc_next, sc_after;
   load_dy(0);
-  load_codes(0);
+  load_codes(0, sc_next);
   store_dy(0);
-  decode_store(0);
+  decode(sc_next, s_w[0]);
+  if (nsteps > 1) load_codes(1, sc_next);
   __syncthreads();
 
   for (int64_t st = 0; st < nsteps; ++st) {
     const int buf = static_cast<int>(st & 1);
     const bool more = st + 1 < nsteps;
-    if (more) {
-      load_dy(st + 1);
-      load_codes(st + 1);
-    }
-    const uint8_t* wb = s_w[buf];
-    const uint8_t* db = s_dy[buf];
-#pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int chunk = 2 * nn + h;
-      u32x4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(wb + off64(wk * 128 + i * 32 + l32, chunk));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(db + off64(wm * 128 + j * 32 + l32, chunk));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) {
-      store_dy(buf ^ 1);
-      decode_store(buf ^ 1);
-    }
+    // unconditional (clamped) loads: with a fixed number of loads per step
+    // the compiler waits for exactly the older ones it needs
+    load_dy(st + 1);
+    load_codes(st + 2, sc_after);
+    // one copy of the products; the decode sits before them in waves 4..7
+    // and after them in waves 0..3 (a scalar branch either way)
+    if (more && !mfma_first) decode(sc_next, s_w[buf ^ 1]);
+    products(buf);
+    if (more && mfma_first) decode(sc_next, s_w[buf ^ 1]);
+    if (more) store_dy(buf ^ 1);
+    sc_next = sc_after;
     __syncthreads();
   }
 
@@ -223,8 +260,8 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         af[i] = u32x4{v[0], v[1], v[2], v[3]};
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int64_t m = m0 + wm * 128 + j * 32 + l32;
+      for (int j = 0; j < 2; ++j) {
+        int64_t m = m0 + wm * 64 + j * 32 + l32;
         m = m < M ? m : M - 1;
         const float* dr = a.du + m * rr;
         float hv[8], lv[8];
@@ -254,8 +291,8 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + wm * 128 + j * 32 + l32;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t m = m0 + wm * 64 + j * 32 + l32;
       if (m >= M) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -283,9 +320,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 hipError_t launch_dx_gemm(const DxArgs& a, int fmt, hipStream_t stream) {
   const int grid = static_cast<int>(((a.M + kTMx - 1) / kTMx) * ((a.w.K + kTK - 1) / kTK));
   if (fmt == kFmtNF4)
-    hipLaunchKernelGGL(k_dx_gemm<kFmtNF4>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_dx_gemm<kFmtNF4>, dim3(grid), dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_dx_gemm<kFmtINT4>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_dx_gemm<kFmtINT4>, dim3(grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
