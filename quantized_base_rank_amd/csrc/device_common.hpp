@@ -319,6 +319,9 @@ __device__ __forceinline__ void st_sys16(rsrc_t r, uint32_t off, f32x4 v) {
 __device__ __forceinline__ f32x4 ld_sys16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
 }
+__device__ __forceinline__ f32x2 ld_sys8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent));
+}
 
 // Waits until this workgroup's write-through stores are acknowledged, then
 // takes a ticket on `counter` (one per output tile).  Returns the ticket in

@@ -164,6 +164,9 @@ def _check(oracle, got, ref, keys=("y", "u", "dX", "dA", "dB")):
     (336, 1088, 1, 16),       # weight-streaming path, ragged splits
     (336, 1088, 5, 16),
     (4096, 4096, 16, 16),     # q_proj shape, decode-sized batch
+    (512, 1024, 7, 64),       # weight-streaming, adapter wider than 16 (extra du rounds)
+    (256, 512, 16, 128),      # weight-streaming, widest adapter
+    (4608, 512, 4, 16),       # weight-streaming, 9 row splits (two fix-up batches)
     (528, 320, 300, 64),      # MFMA path: 2 + ragged tiles, K tail of 64
     (512, 1024, 17, 8),       # just above the weight-streaming threshold
     (1040, 768, 513, 48),
