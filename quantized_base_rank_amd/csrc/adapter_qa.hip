@@ -22,52 +22,58 @@ constexpr int kQaDaBlk = 32;   // tokens staged per step of a dA partial
 constexpr int kQaMaxRank = 128;
 constexpr int kQaGiRows = 32;  // rows of A staged per step of the input gradient
 
-// P and u for a block of tokens.  In a pass, lane c loads the 16-byte piece
-// c of every token row of the block (a wave reads 1 KB contiguous per row)
-// and adds its 8 elements in order; the four neighbouring lanes that hold one group add
-// their sums pairwise in lane order.  u then reads each row of A once for all
-// tokens of the block: lanes run across groups and the lane sums are added
-// with a fixed butterfly (lane 0's result is stored).
-__global__ __launch_bounds__(256) void k_qa_pool_u(QaArgs a) {
+// P and u for a block of tokens (1024 threads).  A pass loads 8 16-byte
+// pieces per thread, flattened over (token, piece) so that every load of
+// the pass is in flight at once (two passes cover 8 tokens of K = 11008);
+// each thread adds its pieces' 8 elements in order and the four
+// neighbouring lanes that hold one group add their sums pairwise in lane
+// order.  u then reads each row of A once for all tokens of the block:
+// lanes run across groups and the lane sums are added with a fixed
+// butterfly (lane 0's result is stored).
+constexpr int kQaThreads = 1024;
+constexpr int kQaPer = 8;  // loads per thread and pass
+__global__ __launch_bounds__(kQaThreads) void k_qa_pool_u(QaArgs a) {
   extern __shared__ float s_p[];  // [tok][G]
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tok = a.tok;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * tok;
   const int64_t G = a.G, K = a.K;
-  const int64_t npiece = K / 8;
-  // one pass reads piece c of every token of the block (all loads issued
-  // before any is used), then reduces them
-  for (int64_t c0 = 0; c0 < npiece; c0 += 256) {
-    const int64_t c = c0 + tid;
-    const int64_t cc = c < npiece ? c : npiece - 1;
-    u32x4 w[kQaTokMax];
+  const int npiece = static_cast<int>(K / 8);  // 16-byte pieces per token row (a multiple of 4)
+  const int total = tok * npiece;
+  for (int p0 = 0; p0 < total; p0 += kQaThreads * kQaPer) {
+    u32x4 w[kQaPer];
+    int tk[kQaPer], pc[kQaPer];
 #pragma unroll
-    for (int t = 0; t < kQaTokMax; ++t) {
-      const int64_t m = m0 + t;
-      const int64_t mc = t < tok && m < a.M ? m : a.M - 1;
-      w[t] = *reinterpret_cast<const u32x4*>(a.x + mc * K + cc * 8);
+    for (int i = 0; i < kQaPer; ++i) {
+      const int pf = p0 + i * kQaThreads + tid;
+      const int pcl = pf < total ? pf : total - 1;
+      tk[i] = pcl / npiece;
+      pc[i] = pcl - tk[i] * npiece;
+      const int64_t m = m0 + tk[i];
+      w[i] = *reinterpret_cast<const u32x4*>(a.x + (m < a.M ? m : a.M - 1) * K + static_cast<int64_t>(pc[i]) * 8);
     }
 #pragma unroll
-    for (int t = 0; t < kQaTokMax; ++t) {
-      if (t >= tok) break;
-      float v = bf16_lo(w[t].x);
-      v += bf16_hi(w[t].x);
-      v += bf16_lo(w[t].y);
-      v += bf16_hi(w[t].y);
-      v += bf16_lo(w[t].z);
-      v += bf16_hi(w[t].z);
-      v += bf16_lo(w[t].w);
-      v += bf16_hi(w[t].w);
+    for (int i = 0; i < kQaPer; ++i) {
+      float v = bf16_lo(w[i].x);
+      v += bf16_hi(w[i].x);
+      v += bf16_lo(w[i].y);
+      v += bf16_hi(w[i].y);
+      v += bf16_lo(w[i].z);
+      v += bf16_hi(w[i].z);
+      v += bf16_lo(w[i].w);
+      v += bf16_hi(w[i].w);
       // (lane 4q + 0 + lane 4q + 1) + (lane 4q + 2 + lane 4q + 3), the same
       // value in all four lanes
       const float v1 = __shfl_xor(v, 1, 64);
-      const float p = (lane & 1) ? v1 + v : v + v1;
-      const float p2 = __shfl_xor(p, 2, 64);
-      const float q = (lane & 2) ? p2 + p : p + p2;
-      const int64_t m = m0 + t;
-      if ((lane & 3) == 0 && c < npiece) {
-        const int64_t g = c >> 2;
-        s_p[t * G + g] = q;
+      const float q1 = (lane & 1) ? v1 + v : v + v1;
+      const float q2 = __shfl_xor(q1, 2, 64);
+      const float q = (lane & 2) ? q2 + q1 : q1 + q2;
+      const int pf = p0 + i * kQaThreads + tid;
+      const int64_t m = m0 + tk[i];
+      if ((lane & 3) == 0 && pf < total) {
+        const int64_t g = pc[i] >> 2;
+        s_p[tk[i] * G + g] = q;
         if (a.P_out != nullptr && m < a.M) a.P_out[m * G + g] = q;
       }
     }
@@ -79,11 +85,11 @@ __global__ __launch_bounds__(256) void k_qa_pool_u(QaArgs a) {
   if (a.stage_a) {
     const int64_t n16 = static_cast<int64_t>(a.r) * G / 8;
 #pragma unroll 4
-    for (int64_t i = tid; i < n16; i += 256)
+    for (int64_t i = tid; i < n16; i += kQaThreads)
       reinterpret_cast<u32x4*>(s_A)[i] = reinterpret_cast<const u32x4*>(a.A)[i];
   }
   __syncthreads();
-  for (int j = wave; j < a.r; j += 4) {
+  for (int j = wave; j < a.r; j += kQaThreads / 64) {
     const uint16_t* ar = a.stage_a ? s_A + static_cast<int64_t>(j) * G : a.A + static_cast<int64_t>(j) * G;
     float acc[kQaTokMax];
 #pragma unroll
@@ -200,9 +206,14 @@ __global__ __launch_bounds__(256) void k_qa_grad_in(QaArgs a) {
   const int64_t g0 = static_cast<int64_t>(blockIdx.x) * 256;
   const int64_t G = a.G;
   const int r = a.r;
-  for (int idx = tid; idx < tok * r; idx += 256) {
-    const int t = idx / r, j = idx % r;
-    s_du[idx] = m0 + t < a.M ? a.du[(m0 + t) * r + j] : 0.0f;
+  // du of the block (tok * r <= 1024 values): four unconditional loads per
+  // thread, issued together with the first rows of A below
+  float dv[kQaTokMax * kQaMaxRank / 256];
+  const int64_t dlast = a.M * r - 1;
+#pragma unroll
+  for (int i = 0; i < kQaTokMax * kQaMaxRank / 256; ++i) {
+    const int64_t e = m0 * r + i * 256 + tid;
+    dv[i] = a.du[e < dlast ? e : dlast];
   }
   const int64_t g = g0 + tid;
   float acc[kQaTokMax];
@@ -229,6 +240,13 @@ __global__ __launch_bounds__(256) void k_qa_grad_in(QaArgs a) {
       }
     }
     __syncthreads();  // the previous block's rows are consumed
+    if (jb == 0) {
+#pragma unroll
+      for (int i = 0; i < kQaTokMax * kQaMaxRank / 256; ++i) {
+        const int idx = i * 256 + tid;
+        if (idx < tok * r) s_du[idx] = m0 * r + idx <= dlast ? dv[i] : 0.0f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kQaGiRows * 32 / 256; ++i) {
       const int idx = i * 256 + tid;
@@ -276,7 +294,7 @@ hipError_t launch_qa_pool_u(const QaArgs& in, hipStream_t stream) {
   a.stage_a = a.u_out != nullptr && a.G % 8 == 0 && lds + a_bytes <= 65536;
   if (a.stage_a) lds += a_bytes;
   const uint32_t grid = static_cast<uint32_t>((a.M + a.tok - 1) / a.tok);
-  hipLaunchKernelGGL(k_qa_pool_u, dim3(grid), dim3(256), static_cast<uint32_t>(lds), stream, a);
+  hipLaunchKernelGGL(k_qa_pool_u, dim3(grid), dim3(kQaThreads), static_cast<uint32_t>(lds), stream, a);
   return hipGetLastError();
 }
 

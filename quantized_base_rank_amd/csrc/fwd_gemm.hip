@@ -281,52 +281,84 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
     __syncthreads();
   }
 
-  // adapter term: acc += B[n][j] * (s u[m][j]) over j, in k16 steps.
-  // Loads use clamped indices and a select (no divergent branches).
+  // adapter term: acc += B[n][j] * (s u[m][j]) over j, in k16 steps, with
+  // s u split into hi + lo bf16 halves (two MFMAs per step).  s u of the
+  // tile's 256 tokens (as the two halves) and B of its 256 features are
+  // staged in LDS 64 adapter columns at a time (rows padded by 16 B against
+  // bank conflicts), every load of a chunk in flight at once.  Indices are
+  // clamped and values masked (no divergent branches around loads).
   if (sp == 0 && a.u != nullptr && a.r > 0) {
     const int rr = a.r;
-    const int jsteps = (rr + 15) / 16;
-    for (int jt = 0; jt < jsteps; ++jt) {
-      const int j0 = jt * 16 + h * 8;
-      u32x4 bf[2];
+    constexpr int kJC = 64;          // adapter columns per staged chunk
+    constexpr int rp = kJC + 8;      // staged row length (elements)
+    constexpr int q4 = kJC / 4;      // 4-element pieces of a staged row
+    uint16_t* s_uh = reinterpret_cast<uint16_t*>(&s_x[0][0]);  // [256 m][rp]
+    uint16_t* s_ul = s_uh + kTM * rp;                           // [256 m][rp]
+    uint16_t* s_b = s_ul + kTM * rp;                            // [256 n][rp], 110.6 KB in all
+    constexpr int kUPer = kTM * q4 / 256;                       // 16 pieces of each kind per thread
+    for (int jc = 0; jc < rr; jc += kJC) {
+      f32x4 uv[kUPer];
+      u32x2 bv[kUPer];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint16_t* brow = a.B + nr[r] * rr;
-        uint32_t v[4];
+      for (int q = 0; q < kUPer; ++q) {
+        const int it = q * 256 + tid;
+        const int row = it / q4, j = jc + (it - row * q4) * 4;
+        int64_t mg = m0 + row, ng = n0 + row;
+        mg = mg < M ? mg : M - 1;
+        ng = ng < N ? ng : N - 1;
+        const float* urow = a.u + mg * rr;
+        const uint16_t* brow = a.B + ng * rr;
+        if ((rr & 3) == 0) {
+          const int jj = j < rr ? j : rr - 4;
+          uv[q] = *reinterpret_cast<const f32x4*>(urow + jj);
+          bv[q] = *reinterpret_cast<const u32x2*>(brow + jj);
+        } else {
+          uint32_t e4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ja = j0 + 2 * e, jb = ja + 1;
-          const uint32_t lo = brow[ja < rr ? ja : rr - 1];
-          const uint32_t hi = brow[jb < rr ? jb : rr - 1];
-          v[e] = (ja < rr ? lo : 0u) | ((jb < rr ? hi : 0u) << 16);
+          for (int e = 0; e < 4; ++e) {
+            const int jj = j + e < rr ? j + e : rr - 1;
+            uv[q][e] = urow[jj];
+            e4[e] = brow[jj];
+          }
+          bv[q] = u32x2{e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16)};
         }
-        bf[r] = u32x4{v[0], v[1], v[2], v[3]};
       }
+      if (jc > 0) __syncthreads();  // the previous chunk's operands are consumed
 #pragma unroll
-      for (int ms = 0; ms < 8; ++ms) {
-        int64_t m = m0 + ms * 32 + l32;
-        m = m < M ? m : M - 1;
-        const float* urow = a.u + m * rr;
-        float hv[8], lv[8];
+      for (int q = 0; q < kUPer; ++q) {
+        const int it = q * 256 + tid;
+        const int row = it / q4, jl = (it - row * q4) * 4, j = jc + jl;
+        float hv[4], lv[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + e;
-          const float uraw = urow[j < rr ? j : rr - 1];
-          split_bf16(j < rr ? a.s * uraw : 0.0f, hv[e], lv[e]);
+        for (int e = 0; e < 4; ++e) split_bf16(j + e < rr ? a.s * uv[q][e] : 0.0f, hv[e], lv[e]);
+        *reinterpret_cast<u32x2*>(s_uh + row * rp + jl) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+        *reinterpret_cast<u32x2*>(s_ul + row * rp + jl) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+        const uint32_t k0 = (j < rr ? 0x0000FFFFu : 0u) | (j + 1 < rr ? 0xFFFF0000u : 0u);
+        const uint32_t k1 = (j + 2 < rr ? 0x0000FFFFu : 0u) | (j + 3 < rr ? 0xFFFF0000u : 0u);
+        *reinterpret_cast<u32x2*>(s_b + row * rp + jl) = u32x2{bv[q].x & k0, bv[q].y & k1};
+      }
+      __syncthreads();
+      const int jt_n = (rr - jc < kJC ? rr - jc + 15 : kJC) / 16;
+      for (int jt = 0; jt < jt_n; ++jt) {
+        const int j0 = jt * 16 + h * 8;
+        u32x4 bf[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          bf[r] = *reinterpret_cast<const u32x4*>(s_b + (wave * 64 + r * 32 + l32) * rp + j0);
+#pragma unroll
+        for (int ms = 0; ms < 8; ++ms) {
+          const int ml = ms * 32 + l32;
+          const u32x4 uh = *reinterpret_cast<const u32x4*>(s_uh + ml * rp + j0);
+          const u32x4 ul = *reinterpret_cast<const u32x4*>(s_ul + ml * rp + j0);
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            acc[r][ms] = mfma32(bf[r], uh, acc[r][ms]);
+            acc[r][ms] = mfma32(bf[r], ul, acc[r][ms]);
+          }
         }
-        u32x4 uh, ul;
-        uh.x = pack_bf16x2(hv[0], hv[1]); uh.y = pack_bf16x2(hv[2], hv[3]);
-        uh.z = pack_bf16x2(hv[4], hv[5]); uh.w = pack_bf16x2(hv[6], hv[7]);
-        ul.x = pack_bf16x2(lv[0], lv[1]); ul.y = pack_bf16x2(lv[2], lv[3]);
-        ul.z = pack_bf16x2(lv[4], lv[5]); ul.w = pack_bf16x2(lv[6], lv[7]);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          acc[r][ms] = mfma32(bf[r], uh, acc[r][ms]);
-          acc[r][ms] = mfma32(bf[r], ul, acc[r][ms]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __syncthreads();  // the staged operands are read before s_x is reused
   }
 
   if (a.splits > 1) {
