@@ -71,8 +71,11 @@ struct StepCodes<kFmtINT4> {
 
 template <int FMT>
 __global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[2][kWStage];    // [n][k] bf16, pieces at wpos
-  __shared__ __attribute__((aligned(16))) uint8_t s_dy[2][kDyStage];  // [m][n] bf16
+  // [W stage 0 | W stage 1 | dY stage 0 | dY stage 1], 128 KB; after the
+  // loop the same memory holds the adapter operands
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[2 * kWStage + 2 * kDyStage];
+  uint8_t (*const s_w)[kWStage] = reinterpret_cast<uint8_t (*)[kWStage]>(s_lds);            // [n][k] bf16, pieces at wpos
+  uint8_t (*const s_dy)[kDyStage] = reinterpret_cast<uint8_t (*)[kDyStage]>(s_lds + 2 * kWStage);  // [m][n] bf16
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -237,51 +240,81 @@ __global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
     __syncthreads();
   }
 
-  // adapter term du A: D[k][m] += sum_j A^T[k][j] du[m][j]
+  // adapter term du A: D[k][m] += sum_j A^T[k][j] du[m][j], in k16 steps,
+  // du split into hi + lo bf16 halves.  du of the tile's 256 tokens (as the
+  // two halves) and A^T of its 256 columns are staged in LDS 64 adapter
+  // columns at a time (rows padded by 16 B against bank conflicts), every
+  // load of a chunk in flight at once.  Indices are clamped and values
+  // masked (no divergent branches around loads).
   if (a.du != nullptr && a.At != nullptr && a.r > 0) {
     const int rr = a.r;
-    const int jsteps = (rr + 15) / 16;
-    for (int jt = 0; jt < jsteps; ++jt) {
-      const int j0 = jt * 16 + h * 8;
-      u32x4 af[4];
+    constexpr int kJC = 64;          // adapter columns per staged chunk
+    constexpr int rp = kJC + 8;      // staged row length (elements)
+    constexpr int q4 = kJC / 4;      // 4-element pieces of a staged row
+    uint16_t* s_dh = reinterpret_cast<uint16_t*>(s_lds);  // [256 m][rp]
+    uint16_t* s_dl = s_dh + kTMx * rp;                     // [256 m][rp]
+    uint16_t* s_at = s_dl + kTMx * rp;                     // [256 k][rp], 110.6 KB in all
+    constexpr int kUPer = kTMx * q4 / 512;                 // 8 pieces of each kind per thread
+    for (int jc = 0; jc < rr; jc += kJC) {
+      f32x4 dv[kUPer];
+      u32x2 av[kUPer];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t k = k0 + wk * 128 + i * 32 + l32;
-        k = k < K ? k : K - 1;
-        const uint16_t* ar = a.At + k * rr;
-        uint32_t v[4];
+      for (int q = 0; q < kUPer; ++q) {
+        const int it = q * 512 + tid;
+        const int row = it / q4, j = jc + (it - row * q4) * 4;
+        int64_t mg = m0 + row, kg = k0 + row;
+        mg = mg < M ? mg : M - 1;
+        kg = kg < K ? kg : K - 1;
+        const float* drow = a.du + mg * rr;
+        const uint16_t* arow = a.At + kg * rr;
+        if ((rr & 3) == 0) {
+          const int jj = j < rr ? j : rr - 4;
+          dv[q] = *reinterpret_cast<const f32x4*>(drow + jj);
+          av[q] = *reinterpret_cast<const u32x2*>(arow + jj);
+        } else {
+          uint32_t e4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ja = j0 + 2 * e, jb = ja + 1;
-          const uint32_t lo = ar[ja < rr ? ja : rr - 1];
-          const uint32_t hi = ar[jb < rr ? jb : rr - 1];
-          v[e] = (ja < rr ? lo : 0u) | ((jb < rr ? hi : 0u) << 16);
+          for (int e = 0; e < 4; ++e) {
+            const int jj = j + e < rr ? j + e : rr - 1;
+            dv[q][e] = drow[jj];
+            e4[e] = arow[jj];
+          }
+          av[q] = u32x2{e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16)};
         }
-        af[i] = u32x4{v[0], v[1], v[2], v[3]};
       }
+      __syncthreads();  // the loop's (or the previous chunk's) operands are consumed
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        int64_t m = m0 + wm * 64 + j * 32 + l32;
-        m = m < M ? m : M - 1;
-        const float* dr = a.du + m * rr;
-        float hv[8], lv[8];
+      for (int q = 0; q < kUPer; ++q) {
+        const int it = q * 512 + tid;
+        const int row = it / q4, jl = (it - row * q4) * 4, j = jc + jl;
+        float hv[4], lv[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = j0 + e;
-          const float dv = dr[jj < rr ? jj : rr - 1];
-          split_bf16(jj < rr ? dv : 0.0f, hv[e], lv[e]);
+        for (int e = 0; e < 4; ++e) split_bf16(j + e < rr ? dv[q][e] : 0.0f, hv[e], lv[e]);
+        *reinterpret_cast<u32x2*>(s_dh + row * rp + jl) = u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+        *reinterpret_cast<u32x2*>(s_dl + row * rp + jl) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
+        const uint32_t k0m = (j < rr ? 0x0000FFFFu : 0u) | (j + 1 < rr ? 0xFFFF0000u : 0u);
+        const uint32_t k1m = (j + 2 < rr ? 0x0000FFFFu : 0u) | (j + 3 < rr ? 0xFFFF0000u : 0u);
+        *reinterpret_cast<u32x2*>(s_at + row * rp + jl) = u32x2{av[q].x & k0m, av[q].y & k1m};
+      }
+      __syncthreads();
+      const int jt_n = (rr - jc < kJC ? rr - jc + 15 : kJC) / 16;
+      for (int jt = 0; jt < jt_n; ++jt) {
+        const int j0 = jt * 16 + h * 8;
+        u32x4 af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const u32x4*>(s_at + (wk * 128 + i * 32 + l32) * rp + j0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int ml = wm * 64 + j * 32 + l32;
+          const u32x4 uh = *reinterpret_cast<const u32x4*>(s_dh + ml * rp + j0);
+          const u32x4 ul = *reinterpret_cast<const u32x4*>(s_dl + ml * rp + j0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i][j] = mfma32(af[i], uh, acc[i][j]);
+            acc[i][j] = mfma32(af[i], ul, acc[i][j]);
+          }
         }
-        u32x4 uh, ul;
-        uh.x = pack_bf16x2(hv[0], hv[1]); uh.y = pack_bf16x2(hv[2], hv[3]);
-        uh.z = pack_bf16x2(hv[4], hv[5]); uh.w = pack_bf16x2(hv[6], hv[7]);
-        ul.x = pack_bf16x2(lv[0], lv[1]); ul.y = pack_bf16x2(lv[2], lv[3]);
-        ul.z = pack_bf16x2(lv[4], lv[5]); ul.w = pack_bf16x2(lv[6], lv[7]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i][j] = mfma32(af[i], uh, acc[i][j]);
-          acc[i][j] = mfma32(af[i], ul, acc[i][j]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
