@@ -111,8 +111,10 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.small = M <= kSmallM;
   // u and du reductions: ~512 workgroups, but never fewer than 64 k16
   // steps per workgroup
-  p.nt_splits_u = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), K / 16 / 64), 1, 64));
-  p.nt_splits_du = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), N / 16 / 64), 1, 64));
+  // skinny products: ~512 workgroups of 64 rows, at least 4 chunks of 128
+  // columns per split
+  p.nt_splits_u = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), ceil_div(K, 128) / 4), 1, 64));
+  p.nt_splits_du = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), ceil_div(N, 128) / 4), 1, 64));
   // token-share splits of the adapter-gradient reductions: ~320 workgroups,
   // at least 256 tokens per share
   const int64_t max_shares = std::max<int64_t>(1, M / 256);
