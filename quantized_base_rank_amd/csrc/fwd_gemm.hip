@@ -362,27 +362,42 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   }
 
   if (a.splits > 1) {
-    float* part = a.partial + (static_cast<int64_t>(tmn) * a.splits + sp) * (kTM * kTN);
+    // publish this split's partial tile as 16-byte pieces (four consecutive
+    // accumulator values of a lane); the tile's last workgroup adds the
+    // splits in fixed order
+    const rsrc_t pr = make_rsrc(a.partial);
+    auto poff = [&](int s2, int r, int ms, int v4) {
+      return static_cast<uint32_t>((((static_cast<int64_t>(tmn) * a.splits + s2) * (kTM * kTN)) +
+                                    ((r * 8 + ms) * 4 + v4) * 1024 + tid * 4) * 4);
+    };
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) st_sys(part + ((r * 8 + ms) * 16 + v) * 256 + tid, acc[r][ms][v]);
+        for (int v4 = 0; v4 < 4; ++v4)
+          st_sys16(pr, poff(sp, r, ms, v4),
+                   f32x4{acc[r][ms][4 * v4], acc[r][ms][4 * v4 + 1], acc[r][ms][4 * v4 + 2], acc[r][ms][4 * v4 + 3]});
     if (publish_and_ticket(a.counters + tmn, s_ticket) != static_cast<uint32_t>(a.splits - 1))
       return;
-    const float* base = a.partial + static_cast<int64_t>(tmn) * a.splits * (kTM * kTN);
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int ms = 0; ms < 8; ++ms)
+      for (int ms = 0; ms < 8; ++ms) {
+        f32x4 sum[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                        f32x4{0.f, 0.f, 0.f, 0.f}};
+        for (int s2 = 0; s2 < a.splits; ++s2) {
+          f32x4 v[4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float sum = 0.0f;
-          for (int s2 = 0; s2 < a.splits; ++s2)
-            sum += ld_sys(base + s2 * (kTM * kTN) + ((r * 8 + ms) * 16 + v) * 256 + tid);
-          acc[r][ms][v] = sum;
+          for (int v4 = 0; v4 < 4; ++v4) v[v4] = ld_sys16(pr, poff(s2, r, ms, v4));
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) sum[v4] += v[v4];
         }
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[r][ms][4 * v4 + e] = sum[v4][e];
+      }
     if (tid == 0) a.counters[tmn] = 0u;
   }
 
