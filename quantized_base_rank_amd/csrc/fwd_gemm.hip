@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXTile + kCTile];
   uint32_t* s_ticket = reinterpret_cast<uint32_t*>(&s_x[0][0]);  // used after the K loop
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const int64_t M = a.M, N = a.w.N, K = a.w.K;
   const int tiles_m = static_cast<int>((M + kTM - 1) / kTM);
@@ -209,8 +210,11 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   };
   auto step_valid = [&](int64_t ks) { return ks * kKS + h * 64 < K; };
 
-  // Tiles and codes run one K step ahead, block constants two: step ks+1's
-  // tables are built while step ks's last MFMAs run.
+  // Tiles and codes run one K step ahead, block constants two.  The stage
+  // barrier sits after sub-step 6: by then every wave has read its last
+  // token fragments of the step, and the next step's data has landed, so
+  // sub-step 7 overlaps its MFMAs with the next step's tables, code reads
+  // and first decode (no bubble at the top of a step).
   StepParams<FMT> pc, pn, p2;
   load_x(ks0, 0);
   load_codes(ks0, 0);
@@ -224,32 +228,33 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   // while the 16 MFMAs of sub-step tt run, the weight words of tt + 1 are
   // decoded and its token fragments read from LDS.
   u32x4 cw[2][2], wf[2][2], xf[2][8];
+  read_codes(0, cw);
+  read_x(s_x[0], 0, xf[0]);
+  decode_w(cw, 0, wf[0]);
+  // The loop body has no branches (a branch splits the scheduling region and
+  // the MFMA / decode interleave is lost), so it is instantiated once per
+  // wave with that wave's load slot fixed, and the loads of a missing next
+  // step are clamped to re-read the current one into the idle stage.
+  auto k_loop = [&](auto wave_c) __attribute__((always_inline)) {
+  constexpr int W = decltype(wave_c)::value;
   for (int64_t ks = ks0; ks < ks1; ++ks) {
     const int buf = static_cast<int>((ks - ks0) & 1);
-    const bool more = ks + 1 < ks1;
+    const int64_t kn = ks + 1 < ks1 ? ks + 1 : ks;
+    const int64_t kp = ks + 2 < ks1 ? ks + 2 : ks1 - 1;
     const uint8_t* xb = s_x[buf];
-    read_codes(buf, cw);
-    read_x(xb, 0, xf[0]);
-    decode_w(cw, 0, wf[0]);
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int cur = tt & 1, nxt = cur ^ 1;
-      // Next step's loads, one wave at a time: a wave blocks while the load
-      // path takes its 1 KB load instructions, so the waves take turns
-      // (wave w at sub-step 2w) and the other three keep issuing MFMAs.
-      // The target stage was last read before the previous barrier.
-      if (tt == 2 * wave) {
-        if (more) {
-          load_x(ks + 1, buf ^ 1);
-          load_codes(ks + 1, buf ^ 1);
-        }
-        if (ks + 2 < ks1) load_step_params(ks + 2, p2);
-      }
       if (tt < 7) {
         decode_w(cw, tt + 1, wf[nxt]);
         read_x(xb, tt + 1, xf[nxt]);
-      } else if (more) {
+      } else {
+        // the next step's tables, codes, first token fragments and first
+        // decode (on the last step: harmless reads of the idle stage)
         build_luts(pn, step_valid(ks + 1));
+        read_codes(buf ^ 1, cw);
+        read_x(s_x[buf ^ 1], 0, xf[nxt]);
+        decode_w(cw, 0, wf[nxt]);
       }
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms) {
@@ -257,28 +262,50 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
         acc[1][ms] = mfma32(wf[cur][1], xf[cur][ms], acc[1][ms]);
       }
       if (tt < 7) {
-        // issue order: 2 MFMA, 1 LDS read of the next sub-step, ~7 VALU of
-        // the next decode; x8 (measured best: an LDS read issued ahead of
-        // the MFMA pair delays it, one issued last lands too late)
+        // issue order: 2 MFMA, 1 LDS read of the next sub-step, ~6 VALU of
+        // the next decode; x8
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
         }
       } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 7; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 15, 0);
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Next step's loads, one wave at a time: a wave blocks while the load
+      // path takes its 1 KB load instructions, so the waves take turns
+      // (wave w after sub-step w) and the other three keep issuing MFMAs.
+      // The target stage was last read before the previous step's barrier.
+      if (tt == W) {
+        load_x(kn, buf ^ 1);
+        load_codes(kn, buf ^ 1);
+        load_step_params(kp, p2);
+      }
+      if (tt == 6) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     pc = pn;
     pn = p2;
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  }
+  };
+  switch (wave) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    default: k_loop(std::integral_constant<int, 3>{}); break;
   }
 
   // adapter term: acc += B[n][j] * (s u[m][j]) over j, in k16 steps, with
