@@ -4,21 +4,21 @@
 //  dequantized weight; W itself receives no gradient.]
 //
 // The reduction runs over the output features n, i.e. across rows of the
-// packed weight.  Each 64 x 256 weight slab of a step is decoded in its
-// natural row orientation (wave w: columns [32 w, 32 w + 32) of the tile,
-// lane l: row l, one table per lane) and written to LDS row-major; the
-// transposing LDS read turns 8 consecutive rows of one column into an MFMA
-// operand.
-//
-// Tile: 256 columns of dX x 256 tokens per workgroup, 8 waves (two per SIMD)
-// each owning 128 columns x 64 tokens.  The two waves that share a SIMD work
-// in opposite order within a step (products then the next step's decode, or
-// the reverse), so that one wave's lookups overlap the other's products.
-// The next step's dY tile (buffer loads into registers) and the codes two
-// steps ahead load during the step; the dY tile goes to LDS at its end.  Both
-// LDS stages are double buffered, one barrier per step.  The adapter term
-// du A is 2*ceil(r/16) extra MFMA k-steps (du split hi + lo), read from A^T
-// [K][r].
+// packed weight.  Tile: 256 columns of dX x 256 tokens per workgroup of 4
+// waves, one per SIMD; wave w owns columns [64 w, 64 w + 64) (one NF4 block,
+// two INT4 groups) for all 256 tokens.  In each 64-row step every lane
+// decodes one weight row of its wave's columns (one table per lane) and
+// writes it row-major into the wave's own LDS slab; the transposing LDS read
+// then turns 8 consecutive rows of one column into an MFMA operand.  A wave
+// only ever reads the weights it decoded itself, so only the shared dY tile
+// needs the workgroup barrier.  The next step's weights are decoded while
+// the current step's MFMAs run (a two-stage register pipeline over the four
+// 16-row sub-steps, two words of the decode in each).  The dY tile of a step
+// arrives by direct-to-LDS loads two steps ahead, the codes three.  Each LDS
+// stage is an array of its own, so that the compiler can tell that reads of
+// one stage do not depend on loads still landing in another.
+// The adapter term du A is 2*ceil(r/16) extra MFMA k-steps (du split hi +
+// lo), read from A^T [K][r].
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -29,23 +29,25 @@ namespace {
 constexpr int kTK = 256;                  // dX columns per tile
 constexpr int kTMx = 256;                 // tokens per tile
 constexpr int kNS = 64;                   // reduction rows per step
-constexpr int kWRow = kTK * 2;            // one W row of the tile in LDS: 512 B
-constexpr int kWStage = kNS * kWRow;      // 32 KB
+constexpr int kWReg = kNS * 64 * 2;       // one wave's decoded slab: 64 rows x 64 columns, 8 KB
+constexpr int kWStage = 4 * kWReg;        // 32 KB
 constexpr int kDyStage = kTMx * kNS * 2;  // 32 KB
 
-// dY tile [m][64 bf16]: rows of 128 B, 16-byte chunks XOR-swizzled by row
-__device__ __forceinline__ uint32_t off64(int row, int chunk) {
-  return static_cast<uint32_t>(row * 128 + ((chunk ^ (row & 7)) << 4));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Decoded slab row n: 128 B, 16-byte piece c (columns 8c .. 8c+7) at
+// position c ^ wsw(n).  The 16 rows written by one 16-lane group land in 16
+// distinct bank groups (row parity x 8 positions), and the 4 rows x 4 pieces
+// read by 32 lanes of a transposing read do too (rows 2g and 2g+2 differ in
+// bit 2 of the position).
+__device__ __forceinline__ int wsw(int n) {
+  const int g = (n >> 1) & 7;
+  return ((g & 1) << 2) | (g >> 1);
 }
 
-// Position of the 16-byte piece c (columns 8c .. 8c+7) of W row r.  The
-// row term spreads the 16 consecutive rows that one write instruction covers
-// over 16 positions; the column term puts the two column halves read by one
-// transposing read (pieces 4j, 4j+1 and 4j+2, 4j+3) in different 128-byte
-// halves.
-__device__ __forceinline__ int wpos(int c, int r) {
-  return c ^ (((c >> 1) & 1) << 3) ^ (((r & 7) << 1) | ((r >> 3) & 1));
-}
+// dY tile [m][64 bf16]: rows of 128 B, 16-byte chunk c at c ^ ((m / 2) % 8),
+// so that 16 consecutive rows read one chunk from 16 distinct bank groups.
+__device__ __forceinline__ int dsw(int m) { return (m >> 1) & 7; }
 
 __device__ __forceinline__ int remap_xcd(int bid, int n) {
   const int q = n >> 3, rem = n & 7;
@@ -53,214 +55,281 @@ __device__ __forceinline__ int remap_xcd(int bid, int n) {
   return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
-// Codes and raw decode constants of one lane's 32-column piece of a step.
+// Codes and raw decode constants of one lane's row segment (64 columns).
 template <int FMT>
-struct StepCodes;
+struct RowCodes;
 template <>
-struct StepCodes<kFmtNF4> {
-  u32x4 cw;
+struct RowCodes<kFmtNF4> {
+  u32x4 c[2];
   BlockParams bp;
-  bool valid;
 };
 template <>
-struct StepCodes<kFmtINT4> {
-  u32x4 cw;
-  uint32_t sz;  // scale | zero << 16 of the piece's group
-  bool valid;
+struct RowCodes<kFmtINT4> {
+  u32x4 c[2];
+  uint32_t sz[2];  // per group: scale | zero << 16
 };
 
 template <int FMT>
-__global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
-  // [W stage 0 | W stage 1 | dY stage 0 | dY stage 1], 128 KB; after the
-  // loop the same memory holds the adapter operands
-  __shared__ __attribute__((aligned(16))) uint8_t s_lds[2 * kWStage + 2 * kDyStage];
-  uint8_t (*const s_w)[kWStage] = reinterpret_cast<uint8_t (*)[kWStage]>(s_lds);            // [n][k] bf16, pieces at wpos
-  uint8_t (*const s_dy)[kDyStage] = reinterpret_cast<uint8_t (*)[kDyStage]>(s_lds + 2 * kWStage);  // [m][n] bf16
+__global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
+  // decoded-weight and dY stages, 128 KB; after the loop the same memory
+  // holds the adapter operands
+  __shared__ __attribute__((aligned(16))) uint8_t s_w0[kWStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_w1[kWStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dy0[kDyStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dy1[kDyStage];
+  uint8_t* const s_w[2] = {s_w0, s_w1};
+  uint8_t* const s_dy[2] = {s_dy0, s_dy1};
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
   const int l32 = lane & 31, h = lane >> 5, l16 = lane & 15;
-  const int wk = wave & 1, wm = (wave >> 1) & 3;  // products: columns wk*128.., tokens wm*64..
-  const bool mfma_first = wave < 4;              // waves w and w + 4 share a SIMD
   const int64_t M = a.M, N = a.w.N, K = a.w.K;
   const int tiles_m = static_cast<int>((M + kTMx - 1) / kTMx);
   const int tiles_k = static_cast<int>((K + kTK - 1) / kTK);
   const int t = remap_xcd(static_cast<int>(blockIdx.x), tiles_m * tiles_k);
-  // (uniform; said so, so that the buffer resource below stays scalar)
   const int tm = __builtin_amdgcn_readfirstlane(t / tiles_k);
   const int tk = __builtin_amdgcn_readfirstlane(t % tiles_k);
   const int64_t m0 = static_cast<int64_t>(tm) * kTMx, k0 = static_cast<int64_t>(tk) * kTK;
+  // whole pairs of steps (a step past the last one meets weight rows past N,
+  // which decode to zero)
   const int64_t nsteps = (N + kNS - 1) / kNS;
+  const int64_t npairs = (nsteps + 1) >> 1;
 
-  // decode assignment: row `lane` of each step, columns [32 wave, +32)
-  const int64_t kcol = k0 + wave * 32;
-  const bool kvalid = kcol < K;
-  const int64_t kcc = kvalid ? kcol : k0;
+  // this wave's 64 columns (clamped into the matrix; masked when past K)
+  const int64_t kw = k0 + wave * 64;
+  const bool kvalid = kw < K;
+  const int64_t kwc = kvalid ? kw : k0;
 
-  f32x16 acc[4][2];
+  f32x16 acc[2][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x16{};
 
-  // dY tile of a step (256 tokens x 64 rows of dY^T) through registers from a
-  // buffer resource over the tile's tokens: instruction i of lane L, wave w
-  // holds 16 bytes of token row 64 i + 8 w + L / 8, chunk (L % 8) XOR the row,
-  // and writes them where a whole-line direct-to-LDS load would put them.
-  // Rows past M read as zero (their outputs are never stored); a chunk past
-  // N reads the row's last 8 columns (those weight rows decode to zero).
+  // dY tile of a step by direct-to-LDS loads: instruction i of wave w
+  // covers rows 32 i + 8 w .. +7 (1 KB), the swizzle applied to the source
+  // chunk.  Rows past M fall outside the resource (their outputs are never
+  // stored); columns past N read the next row's values, which meet weight
+  // rows past N that decode to zero.
   const int64_t dy_rows = M - m0 < kTMx ? M - m0 : kTMx;
   const rsrc_t dyr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.dy + m0 * N), 0, static_cast<int>(dy_rows * N * 2), 0x00020000);
-  const int dy_lrow = wave * 8 + (lane >> 3);
-  const int dy_c = (lane & 7) ^ (dy_lrow & 7);
-  u32x4 dyv[4];
-  auto load_dy = [&](int64_t st) {
-    int64_t n = st * kNS + dy_c * 8;
-    n = n < N ? n : N - 8;  // also clamps a step past the last
-    const uint32_t voff = static_cast<uint32_t>((dy_lrow * N + n) * 2);
+  const int dlrow = wave * 8 + (lane >> 3);
+  const uint32_t dyvoff = static_cast<uint32_t>(dlrow * N * 2 + (((lane & 7) ^ dsw(dlrow)) << 4));
+  auto load_dy = [&](int64_t st, int stage) {
+    const int64_t stc = st < nsteps ? st : nsteps - 1;
+    const uint32_t nb = static_cast<uint32_t>(stc * kNS * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dyv[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(dyr, voff, static_cast<int>(i * 64 * N * 2), 0));
-  };
-  auto store_dy = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&s_dy[buf][(i * 8 + wave) * 1024 + lane * 16]) = dyv[i];
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          dyr, (lds_ptr_t)(s_dy[stage] + (i * 4 + wave) * 1024), 16, dyvoff,
+          static_cast<int>(static_cast<uint32_t>(i * 32 * N * 2) + nb), 0, 0);
   };
 
-  auto load_codes = [&](int64_t st, StepCodes<FMT>& sc) {
+  // codes of row st*64 + lane, columns [kwc, kwc + 64): two 16-byte loads
+  auto load_codes = [&](int64_t st, RowCodes<FMT>& rc) {
     const int64_t n = st * kNS + lane;
-    sc.valid = kvalid && n < N;
-    // unconditional loads from clamped addresses; invalid rows decode to zero
     const int64_t nc = n < N ? n : N - 1;
-    sc.cw = *reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (kcc >> 1));
+    const uint8_t* row = a.w.codes + nc * (K >> 1) + (kwc >> 1);
+    rc.c[0] = *reinterpret_cast<const u32x4*>(row);
+    rc.c[1] = *reinterpret_cast<const u32x4*>(row + 16);
     if constexpr (FMT == kFmtNF4) {
-      sc.bp = load_block_params<kFmtNF4>(a.w, nc, kcc >> 6, true);
+      rc.bp = load_block_params<kFmtNF4>(a.w, nc, kwc >> 6, true);
     } else {
-      const int64_t gi = nc * (K >> 5) + (kcc >> 5);
-      sc.sz = static_cast<uint32_t>(a.w.scale[gi]) | (static_cast<uint32_t>(a.w.zero[gi]) << 16);
+      const int64_t g = nc * (K >> 5) + (kwc >> 5);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        rc.sz[q] = static_cast<uint32_t>(a.w.scale[g + q]) | (static_cast<uint32_t>(a.w.zero[g + q]) << 16);
     }
   };
-  // one table per lane (an invalid row gets all-zero constants), 4 lookups
-  // of 8, 16-byte writes to the lane's row
-  auto decode = [&](const StepCodes<FMT>& sc, uint8_t* wt) {
-    Lut16 lut;
+  // Tables of a step's row, two sets (by step parity), each built in two
+  // parts so that the work spreads over two sub-steps: NF4 entries 0..7 then
+  // 8..15 of the block's table, INT4 the tables of the two groups.  An
+  // invalid row or column range gets zeros.
+  constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
+  Lut16 lut[2][NL];
+  float lscale[2];
+  auto build_lut_part = [&](int set, const RowCodes<FMT>& rc, int64_t st, int part) {
+    const bool valid = kvalid && st * kNS + lane < N;
     if constexpr (FMT == kFmtNF4) {
-      BlockParams bp = sc.bp;
-      bp.a = sc.valid ? bp.a : 0u;
-      bp.b = sc.valid ? bp.b : 0u;
-      lut = lut_nf4(a.w.cb, nf4_params_scale(a.w, bp));
+      if (part == 0) lscale[set] = valid ? nf4_params_scale(a.w, rc.bp) : 0.0f;
+      const float sc = lscale[set];
+      uint32_t pr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pr[j] = pack_bf16x2(a.w.cb.c[8 * part + 2 * j] * sc, a.w.cb.c[8 * part + 2 * j + 1] * sc);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        lut[set][0].lo[2 * part + q] = perm(pr[2 * q + 1], pr[2 * q], 0x06040200u);
+        lut[set][0].hi[2 * part + q] = perm(pr[2 * q + 1], pr[2 * q], 0x07050301u);
+      }
     } else {
-      const uint32_t sz = sc.valid ? sc.sz : 0u;
-      lut = lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
-                     half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
+      const uint32_t sz = valid ? rc.sz[part] : 0u;
+      lut[set][part] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
+                                half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
     }
-    u32x4 d[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = lut_decode8(lut, sc.cw[q]);
-    uint8_t* row = wt + lane * kWRow;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(row + (wpos(4 * wave + q, lane) << 4)) = d[q];
+  };
+  // decoded word q (columns 8q .. 8q+7) of this lane's row into a slab stage
+  const int wrow = wave * kWReg + lane * 128;
+  const int wswl = wsw(lane);
+  auto decode_word = [&](int set, const RowCodes<FMT>& rc, int q, int stage) {
+    const u32x4 d = lut_decode8(lut[set][NL == 1 ? 0 : (q >> 2)], rc.c[q >> 2][q & 3]);
+    *reinterpret_cast<u32x4*>(s_w[stage] + wrow + ((q ^ wswl) << 4)) = d;
   };
 
-  // MFMA operand: rows nb .. nb+7 of column col0 + (lane % 16) of a W tile,
-  // two transposing reads of 4 rows.  Within a step, rows nb = 16 nn + 8 h +
-  // (lane % 16) / 4 (+ 4) keep their row bits 0..3 for every nn, so the
-  // positions depend on nn only through an immediate offset of nn * 16 rows:
-  // the byte offsets for nn = 0 are formed once.
-  uint32_t wofs[2][4];
+  // MFMA operands of sub-step nn (rows 16 nn .. 16 nn + 15 of the step).
+  // A = W^T: for column tile i, lane p of each 16-lane group points at row
+  // 8 h + p / 4 (+ 4), columns 32 i + (l32 & 16) + 4 (p % 4) .. +3 of the
+  // slab; the transposing read hands lane t column 32 i + (l32 & 16) + t.
+  // B = dY^T: token 32 j + l32, reduction chunk 2 nn + h.  Row terms of nn
+  // and j are immediate offsets.
+  uint32_t aofs[2][2];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = wk * 128 + i * 32 + (l32 & 16) + 4 * (l16 & 3);
-      const int c = col >> 3, half8 = ((col >> 2) & 1) * 8;
+    for (int x = 0; x < 2; ++x) {
       const int r = 8 * h + (l16 >> 2) + 4 * x;
-      wofs[x][i] = static_cast<uint32_t>(r * kWRow + (wpos(c, r) << 4) + half8);
+      const int col = 32 * i + (l32 & 16) + 4 * (l16 & 3);
+      aofs[i][x] = static_cast<uint32_t>(wave * kWReg + r * 128 + (((col >> 3) ^ wsw(r)) << 4) + ((col >> 2) & 1) * 8);
     }
-  // D[k][m] += sum_n W^T[k][n] dY^T[n][m] over a step: lane (l32, h) of the
-  // A operand holds 8 rows of column k, of the B operand 8 rows of token m
-  const int dyx = h ^ (l32 & 7);  // chunk 2 nn + h of row ... + l32 sits at (2 nn) ^ dyx
-  // The operands of sub-step nn + 1 are read before the products of nn, so
-  // that their LDS latency overlaps those products.
-  auto read_ops = [&](const uint8_t* wt, const uint8_t* db, int nn, u32x4 (&af)[4], u32x4 (&bf)[2]) {
+  uint32_t bofs[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x2 lo = ds_read_tr16(wt + nn * 16 * kWRow + wofs[0][i]);
-      const u32x2 hi = ds_read_tr16(wt + nn * 16 * kWRow + wofs[1][i]);
-      af[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      bf[j] = *reinterpret_cast<const u32x4*>(db + (wm * 64 + j * 32 + l32) * 128 + (((2 * nn) ^ dyx) << 4));
+  for (int nn = 0; nn < 4; ++nn)
+    bofs[nn] = static_cast<uint32_t>(l32 * 128 + (((2 * nn + h) ^ dsw(l32)) << 4));
+  auto read_a = [&](int stage, int nn, int i) {
+    const uint8_t* wa = s_w[stage] + nn * 16 * 128;
+    const u32x2 lo = ds_read_tr16(wa + aofs[i][0]);
+    const u32x2 hi = ds_read_tr16(wa + aofs[i][1]);
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
   };
-  auto products = [&](int buf) {
-    const uint8_t* wt = s_w[buf];
-    const uint8_t* db = s_dy[buf];
-    u32x4 af[2][4], bf[2][2];
-    read_ops(wt, db, 0, af[0], bf[0]);
+  auto read_b = [&](int stage, int nn, u32x4 (&bf)[8]) {
 #pragma unroll
-    for (int nn = 0; nn < 4; ++nn) {
-      const int cur = nn & 1;
-      if (nn + 1 < 4) read_ops(wt, db, nn + 1, af[cur ^ 1], bf[cur ^ 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int j = 0; j < 8; ++j)
+      bf[j] = *reinterpret_cast<const u32x4*>(s_dy[stage] + j * 32 * 128 + bofs[nn]);
   };
 
-  StepCodes<FMT> sc_next, sc_after;
-  load_dy(0);
-  load_codes(0, sc_next);
-  store_dy(0);
-  decode(sc_next, s_w[0]);
-  if (nsteps > 1) load_codes(1, sc_next);
+  // Prologue: dY of steps 0 and 1 in LDS, codes of steps 1 and 2 in
+  // registers, step 0 decoded and the tables of step 1 built before the
+  // loop.
+  RowCodes<FMT> rc[2];
+  load_dy(0, 0);
+  load_dy(1, 1);
+  load_codes(0, rc[0]);
+  load_codes(1, rc[1]);
+  build_lut_part(0, rc[0], 0, 0);
+  build_lut_part(0, rc[0], 0, 1);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) decode_word(0, rc[0], q, 0);
+  build_lut_part(1, rc[1], 1, 0);
+  build_lut_part(1, rc[1], 1, 1);
+  load_codes(2, rc[0]);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int64_t st = 0; st < nsteps; ++st) {
-    const int buf = static_cast<int>(st & 1);
-    const bool more = st + 1 < nsteps;
-    // unconditional (clamped) loads: with a fixed number of loads per step
-    // the compiler waits for exactly the older ones it needs
-    load_dy(st + 1);
-    load_codes(st + 2, sc_after);
-    // one copy of the products; the decode sits before them in waves 4..7
-    // and after them in waves 0..3 (a scalar branch either way)
-    if (more && !mfma_first) decode(sc_next, s_w[buf ^ 1]);
-    products(buf);
-    if (more && mfma_first) decode(sc_next, s_w[buf ^ 1]);
-    if (more) store_dy(buf ^ 1);
-    sc_next = sc_after;
-    __syncthreads();
+  u32x4 af[2][2], bf[2][8];
+  af[0][0] = read_a(0, 0, 0);
+  read_b(0, 0, bf[0]);
+  // One step st (ri = st & 1: dY and weight stage, table set of step st + 2,
+  // code set of step st + 2; the other sets hold step st + 1): the products
+  // of st while step st + 1 is decoded into the other weight stage, two
+  // words per sub-step, and the tables of step st + 2 are built in
+  // sub-steps 2 and 3.  After sub-step 2 the stage barrier (the dY of st + 1
+  // has landed; every wave has read its last dY fragments of st).  Sub-step
+  // 3 reads the first column tile and the dY fragments of st + 1; its
+  // second column tile is read at the top of st + 1, under the first
+  // tile's products.
+  // Loads: waves 0, 1 take the dY of st + 2 right after the barrier, waves
+  // 2, 3 after sub-step 3 (so that two waves keep the matrix cores busy
+  // while the other two issue), and all take the codes of st + 3 after
+  // sub-step 3 (their code set is decoded by then).
+  auto k_loop = [&](auto early_c) __attribute__((always_inline)) {
+  constexpr bool early = decltype(early_c)::value;
+  auto step = [&](int64_t st, auto ri_c) __attribute__((always_inline)) {
+    constexpr int ri = decltype(ri_c)::value;
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn) {
+      const int cur = nn & 1, nxt = cur ^ 1;
+      if (nn == 0) af[cur][1] = read_a(ri, 0, 1);
+      if (nn < 3) {
+        af[nxt][0] = read_a(ri, nn + 1, 0);
+        af[nxt][1] = read_a(ri, nn + 1, 1);
+        read_b(ri, nn + 1, bf[nxt]);
+      } else {
+        af[nxt][0] = read_a(ri ^ 1, 0, 0);
+        read_b(ri ^ 1, 0, bf[nxt]);
+      }
+      decode_word(ri ^ 1, rc[ri ^ 1], 2 * nn, ri ^ 1);
+      decode_word(ri ^ 1, rc[ri ^ 1], 2 * nn + 1, ri ^ 1);
+      if (nn == 2) build_lut_part(ri, rc[ri], st + 2, 0);
+      if (nn == 3) build_lut_part(ri, rc[ri], st + 2, 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
+      // issue order: 1 MFMA, a share of the decode, the operand reads of
+      // the next sub-step and the decode's LDS writes spread between
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (nn < 2)
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        if (g % 4 == 3)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (g == 5 || g == 11) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (nn == 2) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (early) load_dy(st + 2, ri);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (nn == 3) {
+        if (!early) load_dy(st + 2, ri);
+        load_codes(st + 3, rc[ri ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  for (int64_t sp = 0; sp < npairs; ++sp) {
+    step(2 * sp, std::integral_constant<int, 0>{});
+    step(2 * sp + 1, std::integral_constant<int, 1>{});
   }
+  };
+  if (wave < 2)
+    k_loop(std::true_type{});
+  else
+    k_loop(std::false_type{});
+  // every load has landed and every wave is past its reads before the
+  // memory is reused
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // adapter term du A: D[k][m] += sum_j A^T[k][j] du[m][j], in k16 steps,
   // du split into hi + lo bf16 halves.  du of the tile's 256 tokens (as the
-  // two halves) and A^T of its 256 columns are staged in LDS 64 adapter
+  // two halves) and A^T of its 256 columns are staged in LDS 48 adapter
   // columns at a time (rows padded by 16 B against bank conflicts), every
   // load of a chunk in flight at once.  Indices are clamped and values
   // masked (no divergent branches around loads).
   if (a.du != nullptr && a.At != nullptr && a.r > 0) {
     const int rr = a.r;
-    constexpr int kJC = 64;          // adapter columns per staged chunk
-    constexpr int rp = kJC + 8;      // staged row length (elements)
+    constexpr int kJC = 48;          // adapter columns per staged chunk
+    constexpr int rp = kJC + 8;      // staged row length (elements): 28 KB per operand
     constexpr int q4 = kJC / 4;      // 4-element pieces of a staged row
-    uint16_t* s_dh = reinterpret_cast<uint16_t*>(s_lds);  // [256 m][rp]
-    uint16_t* s_dl = s_dh + kTMx * rp;                     // [256 m][rp]
-    uint16_t* s_at = s_dl + kTMx * rp;                     // [256 k][rp], 110.6 KB in all
-    constexpr int kUPer = kTMx * q4 / 512;                 // 8 pieces of each kind per thread
+    uint16_t* s_dh = reinterpret_cast<uint16_t*>(s_w0);   // [256 m][rp]
+    uint16_t* s_dl = reinterpret_cast<uint16_t*>(s_w1);   // [256 m][rp]
+    uint16_t* s_at = reinterpret_cast<uint16_t*>(s_dy0);  // [256 k][rp]
+    constexpr int kUPer = kTMx * q4 / 256;                 // 12 pieces of each kind per thread
     for (int jc = 0; jc < rr; jc += kJC) {
       f32x4 dv[kUPer];
       u32x2 av[kUPer];
 #pragma unroll
       for (int q = 0; q < kUPer; ++q) {
-        const int it = q * 512 + tid;
+        const int it = q * 256 + tid;
         const int row = it / q4, j = jc + (it - row * q4) * 4;
         int64_t mg = m0 + row, kg = k0 + row;
         mg = mg < M ? mg : M - 1;
@@ -282,10 +351,10 @@ __global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
           av[q] = u32x2{e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16)};
         }
       }
-      __syncthreads();  // the loop's (or the previous chunk's) operands are consumed
+      if (jc > 0) __syncthreads();  // the previous chunk's operands are consumed
 #pragma unroll
       for (int q = 0; q < kUPer; ++q) {
-        const int it = q * 512 + tid;
+        const int it = q * 256 + tid;
         const int row = it / q4, jl = (it - row * q4) * 4, j = jc + jl;
         float hv[4], lv[4];
 #pragma unroll
@@ -300,19 +369,19 @@ __global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
       const int jt_n = (rr - jc < kJC ? rr - jc + 15 : kJC) / 16;
       for (int jt = 0; jt < jt_n; ++jt) {
         const int j0 = jt * 16 + h * 8;
-        u32x4 af[4];
+        u32x4 at[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const u32x4*>(s_at + (wk * 128 + i * 32 + l32) * rp + j0);
+        for (int i = 0; i < 2; ++i)
+          at[i] = *reinterpret_cast<const u32x4*>(s_at + (wave * 64 + i * 32 + l32) * rp + j0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int ml = wm * 64 + j * 32 + l32;
+        for (int j = 0; j < 8; ++j) {
+          const int ml = j * 32 + l32;
           const u32x4 uh = *reinterpret_cast<const u32x4*>(s_dh + ml * rp + j0);
           const u32x4 ul = *reinterpret_cast<const u32x4*>(s_dl + ml * rp + j0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i][j] = mfma32(af[i], uh, acc[i][j]);
-            acc[i][j] = mfma32(af[i], ul, acc[i][j]);
+          for (int i = 0; i < 2; ++i) {
+            acc[i][j] = mfma32(at[i], uh, acc[i][j]);
+            acc[i][j] = mfma32(at[i], ul, acc[i][j]);
           }
         }
       }
@@ -322,14 +391,14 @@ __global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
   // store: lane holds D[k = 8q + 4h + t][m = l32] of each 32x32 tile
   const int64_t G = a.Gq != nullptr ? (K >> a.pool_shift) : 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t m = m0 + wm * 64 + j * 32 + l32;
+    for (int j = 0; j < 8; ++j) {
+      const int64_t m = m0 + j * 32 + l32;
       if (m >= M) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t k = k0 + wk * 128 + i * 32 + 8 * q + 4 * h;
+        const int64_t k = k0 + wave * 64 + i * 32 + 8 * q + 4 * h;
         if (k >= K) continue;
         float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
         float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
@@ -353,9 +422,9 @@ __global__ __launch_bounds__(512, 1) void k_dx_gemm(DxArgs a) {
 hipError_t launch_dx_gemm(const DxArgs& a, int fmt, hipStream_t stream) {
   const int grid = static_cast<int>(((a.M + kTMx - 1) / kTMx) * ((a.w.K + kTK - 1) / kTK));
   if (fmt == kFmtNF4)
-    hipLaunchKernelGGL(k_dx_gemm<kFmtNF4>, dim3(grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(k_dx_gemm<kFmtNF4>, dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_dx_gemm<kFmtINT4>, dim3(grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(k_dx_gemm<kFmtINT4>, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
