@@ -13,10 +13,11 @@
 // only ever reads the weights it decoded itself, so only the shared dY tile
 // needs the workgroup barrier.  The next step's weights are decoded while
 // the current step's MFMAs run (a two-stage register pipeline over the four
-// 16-row sub-steps, two words of the decode in each).  The dY tile of a step
-// arrives by direct-to-LDS loads two steps ahead, the codes three.  Each LDS
-// stage is an array of its own, so that the compiler can tell that reads of
-// one stage do not depend on loads still landing in another.
+// 16-row sub-steps).  The dY tile of a step arrives by direct-to-LDS loads
+// two steps ahead, the packed codes (whole rows, shared by the four waves)
+// three steps ahead.  Each LDS stage is an array of its own, so that the
+// compiler can tell that reads of one stage do not depend on loads still
+// landing in another.
 // The adapter term du A is 2*ceil(r/16) extra MFMA k-steps (du split hi +
 // lo), read from A^T [K][r].
 #include "device_common.hpp"
@@ -32,6 +33,7 @@ constexpr int kNS = 64;                   // reduction rows per step
 constexpr int kWReg = kNS * 64 * 2;       // one wave's decoded slab: 64 rows x 64 columns, 8 KB
 constexpr int kWStage = 4 * kWReg;        // 32 KB
 constexpr int kDyStage = kTMx * kNS * 2;  // 32 KB
+constexpr int kCStage = kNS * kTK / 2;    // packed codes of a step: 8 KB
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -55,17 +57,15 @@ __device__ __forceinline__ int remap_xcd(int bid, int n) {
   return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
-// Codes and raw decode constants of one lane's row segment (64 columns).
+// Raw decode constants of one lane's row segment (64 columns).
 template <int FMT>
-struct RowCodes;
+struct RowParams;
 template <>
-struct RowCodes<kFmtNF4> {
-  u32x4 c[2];
+struct RowParams<kFmtNF4> {
   BlockParams bp;
 };
 template <>
-struct RowCodes<kFmtINT4> {
-  u32x4 c[2];
+struct RowParams<kFmtINT4> {
   uint32_t sz[2];  // per group: scale | zero << 16
 };
 
@@ -77,8 +77,11 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_w1[kWStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_dy0[kDyStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_dy1[kDyStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_c0[kCStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_c1[kCStage];
   uint8_t* const s_w[2] = {s_w0, s_w1};
   uint8_t* const s_dy[2] = {s_dy0, s_dy1};
+  uint8_t* const s_c[2] = {s_c0, s_c1};
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -126,13 +129,37 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
           static_cast<int>(static_cast<uint32_t>(i * 32 * N * 2) + nb), 0, 0);
   };
 
-  // codes of row st*64 + lane, columns [kwc, kwc + 64): two 16-byte loads
-  auto load_codes = [&](int64_t st, RowCodes<FMT>& rc) {
+  // Packed codes of a step (64 rows x the tile's 128 bytes) by direct-to-LDS
+  // loads, each instruction 8 whole rows (wave w: rows 16 w .. 16 w + 15),
+  // 16-byte chunk c of row r at c ^ ((r / 2) % 8).  Rows past N fall outside
+  // the resource; columns past K meet masked tables.
+  const rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.w.codes), 0,
+                                                      static_cast<int>(N * (K >> 1)), 0x00020000);
+  uint32_t cvoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int crow = wave * 16 + 8 * i + (lane >> 3);
+    cvoff[i] = static_cast<uint32_t>(crow * (K >> 1) + (k0 >> 1) + (((lane & 7) ^ ((crow >> 1) & 7)) << 4));
+  }
+  auto dma_codes = [&](int64_t st, int stage) {
+    const int64_t stc = st < nsteps ? st : nsteps - 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          cr, (lds_ptr_t)(s_c[stage] + (2 * wave + i) * 1024), 16, cvoff[i],
+          static_cast<int>(static_cast<uint32_t>(stc * kNS * (K >> 1))), 0, 0);
+  };
+  // this lane's row segment (row `lane`, the wave's 32 bytes) of a stage
+  u32x4 cw[2];
+  auto read_codes = [&](int stage) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      cw[q] = *reinterpret_cast<const u32x4*>(s_c[stage] + lane * 128 + (((2 * wave + q) ^ ((lane >> 1) & 7)) << 4));
+  };
+  // decode constants of row st*64 + lane, columns [kwc, kwc + 64)
+  auto load_params = [&](int64_t st, RowParams<FMT>& rc) {
     const int64_t n = st * kNS + lane;
     const int64_t nc = n < N ? n : N - 1;
-    const uint8_t* row = a.w.codes + nc * (K >> 1) + (kwc >> 1);
-    rc.c[0] = *reinterpret_cast<const u32x4*>(row);
-    rc.c[1] = *reinterpret_cast<const u32x4*>(row + 16);
     if constexpr (FMT == kFmtNF4) {
       rc.bp = load_block_params<kFmtNF4>(a.w, nc, kwc >> 6, true);
     } else {
@@ -149,10 +176,19 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
   Lut16 lut[2][NL];
   float lscale[2];
-  auto build_lut_part = [&](int set, const RowCodes<FMT>& rc, int64_t st, int part) {
+  auto build_lut_part = [&](int set, const RowParams<FMT>& rc, int64_t st, int part) {
     const bool valid = kvalid && st * kNS + lane < N;
     if constexpr (FMT == kFmtNF4) {
-      if (part == 0) lscale[set] = valid ? nf4_params_scale(a.w, rc.bp) : 0.0f;
+      if (part == 0) {
+        // the block scale of nf4_params_scale, formed without branches (a
+        // branch here would wait for every load in flight): both forms,
+        // then bit selects on the double-quantization flag and validity
+        const float s2 = __uint_as_float(rc.bp.b);
+        const float sdq = static_cast<float>(static_cast<int8_t>(rc.bp.a & 0xFFu)) * (s2 * (1.0f / 127.0f));
+        const uint32_t dqm = a.w.dq ? 0xFFFFFFFFu : 0u;
+        const uint32_t bits = (__float_as_uint(sdq) & dqm) | (rc.bp.b & ~dqm);
+        lscale[set] = __uint_as_float(valid ? bits : 0u);
+      }
       const float sc = lscale[set];
       uint32_t pr[4];
 #pragma unroll
@@ -172,8 +208,8 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   // decoded word q (columns 8q .. 8q+7) of this lane's row into a slab stage
   const int wrow = wave * kWReg + lane * 128;
   const int wswl = wsw(lane);
-  auto decode_word = [&](int set, const RowCodes<FMT>& rc, int q, int stage) {
-    const u32x4 d = lut_decode8(lut[set][NL == 1 ? 0 : (q >> 2)], rc.c[q >> 2][q & 3]);
+  auto decode_word = [&](int set, int q, int stage) {
+    const u32x4 d = lut_decode8(lut[set][NL == 1 ? 0 : (q >> 2)], cw[q >> 2][q & 3]);
     *reinterpret_cast<u32x4*>(s_w[stage] + wrow + ((q ^ wswl) << 4)) = d;
   };
 
@@ -211,37 +247,43 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   // Prologue: dY of steps 0 and 1 in LDS, codes of steps 1 and 2 in
   // registers, step 0 decoded and the tables of step 1 built before the
   // loop.
-  RowCodes<FMT> rc[2];
+  RowParams<FMT> rc[2];
   load_dy(0, 0);
   load_dy(1, 1);
-  load_codes(0, rc[0]);
-  load_codes(1, rc[1]);
+  dma_codes(0, 0);
+  dma_codes(1, 1);
+  load_params(0, rc[0]);
+  load_params(1, rc[1]);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  read_codes(0);
   build_lut_part(0, rc[0], 0, 0);
   build_lut_part(0, rc[0], 0, 1);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) decode_word(0, rc[0], q, 0);
+  for (int q = 0; q < 8; ++q) decode_word(0, q, 0);
   build_lut_part(1, rc[1], 1, 0);
   build_lut_part(1, rc[1], 1, 1);
-  load_codes(2, rc[0]);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  load_params(2, rc[0]);
+  read_codes(1);
+  __syncthreads();  // every wave has read its step-0 codes
+  dma_codes(2, 0);
 
   u32x4 af[2][2], bf[2][8];
   af[0][0] = read_a(0, 0, 0);
   read_b(0, 0, bf[0]);
-  // One step st (ri = st & 1: dY and weight stage, table set of step st + 2,
-  // code set of step st + 2; the other sets hold step st + 1): the products
-  // of st while step st + 1 is decoded into the other weight stage, two
-  // words per sub-step, and the tables of step st + 2 are built in
+  // One step st (ri = st & 1: dY and weight stage, table and constant set
+  // of step st + 2): the products of st while step st + 1 is decoded from
+  // the code registers into the other weight stage (three, three and two
+  // words in sub-steps 0, 1, 2), and the tables of step st + 2 are built in
   // sub-steps 2 and 3.  After sub-step 2 the stage barrier (the dY of st + 1
-  // has landed; every wave has read its last dY fragments of st).  Sub-step
-  // 3 reads the first column tile and the dY fragments of st + 1; its
-  // second column tile is read at the top of st + 1, under the first
-  // tile's products.
-  // Loads: waves 0, 1 take the dY of st + 2 right after the barrier, waves
-  // 2, 3 after sub-step 3 (so that two waves keep the matrix cores busy
-  // while the other two issue), and all take the codes of st + 3 after
-  // sub-step 3 (their code set is decoded by then).
+  // and the codes of st + 2 have landed; every wave has read its last dY
+  // fragments of st and its codes of st + 1).  Sub-step 3 reads the first
+  // column tile and the dY fragments of st + 1 and this lane's codes of
+  // st + 2; the second column tile is read at the top of st + 1, under the
+  // first tile's products.  Loads: waves 0, 1 take the dY of st + 2 and the
+  // codes of st + 3 right after the barrier, waves 2, 3 after sub-step 3 (so
+  // that two waves keep the matrix cores busy while the other two issue);
+  // the constants of st + 3 load after sub-step 3.
   auto k_loop = [&](auto early_c) __attribute__((always_inline)) {
   constexpr bool early = decltype(early_c)::value;
   auto step = [&](int64_t st, auto ri_c) __attribute__((always_inline)) {
@@ -258,39 +300,49 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         af[nxt][0] = read_a(ri ^ 1, 0, 0);
         read_b(ri ^ 1, 0, bf[nxt]);
       }
-      decode_word(ri ^ 1, rc[ri ^ 1], 2 * nn, ri ^ 1);
-      decode_word(ri ^ 1, rc[ri ^ 1], 2 * nn + 1, ri ^ 1);
+      // words 0-2, 3-5 and 6-7 of the next step's row in sub-steps 0, 1, 2
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q / 3 == nn) decode_word(ri ^ 1, q, ri ^ 1);
       if (nn == 2) build_lut_part(ri, rc[ri], st + 2, 0);
-      if (nn == 3) build_lut_part(ri, rc[ri], st + 2, 1);
+      if (nn == 3) {
+        build_lut_part(ri, rc[ri], st + 2, 1);
+        read_codes(ri);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
-      // issue order: 1 MFMA, a share of the decode, the operand reads of
-      // the next sub-step and the decode's LDS writes spread between
+      // issue order: the operand reads of the next sub-step first (the
+      // LDS, not the matrix cores, is the tighter resource here), then
+      // {1 MFMA, 5 VALU of the decode} x 16
+      if (nn == 0)
+        __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
+      else if (nn < 3)
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (nn < 2)
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        else
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        if (g % 4 == 3)
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        else
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (g == 5 || g == 11) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (nn == 2) {
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (early) load_dy(st + 2, ri);
+        if (early) {
+          load_dy(st + 2, ri);
+          dma_codes(st + 3, ri ^ 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (nn == 3) {
-        if (!early) load_dy(st + 2, ri);
-        load_codes(st + 3, rc[ri ^ 1]);
+        if (!early) {
+          load_dy(st + 2, ri);
+          dma_codes(st + 3, ri ^ 1);
+        }
+        load_params(st + 3, rc[ri ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
