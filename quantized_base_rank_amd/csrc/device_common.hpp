@@ -268,6 +268,18 @@ __device__ __forceinline__ float nf4_params_scale(const WeightView& w, BlockPara
   return w.dq ? nf4_dq_scale(static_cast<int8_t>(p.a), __uint_as_float(p.b)) : __uint_as_float(p.b);
 }
 
+// The same scale (zero for an invalid block) formed without branches: both
+// forms, then bit selects on the flag and on validity.  Inside a pipelined
+// loop a branch here would split the scheduling region and wait for every
+// load in flight.
+__device__ __forceinline__ float nf4_params_scale_sel(const WeightView& w, BlockParams p, bool valid) {
+  const float s2 = __uint_as_float(p.b);
+  const float sdq = nf4_dq_scale(static_cast<int8_t>(p.a & 0xFFu), s2);
+  const uint32_t dqm = w.dq ? 0xFFFFFFFFu : 0u;
+  const uint32_t bits = (__float_as_uint(sdq) & dqm) | (p.b & ~dqm);
+  return __uint_as_float(valid ? bits : 0u);
+}
+
 // lut[0] decodes elements 0..31 of the block, lut[1] elements 32..63.
 template <int FMT>
 __device__ __forceinline__ void luts_from_params(const WeightView& w, BlockParams p,

@@ -179,16 +179,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   auto build_lut_part = [&](int set, const RowParams<FMT>& rc, int64_t st, int part) {
     const bool valid = kvalid && st * kNS + lane < N;
     if constexpr (FMT == kFmtNF4) {
-      if (part == 0) {
-        // the block scale of nf4_params_scale, formed without branches (a
-        // branch here would wait for every load in flight): both forms,
-        // then bit selects on the double-quantization flag and validity
-        const float s2 = __uint_as_float(rc.bp.b);
-        const float sdq = static_cast<float>(static_cast<int8_t>(rc.bp.a & 0xFFu)) * (s2 * (1.0f / 127.0f));
-        const uint32_t dqm = a.w.dq ? 0xFFFFFFFFu : 0u;
-        const uint32_t bits = (__float_as_uint(sdq) & dqm) | (rc.bp.b & ~dqm);
-        lscale[set] = __uint_as_float(valid ? bits : 0u);
-      }
+      if (part == 0) lscale[set] = nf4_params_scale_sel(a.w, rc.bp, valid);
       const float sc = lscale[set];
       uint32_t pr[4];
 #pragma unroll

@@ -89,7 +89,7 @@ __device__ __forceinline__ Lut16 step_lut<kFmtNF4>(const WeightView& w,
                                                    const StepParams<kFmtNF4>& p, int r, int,
                                                    bool valid) {
   // an invalid block (past K) decodes to zeros through a zero scale
-  return lut_nf4(w.cb, valid ? nf4_params_scale(w, p.bp[r]) : 0.0f);
+  return lut_nf4(w.cb, nf4_params_scale_sel(w, p.bp[r], valid));
 }
 template <>
 __device__ __forceinline__ Lut16 step_lut<kFmtINT4>(const WeightView&,
