@@ -130,12 +130,15 @@ __global__ __launch_bounds__(256) void k_nt_skinny(NtArgs a) {
     return static_cast<uint32_t>(((static_cast<int64_t>(tile) * a.splits + sp) * kNtTileFloats +
                                   ((jh + 2 * t) * 32 + l32) * kNtRowsPerWg + mh * 32 + 8 * i + 4 * h) * 4);
   };
+  // only column tiles below JT carry partial sums (a wave whose tiles are
+  // all past JT, e.g. jh = 1 when JT = 1, publishes and reads nothing)
   if (a.splits > 1) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
+      if (jh + 2 * t < JT)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st_sys16(pr, poff(split, t, i), f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]});
+        for (int i = 0; i < 4; ++i)
+          st_sys16(pr, poff(split, t, i), f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]});
     if (__builtin_amdgcn_readfirstlane(publish_and_ticket(a.counters + tile, &s_ticket)) !=
         static_cast<uint32_t>(a.splits - 1))
       return;
@@ -150,15 +153,17 @@ __global__ __launch_bounds__(256) void k_nt_skinny(NtArgs a) {
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
+          if (jh + 2 * t < JT)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[q][t][i] = ld_sys16(pr, poff(sp0 + q < a.splits ? sp0 + q : a.splits - 1, t, i));
+            for (int i = 0; i < 4; ++i) v[q][t][i] = ld_sys16(pr, poff(sp0 + q < a.splits ? sp0 + q : a.splits - 1, t, i));
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (sp0 + q < a.splits)
 #pragma unroll
           for (int t = 0; t < 2; ++t)
+            if (jh + 2 * t < JT)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sum[t][i] += v[q][t][i];
+              for (int i = 0; i < 4; ++i) sum[t][i] += v[q][t][i];
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t)

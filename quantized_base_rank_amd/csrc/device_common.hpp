@@ -321,6 +321,20 @@ __device__ __forceinline__ f32x4 ld_sys4(const float* p) {
 // resource: buffer_{store,load}_dwordx4 with sc0 sc1.  `off` is a byte offset
 // from the (wave-uniform) base; buffers are < 2 GiB.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// A buffer resource over [base, base + bytes) whose fields go through
+// readfirstlane, so that it lives in scalar registers even where the compiler
+// cannot prove the base wave-uniform (a resource in vector registers turns
+// every load into a loop over the lanes).  readfirstlane returns a signed
+// int, so each half of the base is taken back to 32 unsigned bits before it
+// is widened.
+__device__ __forceinline__ rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
+  const uint64_t u = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), 0,
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000);
+}
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }

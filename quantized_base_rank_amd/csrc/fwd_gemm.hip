@@ -42,42 +42,86 @@ __device__ __forceinline__ int remap_xcd(int bid, int n) {
   return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
 }
 
+// Raw block constants of one K step for a lane's two rows (the scale is
+// formed when the table is built, so the loads are consumed a step later).
 template <int FMT>
 struct StepParams;
 template <>
 struct StepParams<kFmtNF4> {
-  BlockParams bp[2];  // per row, raw: the scale is formed when the table is built
+  BlockParams bp[2];  // per row: a = the 8-bit code (DQ), b = fp32 bits of s2 or absmax
 };
 template <>
 struct StepParams<kFmtINT4> {
-  uint32_t sz[2][2];  // per row, per group: scale (lo16) | zero (hi16)
+  uint32_t s[2], z[2];  // per row: fp16 scales and zeros of the two groups, low group first
+};
+
+// Where a lane's block constants live: buffer resources over the constant
+// arrays and per-lane offsets, so that a step's loads take only its scalar
+// offset (no per-lane address arithmetic, no 64-bit pointers).
+template <int FMT>
+struct ParamSrc;
+template <>
+struct ParamSrc<kFmtNF4> {
+  rsrc_t r8, rw;     // 8-bit codes (DQ; any bytes otherwise); wide constants
+  uint32_t lb[2];    // flat block index of the lane's row at step 0
+  uint32_t sh;       // 8 with DQ (group of 256 blocks), else 0
+};
+template <>
+struct ParamSrc<kFmtINT4> {
+  rsrc_t rs, rz;
+  uint32_t lg[2];    // byte offset of the lane's first group at step 0
 };
 
 template <int FMT>
-__device__ __forceinline__ void load_params(const WeightView& w, const int64_t (&nr)[2],
-                                            int64_t kblk, bool valid, StepParams<FMT>& p);
-
+__device__ __forceinline__ ParamSrc<FMT> param_src(const WeightView& w, const int64_t (&nr)[2], int h);
 template <>
-__device__ __forceinline__ void load_params<kFmtNF4>(const WeightView& w, const int64_t (&nr)[2],
-                                                     int64_t kblk, bool valid,
-                                                     StepParams<kFmtNF4>& p) {
-  (void)valid;  // indices are in range; invalid blocks are masked at decode
+__device__ __forceinline__ ParamSrc<kFmtNF4> param_src<kFmtNF4>(const WeightView& w, const int64_t (&nr)[2],
+                                                                int h) {
+  ParamSrc<kFmtNF4> ps;
+  const int64_t nb = w.N * (w.K >> 6);
+  ps.r8 = uniform_rsrc(w.absmax, static_cast<uint32_t>(w.dq ? nb : 4 * nb));
+  ps.rw = uniform_rsrc(w.dq ? static_cast<const void*>(w.absmax2) : w.absmax,
+                       static_cast<uint32_t>(w.dq ? 4 * ((nb + 255) >> 8) : 4 * nb));
 #pragma unroll
-  for (int r = 0; r < 2; ++r) p.bp[r] = load_block_params<kFmtNF4>(w, nr[r], kblk, true);
+  for (int r = 0; r < 2; ++r) ps.lb[r] = static_cast<uint32_t>(nr[r] * (w.K >> 6) + h);
+  ps.sh = w.dq ? 8u : 0u;
+  return ps;
+}
+template <>
+__device__ __forceinline__ ParamSrc<kFmtINT4> param_src<kFmtINT4>(const WeightView& w, const int64_t (&nr)[2],
+                                                                  int h) {
+  ParamSrc<kFmtINT4> ps;
+  const uint32_t bytes = static_cast<uint32_t>(w.N * (w.K >> 5) * 2);
+  ps.rs = uniform_rsrc(w.scale, bytes);
+  ps.rz = uniform_rsrc(w.zero, bytes);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) ps.lg[r] = static_cast<uint32_t>((nr[r] * (w.K >> 5) + 2 * h) * 2);
+  return ps;
 }
 
+// Block constants of K step ks (blocks 2 ks + h).  Near the end of K a lane
+// of the upper half may read the next row's constants (or zeros past the
+// array); such blocks are masked when the table is built.
+template <int FMT>
+__device__ __forceinline__ void load_params(const ParamSrc<FMT>& ps, int64_t ks, StepParams<FMT>& p);
 template <>
-__device__ __forceinline__ void load_params<kFmtINT4>(const WeightView& w, const int64_t (&nr)[2],
-                                                      int64_t kblk, bool valid,
-                                                      StepParams<kFmtINT4>& p) {
+__device__ __forceinline__ void load_params<kFmtNF4>(const ParamSrc<kFmtNF4>& ps, int64_t ks,
+                                                     StepParams<kFmtNF4>& p) {
+  const uint32_t b2 = static_cast<uint32_t>(2 * ks);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int64_t g = nr[r] * (w.K >> 5) + kblk * 2;
+    p.bp[r].a = __builtin_amdgcn_raw_buffer_load_b8(ps.r8, ps.lb[r], static_cast<int>(b2), 0);
+    p.bp[r].b = __builtin_amdgcn_raw_buffer_load_b32(ps.rw, ((ps.lb[r] + b2) >> ps.sh) << 2, 0, 0);
+  }
+}
+template <>
+__device__ __forceinline__ void load_params<kFmtINT4>(const ParamSrc<kFmtINT4>& ps, int64_t ks,
+                                                      StepParams<kFmtINT4>& p) {
+  const int g8 = static_cast<int>(8 * ks);  // 4 groups of 2 bytes per step
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      p.sz[r][q] = valid ? (static_cast<uint32_t>(w.scale[g + q]) |
-                            (static_cast<uint32_t>(w.zero[g + q]) << 16))
-                         : 0u;
+  for (int r = 0; r < 2; ++r) {
+    p.s[r] = __builtin_amdgcn_raw_buffer_load_b32(ps.rs, ps.lg[r], g8, 0);
+    p.z[r] = __builtin_amdgcn_raw_buffer_load_b32(ps.rz, ps.lg[r], g8, 0);
   }
 }
 
@@ -95,7 +139,8 @@ template <>
 __device__ __forceinline__ Lut16 step_lut<kFmtINT4>(const WeightView&,
                                                     const StepParams<kFmtINT4>& p, int r, int q,
                                                     bool valid) {
-  const uint32_t sz = valid ? p.sz[r][q] : 0u;
+  // scale (low 16 bits) | zero (high 16 bits) of group q
+  const uint32_t sz = valid ? perm(p.z[r], p.s[r], q == 0 ? 0x05040100u : 0x07060302u) : 0u;
   return lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
                   half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
 }
@@ -185,10 +230,8 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
         c[r][q] = *reinterpret_cast<const u32x4*>(&s_x[buf][kXTile + row * 64 + (((2 * h + q) ^ sw) << 4)]);
     }
   };
-  auto load_step_params = [&](int64_t ks, StepParams<FMT>& p) {
-    const int64_t kk = ks * kKS + h * 64;
-    load_params<FMT>(a.w, nr, (kk < K ? kk : K - 64) >> 6, true, p);
-  };
+  const ParamSrc<FMT> psrc = param_src<FMT>(a.w, nr, h);
+  auto load_step_params = [&](int64_t ks, StepParams<FMT>& p) { load_params<FMT>(psrc, ks, p); };
 
   constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
   Lut16 lut[2][NL];
