@@ -66,7 +66,7 @@ struct RowParams<kFmtNF4> {
 };
 template <>
 struct RowParams<kFmtINT4> {
-  uint32_t sz[2];  // per group: scale | zero << 16
+  uint32_t s, z;  // fp16 scales and zeros of the two groups, low group first
 };
 
 template <int FMT>
@@ -156,17 +156,32 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     for (int q = 0; q < 2; ++q)
       cw[q] = *reinterpret_cast<const u32x4*>(s_c[stage] + lane * 128 + (((2 * wave + q) ^ ((lane >> 1) & 7)) << 4));
   };
-  // decode constants of row st*64 + lane, columns [kwc, kwc + 64)
+  // decode constants of row st*64 + lane, columns [kwc, kwc + 64), by buffer
+  // loads with a per-lane offset fixed for the kernel and a scalar step
+  // offset (rows past N read zeros; their tables are masked anyway)
+  const int64_t nblk = N * (K >> 6);
+  rsrc_t pr0, pr1;
+  uint32_t plane;
+  if constexpr (FMT == kFmtNF4) {
+    pr0 = uniform_rsrc(a.w.absmax, static_cast<uint32_t>(a.w.dq ? nblk : 4 * nblk));
+    pr1 = uniform_rsrc(a.w.dq ? static_cast<const void*>(a.w.absmax2) : a.w.absmax,
+                       static_cast<uint32_t>(a.w.dq ? 4 * ((nblk + 255) >> 8) : 4 * nblk));
+    plane = static_cast<uint32_t>(lane * (K >> 6) + (kwc >> 6));
+  } else {
+    pr0 = uniform_rsrc(a.w.scale, static_cast<uint32_t>(4 * nblk));
+    pr1 = uniform_rsrc(a.w.zero, static_cast<uint32_t>(4 * nblk));
+    plane = static_cast<uint32_t>((lane * (K >> 5) + (kwc >> 5)) * 2);
+  }
+  const uint32_t pshift = a.w.dq ? 8u : 0u;
   auto load_params = [&](int64_t st, RowParams<FMT>& rc) {
-    const int64_t n = st * kNS + lane;
-    const int64_t nc = n < N ? n : N - 1;
     if constexpr (FMT == kFmtNF4) {
-      rc.bp = load_block_params<kFmtNF4>(a.w, nc, kwc >> 6, true);
+      const uint32_t sb = static_cast<uint32_t>(st * kNS * (K >> 6));
+      rc.bp.a = __builtin_amdgcn_raw_buffer_load_b8(pr0, plane, static_cast<int>(sb), 0);
+      rc.bp.b = __builtin_amdgcn_raw_buffer_load_b32(pr1, ((plane + sb) >> pshift) << 2, 0, 0);
     } else {
-      const int64_t g = nc * (K >> 5) + (kwc >> 5);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        rc.sz[q] = static_cast<uint32_t>(a.w.scale[g + q]) | (static_cast<uint32_t>(a.w.zero[g + q]) << 16);
+      const int so = static_cast<int>(st * kNS * (K >> 5) * 2);
+      rc.s = __builtin_amdgcn_raw_buffer_load_b32(pr0, plane, so, 0);
+      rc.z = __builtin_amdgcn_raw_buffer_load_b32(pr1, plane, so, 0);
     }
   };
   // Tables of a step's row, two sets (by step parity), each built in two
@@ -191,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         lut[set][0].hi[2 * part + q] = perm(pr[2 * q + 1], pr[2 * q], 0x07050301u);
       }
     } else {
-      const uint32_t sz = valid ? rc.sz[part] : 0u;
+      const uint32_t sz = valid ? perm(rc.z, rc.s, part == 0 ? 0x05040100u : 0x07060302u) : 0u;
       lut[set][part] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
                                 half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
     }
