@@ -305,23 +305,22 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
         acc[1][ms] = mfma32(wf[cur][1], xf[cur][ms], acc[1][ms]);
       }
       if (tt < 7) {
-        // issue order: 2 MFMA, 1 LDS read of the next sub-step, ~6 VALU of
-        // the next decode; x8
+        // issue order: the 8 LDS reads of the next sub-step first, then
+        // {1 MFMA, 3 VALU of the next decode} x 16
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
       } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        // the next step's 4 code reads and 8 token-fragment reads first,
+        // then {1 MFMA, 7 VALU of its tables and first decode} x 16
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-        for (int i = 0; i < 7; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 15, 0);
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
