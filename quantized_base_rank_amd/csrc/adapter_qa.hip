@@ -230,8 +230,11 @@ __global__ __launch_bounds__(256) void k_qa_grad_in(QaArgs a) {
       const int j = jb + (idx >> 5), q = idx & 31;
       const uint16_t* arow = a.A + static_cast<int64_t>(j < r ? j : r - 1) * G;
       const int64_t gq = g0 + q * 8;
-      if (vec && gq + 8 <= G) {
-        av[i] = *reinterpret_cast<const u32x4*>(arow + gq);
+      if (vec) {
+        // wave-uniform path: the load address is clamped into the row and the
+        // pieces past G are zeroed after the load (no divergent branch)
+        const u32x4 v = *reinterpret_cast<const u32x4*>(arow + (gq + 8 <= G ? gq : G - 8));
+        av[i] = gq + 8 <= G ? v : u32x4{0u, 0u, 0u, 0u};
       } else {
         uint32_t h[8];
 #pragma unroll
