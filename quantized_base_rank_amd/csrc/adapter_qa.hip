@@ -4,7 +4,10 @@
 // features.]
 //
 //   P[m][g]  = sum_{i < 32} x[m][32 g + i]     u[m][j]  = sum_g P[m][g] A[j][g]
-//   dA[j][g] = sum_m du[m][j] P[m][g]          Gq[m][g] = sum_j du[m][j] A[j][g]
+//   dA[j][g] = sum_m du[m][j] P[m][g]
+//
+// (The input gradient du A, repeated over each group, is added by the large-M
+// input-gradient GEMM from A^T with one row per group.)
 //
 // The pool is the INT4 group (32), the only pooled case.  Every sum is taken
 // in a fixed order, so results are bit-identical from run to run.
@@ -20,7 +23,6 @@ constexpr int kQaTokMax = 8;  // tokens per workgroup (pooling, input gradient)
 constexpr int kQaDaTile = 64;  // dA tile: 64 adapter rows x 64 groups
 constexpr int kQaDaBlk = 32;   // tokens staged per step of a dA partial
 constexpr int kQaMaxRank = 128;
-constexpr int kQaGiRows = 32;  // rows of A staged per step of the input gradient
 
 // P and u for a block of tokens (1024 threads).  A pass loads 8 16-byte
 // pieces per thread, flattened over (token, piece) so that every load of
@@ -193,83 +195,6 @@ __global__ __launch_bounds__(256) void k_qa_dA_sum(QaArgs a) {
   if (qq == 0 && e0 < n) a.dA_out[e0] = f32_to_bf16(q);
 }
 
-// Gq[m][g] = sum_j du[m][j] A[j][g] (the pooled adapter's input gradient
-// before it is repeated over the group), for a block of 8 tokens and 256
-// groups: du of the block and the A tile (read with 16-byte loads, all issued
-// before use) are staged in LDS; one thread per group.
-__global__ __launch_bounds__(256) void k_qa_grad_in(QaArgs a) {
-  __shared__ float s_du[kQaTokMax * kQaMaxRank];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[kQaGiRows * 256];
-  const int tid = threadIdx.x;
-  const int tok = a.tok;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * tok;
-  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * 256;
-  const int64_t G = a.G;
-  const int r = a.r;
-  // du of the block (tok * r <= 1024 values): four unconditional loads per
-  // thread, issued together with the first rows of A below
-  float dv[kQaTokMax * kQaMaxRank / 256];
-  const int64_t dlast = a.M * r - 1;
-#pragma unroll
-  for (int i = 0; i < kQaTokMax * kQaMaxRank / 256; ++i) {
-    const int64_t e = m0 * r + i * 256 + tid;
-    dv[i] = a.du[e < dlast ? e : dlast];
-  }
-  const int64_t g = g0 + tid;
-  float acc[kQaTokMax];
-#pragma unroll
-  for (int t = 0; t < kQaTokMax; ++t) acc[t] = 0.0f;
-  // rows of A in blocks of 32: thread (row j, piece q) loads 8 groups, as
-  // one 16-byte load when rows are 16-byte aligned (G a multiple of 8)
-  const bool vec = (G & 7) == 0;
-  for (int jb = 0; jb < r; jb += kQaGiRows) {
-    u32x4 av[kQaGiRows * 32 / 256];
-#pragma unroll
-    for (int i = 0; i < kQaGiRows * 32 / 256; ++i) {
-      const int idx = i * 256 + tid;
-      const int j = jb + (idx >> 5), q = idx & 31;
-      const uint16_t* arow = a.A + static_cast<int64_t>(j < r ? j : r - 1) * G;
-      const int64_t gq = g0 + q * 8;
-      if (vec) {
-        // wave-uniform path: the load address is clamped into the row and the
-        // pieces past G are zeroed after the load (no divergent branch)
-        const u32x4 v = *reinterpret_cast<const u32x4*>(arow + (gq + 8 <= G ? gq : G - 8));
-        av[i] = gq + 8 <= G ? v : u32x4{0u, 0u, 0u, 0u};
-      } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = gq + e < G ? arow[gq + e] : 0u;
-        av[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-      }
-    }
-    __syncthreads();  // the previous block's rows are consumed
-    if (jb == 0) {
-#pragma unroll
-      for (int i = 0; i < kQaTokMax * kQaMaxRank / 256; ++i) {
-        const int idx = i * 256 + tid;
-        if (idx < tok * r) s_du[idx] = m0 * r + idx <= dlast ? dv[i] : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kQaGiRows * 32 / 256; ++i) {
-      const int idx = i * 256 + tid;
-      *reinterpret_cast<u32x4*>(&s_a[(idx >> 5) * 256 + (idx & 31) * 8]) = av[i];
-    }
-    __syncthreads();
-    const int jn = r - jb < kQaGiRows ? r - jb : kQaGiRows;
-    for (int jj = 0; jj < jn; ++jj) {
-      const float w = bf16_to_f32(s_a[jj * 256 + tid]);
-#pragma unroll
-      for (int t = 0; t < kQaTokMax; ++t)
-        if (t < tok) acc[t] += s_du[t * r + jb + jj] * w;
-    }
-  }
-  if (g >= G) return;
-#pragma unroll
-  for (int t = 0; t < kQaTokMax; ++t)
-    if (t < tok && m0 + t < a.M) a.Gq_out[(m0 + t) * G + g] = acc[t];
-}
-
 // Tokens per workgroup of the pooling kernel: the P block of all its tokens
 // sits in LDS (at most 64 KB).
 int qa_tokens(int64_t G) {
@@ -309,15 +234,6 @@ hipError_t launch_qa_dA(const QaArgs& in, hipStream_t stream) {
   hipLaunchKernelGGL(k_qa_dA_part, grid, dim3(256), 0, stream, a);
   const int64_t n = static_cast<int64_t>(a.r) * a.G;
   hipLaunchKernelGGL(k_qa_dA_sum, dim3(static_cast<uint32_t>((4 * n + 255) / 256)), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_qa_grad_in(const QaArgs& in, hipStream_t stream) {
-  if (in.r > kQaMaxRank) return hipErrorInvalidValue;
-  QaArgs a = in;
-  a.tok = kQaTokMax;
-  dim3 grid(static_cast<uint32_t>((a.G + 255) / 256), static_cast<uint32_t>((a.M + a.tok - 1) / a.tok));
-  hipLaunchKernelGGL(k_qa_grad_in, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -100,7 +100,7 @@ struct Plan {
   int tn2_splits_dB = 1, tn2_splits_dA = 1;
   int gf_splits = 1, gd_splits = 1;
   size_t off_counters = 0, off_u = 0, off_du = 0, off_Bt = 0, off_At = 0, off_P = 0,
-         off_Gq = 0, off_z = 0, off_partial = 0, total = 0;
+         off_z = 0, off_partial = 0, total = 0;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -147,9 +147,8 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.off_u = off;        off = align256(off + static_cast<size_t>(M) * r * sizeof(float));
   p.off_du = off;       off = align256(off + static_cast<size_t>(M) * r * sizeof(float));
   p.off_Bt = off;       off = align256(off + static_cast<size_t>(N) * r * sizeof(uint16_t));
-  p.off_At = off;       off = align256(off + (pool == 1 ? static_cast<size_t>(K) * r * sizeof(uint16_t) : 0));
+  p.off_At = off;       off = align256(off + static_cast<size_t>(G) * r * sizeof(uint16_t));
   p.off_P = off;        off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
-  p.off_Gq = off;       off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
   p.off_z = off;        off = align256(off + (p.small ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
   p.off_partial = off;  off = align256(off + static_cast<size_t>(partial) * sizeof(float));
   p.total = off;
@@ -374,7 +373,6 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     QLIN_TRY(launch_tn2(a, stream));
   }
   // dA = du^T P
-  float* Gq = nullptr;
   if (pool == 1) {
     QLIN_TRY(launch_split_hl(du, M, r, r, zp + 2 * M * jp, zp + 3 * M * jp, stream));
     Tn2Args a{};
@@ -391,22 +389,15 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     q.dA_out = dA;
     q.part = partial;
     QLIN_TRY(launch_qa_dA(q, stream));
-    if (dx != nullptr) {
-      Gq = ws_at<float>(workspace, p.off_Gq);
-      q.Gq_out = Gq;
-      QLIN_TRY(launch_qa_grad_in(q, stream));
-    }
   }
   if (dx == nullptr) return QLIN_OK;
-  // dX = dY W_bf16 + du A
-  uint16_t* At = nullptr;
-  if (pool == 1) {
-    At = ws_at<uint16_t>(workspace, p.off_At);
-    QLIN_TRY(launch_transpose16(A, r, K, At, stream));
-  }
+  // dX = dY W_bf16 + du A; with the pooled adapter A^T has one row per group
+  // and column k of dX reads row k >> log2(pool)
+  uint16_t* At = ws_at<uint16_t>(workspace, p.off_At);
+  QLIN_TRY(launch_transpose16(A, r, G, At, stream));
   DxArgs a{};
-  a.w = v; a.dy = dy; a.M = M; a.At = At; a.du = pool == 1 ? du : nullptr; a.r = r;
-  a.Gq = Gq; a.pool = pool; a.pool_shift = __builtin_ctz(static_cast<unsigned>(pool));
+  a.w = v; a.dy = dy; a.M = M; a.At = At; a.du = du; a.r = r;
+  a.pool = pool; a.pool_shift = __builtin_ctz(static_cast<unsigned>(pool));
   a.dx = dx;
   return hip_status(launch_dx_gemm(a, fmt, stream));
 }

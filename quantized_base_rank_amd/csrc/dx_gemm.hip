@@ -1,5 +1,5 @@
 // Input gradient of the adapted 4-bit layer for many tokens:
-//     dX = dY W_bf16 + du A            (QA-LoRA: + du A repeated per group)
+//     dX = dY W_bf16 + du A            (QA-LoRA: A repeated over each group)
 // [QLoRA "The QLoRA recipe" stage 3: gradients flow back through the frozen,
 //  dequantized weight; W itself receives no gradient.]
 //
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         mg = mg < M ? mg : M - 1;
         kg = kg < K ? kg : K - 1;
         const float* drow = a.du + mg * rr;
-        const uint16_t* arow = a.At + kg * rr;
+        const uint16_t* arow = a.At + (kg >> a.pool_shift) * rr;  // pooled: one A^T row per group
         if ((rr & 3) == 0) {
           const int jj = j < rr ? j : rr - 4;
           dv[q] = *reinterpret_cast<const f32x4*>(drow + jj);
@@ -447,7 +447,6 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   }
 
   // store: lane holds D[k = 8q + 4h + t][m = l32] of each 32x32 tile
-  const int64_t G = a.Gq != nullptr ? (K >> a.pool_shift) : 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -458,18 +457,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int64_t k = k0 + wave * 64 + i * 32 + 8 * q + 4 * h;
         if (k >= K) continue;
-        float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
-        float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if (a.Gq != nullptr) {
-          const float* gr = a.Gq + m * G;
-          v0 += gr[(k + 0) >> a.pool_shift];
-          v1 += gr[(k + 1) >> a.pool_shift];
-          v2 += gr[(k + 2) >> a.pool_shift];
-          v3 += gr[(k + 3) >> a.pool_shift];
-        }
         u32x2 o;
-        o.x = pack_bf16x2(v0, v1);
-        o.y = pack_bf16x2(v2, v3);
+        o.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+        o.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         *reinterpret_cast<u32x2*>(a.dx + m * K + k) = o;
       }
     }

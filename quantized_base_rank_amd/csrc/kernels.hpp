@@ -61,7 +61,6 @@ struct QaArgs {  // pooled-adapter helpers (QA-LoRA)
   const float* P_in;  // [M][G]
   float* P_out;       // [M][G]
   float* u_out;       // [M][r]
-  float* Gq_out;      // [M][G]
   uint16_t* dA_out;   // [r][G]
   float* part;        // dA partial sums [splits][r][G]
   int64_t M, K, G;
@@ -71,7 +70,6 @@ struct QaArgs {  // pooled-adapter helpers (QA-LoRA)
 hipError_t launch_qa_pool_u(const QaArgs& a, hipStream_t stream);
 int qa_dA_splits(int64_t M);
 int64_t qa_dA_partial_floats(int64_t M, int32_t r, int64_t G);
-hipError_t launch_qa_grad_in(const QaArgs& a, hipStream_t stream);
 hipError_t launch_qa_dA(const QaArgs& a, hipStream_t stream);
 
 // ------------------------------------------------- fused 4-bit GEMM kernels
@@ -93,15 +91,14 @@ hipError_t launch_fwd_gemm(const FwdArgs& a, int fmt, hipStream_t stream);
 int fwd_gemm_tiles(int64_t M, int64_t N);
 int64_t fwd_gemm_partial_floats(int64_t M, int64_t N, int splits);
 
-// dX[M][K] = dY W_bf16 + du A (+ Gq repeated over groups), large M.
+// dX[M][K] = dY W_bf16 + du A (A repeated over the groups of a pooled adapter), large M.
 struct DxArgs {
   WeightView w;
   const uint16_t* dy;  // [M][N]
   int64_t M;
-  const uint16_t* At;  // [K][r] (A transposed) or nullptr
+  const uint16_t* At;  // [K >> pool_shift][r] (A transposed) or nullptr
   const float* du;     // [M][r] or nullptr
   int32_t r;
-  const float* Gq;     // [M][K/pool] pooled-adapter input gradient, or nullptr
   int32_t pool;        // power of two
   int32_t pool_shift;  // log2(pool)
   uint16_t* dx;        // [M][K]
