@@ -470,23 +470,35 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
     if (tid == 0) a.counters[tmn] = 0u;
   }
 
-  // store: lane holds D[n = 8i + 4h + t][m = l32] of each 32x32 tile
+  // store: lane holds D[n = 8i + 4h + t][m = l32] of each 32x32 tile, i.e.
+  // 8 bytes of 32 different output rows per instruction.  The bf16 tile goes
+  // through LDS instead ([256 m][512 B], 16-byte pieces at column piece XOR
+  // the row's low 5 bits), and leaves as whole 16-byte pieces of rows, 32
+  // consecutive threads per 512-byte row.
+  __syncthreads();  // every wave is done with the LDS (adapter operands, ticket)
+  uint8_t* const s_y = &s_x[0][0];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms) {
-      const int64_t m = m0 + ms * 32 + l32;
-      if (m >= M) continue;
+      const int row = ms * 32 + l32;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t n = n0 + wave * 64 + r * 32 + 8 * i + 4 * h;
-        if (n >= N) continue;
+        const int p16 = wave * 8 + r * 4 + i;  // 16-byte piece of the row (columns 8 p16 ..)
         u32x2 o;
         o.x = pack_bf16x2(acc[r][ms][4 * i + 0], acc[r][ms][4 * i + 1]);
         o.y = pack_bf16x2(acc[r][ms][4 * i + 2], acc[r][ms][4 * i + 3]);
-        *reinterpret_cast<u32x2*>(a.y + m * N + n) = o;
+        *reinterpret_cast<u32x2*>(s_y + row * 512 + ((p16 ^ (row & 31)) << 4) + h * 8) = o;
       }
     }
+  __syncthreads();
+#pragma unroll 8
+  for (int q = 0; q < 32; ++q) {
+    const int piece = q * 256 + tid, row = piece >> 5, p16 = piece & 31;
+    const int64_t m = m0 + row, n = n0 + p16 * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(s_y + row * 512 + ((p16 ^ (row & 31)) << 4));
+    if (m < M && n < N) *reinterpret_cast<u32x4*>(a.y + m * N + n) = v;
+  }
 }
 
 }  // namespace
