@@ -446,23 +446,35 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     }
   }
 
-  // store: lane holds D[k = 8q + 4h + t][m = l32] of each 32x32 tile
+  // store: lane holds D[k = 8q + 4h + t][m = l32] of each 32x32 tile, i.e.
+  // 8 bytes of 32 different output rows per instruction.  The bf16 tile goes
+  // through LDS instead (tokens 64 s .. 64 s + 63 in the stage array s, 512 B
+  // per token, 16-byte pieces at column piece XOR the token's low 5 bits) and
+  // leaves as whole 16-byte pieces of rows, 32 consecutive threads per row.
+  __syncthreads();  // every wave is done with the LDS (adapter operands)
+  uint8_t* const s_out[4] = {s_w0, s_w1, s_dy0, s_dy1};
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t m = m0 + j * 32 + l32;
-      if (m >= M) continue;
+      const int row = j * 32 + l32;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t k = k0 + wave * 64 + i * 32 + 8 * q + 4 * h;
-        if (k >= K) continue;
+        const int p16 = wave * 8 + i * 4 + q;  // 16-byte piece of the row (columns 8 p16 ..)
         u32x2 o;
         o.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
         o.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        *reinterpret_cast<u32x2*>(a.dx + m * K + k) = o;
+        *reinterpret_cast<u32x2*>(s_out[j >> 1] + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4) + h * 8) = o;
       }
     }
+  __syncthreads();
+#pragma unroll 8
+  for (int q = 0; q < 32; ++q) {
+    const int piece = q * 256 + tid, row = piece >> 5, p16 = piece & 31;
+    const int64_t m = m0 + row, k = k0 + p16 * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(s_out[q >> 3] + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4));
+    if (m < M && k < K) *reinterpret_cast<u32x4*>(a.dx + m * K + k) = v;
+  }
 }
 
 }  // namespace
