@@ -452,7 +452,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   // per token, 16-byte pieces at column piece XOR the token's low 5 bits) and
   // leaves as whole 16-byte pieces of rows, 32 consecutive threads per row.
   __syncthreads();  // every wave is done with the LDS (adapter operands)
-  uint8_t* const s_out[4] = {s_w0, s_w1, s_dy0, s_dy1};
+  // (a select, not an array of the four addresses: such an array would be
+  // emitted as a constant table of LDS addresses, which has no encoding)
+  auto s_out = [&](int i) -> uint8_t* { return i == 0 ? s_w0 : i == 1 ? s_w1 : i == 2 ? s_dy0 : s_dy1; };
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         u32x2 o;
         o.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
         o.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        *reinterpret_cast<u32x2*>(s_out[j >> 1] + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4) + h * 8) = o;
+        *reinterpret_cast<u32x2*>(s_out(j >> 1) + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4) + h * 8) = o;
       }
     }
   __syncthreads();
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   for (int q = 0; q < 32; ++q) {
     const int piece = q * 256 + tid, row = piece >> 5, p16 = piece & 31;
     const int64_t m = m0 + row, k = k0 + p16 * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(s_out[q >> 3] + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(s_out(q >> 3) + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4));
     if (m < M && k < K) *reinterpret_cast<u32x4*>(a.dx + m * K + k) = v;
   }
 }
