@@ -29,9 +29,7 @@ constexpr int kQaMaxRank = 128;
 // the pass is in flight at once (two passes cover 8 tokens of K = 11008);
 // each thread adds its pieces' 8 elements in order and the four
 // neighbouring lanes that hold one group add their sums pairwise in lane
-// order.  u then reads each row of A once for all tokens of the block:
-// lanes run across groups and the lane sums are added with a fixed
-// butterfly (lane 0's result is stored).
+// order.  u then takes the block's P from LDS into fp32 MFMAs (below).
 constexpr int kQaThreads = 1024;
 constexpr int kQaPer = 8;  // loads per thread and pass
 __global__ __launch_bounds__(kQaThreads) void k_qa_pool_u(QaArgs a) {
@@ -43,6 +41,22 @@ __global__ __launch_bounds__(kQaThreads) void k_qa_pool_u(QaArgs a) {
   const int64_t G = a.G, K = a.K;
   const int npiece = static_cast<int>(K / 8);  // 16-byte pieces per token row (a multiple of 4)
   const int total = tok * npiece;
+  // LDS after the P block: the slices' partial u tiles, then A (staged)
+  const int jt = (a.r + 15) >> 4, nsl = 16 / jt, rp = jt * 16;
+  float* s_red = s_p + tok * G;  // [nsl][tok][rp]
+  uint16_t* s_A = reinterpret_cast<uint16_t*>(s_red + nsl * tok * rp);
+  // the first pieces of A are loaded before the pooling passes, so that
+  // their latency overlaps them (indices clamped: no branch around loads)
+  constexpr int kAPre = 4;
+  const int64_t n16 = a.stage_a ? static_cast<int64_t>(a.r) * G / 8 : 0;
+  u32x4 apre[kAPre];
+  if (n16 > 0) {
+#pragma unroll
+    for (int i = 0; i < kAPre; ++i) {
+      const int64_t idx = i * kQaThreads + tid;
+      apre[i] = reinterpret_cast<const u32x4*>(a.A)[idx < n16 ? idx : n16 - 1];
+    }
+  }
   for (int p0 = 0; p0 < total; p0 += kQaThreads * kQaPer) {
     u32x4 w[kQaPer];
     int tk[kQaPer], pc[kQaPer];
@@ -81,33 +95,90 @@ __global__ __launch_bounds__(kQaThreads) void k_qa_pool_u(QaArgs a) {
     }
   }
   if (a.u_out == nullptr) return;
-  // A itself goes to LDS after the pooled block when it fits (rows 16-byte
-  // aligned), so that the loop below reads no global memory
-  uint16_t* s_A = reinterpret_cast<uint16_t*>(s_p + tok * G);
-  if (a.stage_a) {
-    const int64_t n16 = static_cast<int64_t>(a.r) * G / 8;
-#pragma unroll 4
-    for (int64_t i = tid; i < n16; i += kQaThreads)
+  // u of the block's tokens with fp32 MFMAs (16 x 16 x 4): row i = token,
+  // column = adapter row j, reduction over the groups.  The 16 waves split
+  // into ceil(r/16) column tiles times 16 / ceil(r/16) slices of the group
+  // range; each slice's partial tile goes to LDS and the slices are added
+  // in slice order.  In step e of a 16-group block, lane quarter q takes
+  // group 16 b + 4 e + q (token rows past the block and columns past r are
+  // zero operands).  A goes to LDS first when it fits.
+  if (n16 > 0) {
+#pragma unroll
+    for (int i = 0; i < kAPre; ++i) {
+      const int64_t idx = i * kQaThreads + tid;
+      if (idx < n16) reinterpret_cast<u32x4*>(s_A)[idx] = apre[i];
+    }
+    for (int64_t i = kAPre * kQaThreads + tid; i < n16; i += kQaThreads)
       reinterpret_cast<u32x4*>(s_A)[i] = reinterpret_cast<const u32x4*>(a.A)[i];
   }
   __syncthreads();
-  for (int j = wave; j < a.r; j += kQaThreads / 64) {
-    const uint16_t* ar = a.stage_a ? s_A + static_cast<int64_t>(j) * G : a.A + static_cast<int64_t>(j) * G;
-    float acc[kQaTokMax];
+  const int sl = wave / jt, j = (wave % jt) * 16 + (lane & 15);
+  if (sl < nsl) {
+    const int t = lane & 15, q = lane >> 4;
+    const bool tv = t < tok, jv = j < a.r;
+    const float* prow = s_p + (tv ? t : 0) * G;
+    const int64_t aro = static_cast<int64_t>(jv ? j : 0) * G;
+    const int nblk = static_cast<int>((G + 15) >> 4);
+    const int b0 = sl * nblk / nsl, b1 = (sl + 1) * nblk / nsl;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = b0; b < b1; ++b) {
 #pragma unroll
-    for (int t = 0; t < kQaTokMax; ++t) acc[t] = 0.0f;
-    for (int64_t g = lane; g < G; g += 64) {
-      const float av = bf16_to_f32(ar[g]);
-#pragma unroll
-      for (int t = 0; t < kQaTokMax; ++t)
-        if (t < tok) acc[t] += s_p[t * G + g] * av;
+      for (int e = 0; e < 4; ++e) {
+        const int64_t g = b * 16 + 4 * e + q;
+        const bool gv = g < G;
+        const int64_t gc = gv ? g : G - 1;
+        const float pv = prow[gc];
+        const uint16_t ab = a.stage_a ? s_A[aro + gc] : a.A[aro + gc];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv && gv ? pv : 0.0f, jv && gv ? bf16_to_f32(ab) : 0.0f,
+                                                   acc, 0, 0, 0);
+      }
     }
+    // lane holds rows 4 q + v of column j
 #pragma unroll
-    for (int t = 0; t < kQaTokMax; ++t) {
-      if (t >= tok) break;
-      const float sum = warp_sum(acc[t]);
-      if (lane == 0 && m0 + t < a.M) a.u_out[(m0 + t) * a.r + j] = sum;
+    for (int v = 0; v < 4; ++v) {
+      const int tt = 4 * q + v;
+      if (tt < tok && jv) s_red[(sl * tok + tt) * rp + j] = acc[v];
     }
+  }
+  __syncthreads();
+  for (int i = tid; i < tok * a.r; i += kQaThreads) {
+    const int tt = i / a.r, jj = i - tt * a.r;
+    float sum = s_red[tt * rp + jj];
+    for (int k = 1; k < nsl; ++k) sum += s_red[(k * tok + tt) * rp + jj];
+    if (m0 + tt < a.M) a.u_out[(m0 + tt) * a.r + jj] = sum;
+  }
+}
+
+// P alone (the backward pass, which has u): the same sums as above, the
+// token rows taken as one flat run of 16-byte pieces (four to a group), 8
+// pieces of each thread in flight.
+constexpr int kQaPoolPer = 8;
+__global__ __launch_bounds__(256) void k_qa_pool(const uint16_t* __restrict__ x, float* __restrict__ P,
+                                                 int64_t total) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * (256 * kQaPoolPer);
+  u32x4 w[kQaPoolPer];
+#pragma unroll
+  for (int i = 0; i < kQaPoolPer; ++i) {
+    const int64_t pf = base + i * 256 + tid;
+    w[i] = *reinterpret_cast<const u32x4*>(x + (pf < total ? pf : total - 1) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < kQaPoolPer; ++i) {
+    float v = bf16_lo(w[i].x);
+    v += bf16_hi(w[i].x);
+    v += bf16_lo(w[i].y);
+    v += bf16_hi(w[i].y);
+    v += bf16_lo(w[i].z);
+    v += bf16_hi(w[i].z);
+    v += bf16_lo(w[i].w);
+    v += bf16_hi(w[i].w);
+    const float v1 = __shfl_xor(v, 1, 64);
+    const float q1 = (lane & 1) ? v1 + v : v + v1;
+    const float q2 = __shfl_xor(q1, 2, 64);
+    const float q = (lane & 2) ? q2 + q1 : q1 + q2;
+    const int64_t pf = base + i * 256 + tid;
+    if ((lane & 3) == 0 && pf < total) P[pf >> 2] = q;
   }
 }
 
@@ -215,8 +286,20 @@ int64_t qa_dA_partial_floats(int64_t M, int32_t r, int64_t G) {
 hipError_t launch_qa_pool_u(const QaArgs& in, hipStream_t stream) {
   if (in.pool != kQaPool || in.K % kQaPool != 0) return hipErrorInvalidValue;
   QaArgs a = in;
+  if (a.u_out == nullptr) {
+    if (a.P_out == nullptr) return hipErrorInvalidValue;
+    const int64_t total = a.M * a.K / 8;
+    if (total == 0) return hipSuccess;
+    const int64_t per = 256 * kQaPoolPer;
+    hipLaunchKernelGGL(k_qa_pool, dim3(static_cast<uint32_t>((total + per - 1) / per)), dim3(256), 0, stream,
+                       a.x, a.P_out, total);
+    return hipGetLastError();
+  }
+  if (a.r < 1 || a.r > kQaMaxRank) return hipErrorInvalidValue;
   a.tok = qa_tokens(a.G);
-  size_t lds = static_cast<size_t>(a.tok) * a.G * sizeof(float);
+  const int jt = (a.r + 15) / 16;
+  size_t lds = static_cast<size_t>(a.tok) * a.G * sizeof(float) +
+               static_cast<size_t>(16 / jt) * a.tok * jt * 16 * sizeof(float);
   if (lds > 65536) return hipErrorInvalidValue;
   const size_t a_bytes = static_cast<size_t>(a.r) * a.G * sizeof(uint16_t);
   a.stage_a = a.u_out != nullptr && a.G % 8 == 0 && lds + a_bytes <= 65536;
