@@ -109,12 +109,11 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   Plan p;
   const int64_t N = w->d_out, K = w->d_in, G = K / pool;
   p.small = M <= kSmallM;
-  // u and du reductions: ~512 workgroups, but never fewer than 64 k16
-  // steps per workgroup
-  // skinny products: ~512 workgroups of 64 rows, at least 4 chunks of 128
-  // columns per split
-  p.nt_splits_u = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), ceil_div(K, 128) / 4), 1, 64));
-  p.nt_splits_du = static_cast<int>(clamp64(std::min<int64_t>(512 / nt_tiles(M), ceil_div(N, 128) / 4), 1, 64));
+  // skinny products: ~256 workgroups of 64 rows (one per compute unit; at
+  // 4096 x 4096 and 4096 x 11008 twice as many ran 7-14 % slower, half as
+  // many 28-50 % slower), at least 4 chunks of 128 columns per split
+  p.nt_splits_u = static_cast<int>(clamp64(std::min<int64_t>(256 / nt_tiles(M), ceil_div(K, 128) / 4), 1, 64));
+  p.nt_splits_du = static_cast<int>(clamp64(std::min<int64_t>(256 / nt_tiles(M), ceil_div(N, 128) / 4), 1, 64));
   // token-share splits of the adapter-gradient reductions: ~320 workgroups,
   // at least 256 tokens per share
   const int64_t max_shares = std::max<int64_t>(1, M / 256);
