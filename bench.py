@@ -2,16 +2,26 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--m M]
 
-A step is one forward (qlin_fwd) plus one backward (qlin_bwd: dX, dA, dB) of
-one layer over one batch of synthetic tokens, with inputs resident in HBM.
-The frozen weight is quantized once before timing, as in training.  For the
-weight-streaming (few-token) workloads the step cycles through enough
-distinct packed-weight copies (> 2x the 256 MB Infinity Cache) that every
-step streams its weight from HBM, as a real multi-layer model does.
+A step is one forward (qlin_fwd: y and u) plus one backward (qlin_bwd: dX,
+dA, dB) of one layer over one batch of synthetic tokens, with every input
+resident in HBM.  The frozen weight is quantized once before timing, as in
+training.  The default workload is the LLaMA-2-70B MLP down_proj at its real
+shape (W 8192 x 28672 NF4 + double quantization, LoRA r = 64, 4096 tokens),
+the largest single-GPU configuration; ``value`` is then TFLOP/s of the whole
+step (fwd 2MNK + 2MKr + 2MNr, bwd 2MNK + 4MNr + 4MKr; dequantization counts
+as zero).  Few-token workloads (M <= 16) are HBM-bound: their steps cycle
+through enough distinct packed-weight copies (> 2x the 256 MB Infinity
+Cache) that every step streams its weight from HBM, and ``value`` is the
+weight-stream rate (2 x packed-weight bytes per step / step time).
 
-Prints one JSON line.  ``value`` is the weight-stream rate (packed-weight
-bytes read per step, forward + backward, / step time) for HBM-bound
-workloads and TFLOP/s for MFMA-bound ones.
+``roofline`` describes the step's dominant kernel as the step launches it:
+its average device duration over the timed steps, measured with HIP events
+on the launch stream (for large M: events recorded by the library around
+that kernel's launch inside every timed step; for few tokens, where each
+call is a single launch, a replayed graph of the same call), against its
+algorithmic flops (MFMA-bound) or bytes (HBM-bound) per launch.
+
+Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -35,15 +45,13 @@ MALL_BYTES = 256 << 20
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="q_proj")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="down_proj70b")
     p.add_argument("--m", type=int, default=None, help="token count override")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--kernel-iters", type=int, default=200)
-    p.add_argument("--eager", action="store_true",
-                   help="launch kernels directly instead of replaying a HIP graph "
-                        "(for counter collection, which profiles eager dispatches)")
+    p.add_argument("--kernel-iters", type=int, default=200,
+                   help="few-token workloads: graph-replayed launches for the kernel timing")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="before timing, copy a buffer of this many MiB once: a plain copy "
                         "kernel of known size that scales the HBM byte counters")
@@ -52,17 +60,18 @@ def parse():
 
 # Kernel sources whose HBM byte counts a committed traffic record refers to.
 TRAFFIC_SOURCES = {
-    "k_gemv_fwd": ("quantized_base_rank_amd/csrc/gemv_fwd.hip",
-                   "quantized_base_rank_amd/csrc/device_common.hpp"),
-    "k_fwd_gemm": ("quantized_base_rank_amd/csrc/fwd_gemm.hip",
-                   "quantized_base_rank_amd/csrc/device_common.hpp"),
+    "k_gemv_fwd": ("quantized_base_rank_amd/csrc/gemv_fwd.hip",),
+    "k_gemv_dx": ("quantized_base_rank_amd/csrc/gemv_dx.hip",),
+    "k_fwd_gemm": ("quantized_base_rank_amd/csrc/fwd_gemm.hip",),
+    "k_dx_gemm": ("quantized_base_rank_amd/csrc/dx_gemm.hip",),
 }
+COMMON_SOURCES = ("quantized_base_rank_amd/csrc/device_common.hpp",)
 
 
 def source_digest(kernel):
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES[kernel]:
+    for rel in TRAFFIC_SOURCES[kernel] + COMMON_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -76,12 +85,29 @@ def recorded_traffic(kernel, workload):
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     try:
         with open(path) as f:
-            rec = json.load(f)
+            text = f.read()
+        rec = json.loads(text[text.index("{"):text.rindex("}") + 1])
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != source_digest(kernel):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def kernel_work(wl, kernel):
+    """Algorithmic work of one launch of `kernel` in a step of `wl`:
+    (amount, 'flop' | 'byte')."""
+    M, N, K, r, Ka = wl.M, wl.d_out, wl.d_in, wl.r, wl.k_a
+    wbytes = wl.packed_weight_bytes()
+    if kernel == "k_fwd_gemm":        # x W^T plus the appended adapter term
+        return 2 * M * N * K + 2 * M * N * r, "flop"
+    if kernel == "k_dx_gemm":         # dY W plus the appended du A term
+        return 2 * M * N * K + 2 * M * Ka * r, "flop"
+    if kernel == "k_gemv_fwd":        # W, x, A (fused u), B, y, u
+        return wbytes + 2 * M * K + 2 * r * Ka + 2 * N * r + 2 * M * N + 4 * M * r, "byte"
+    if kernel == "k_gemv_dx":         # W, dY, x, dX, A, B, u, dA, dB
+        return (wbytes + 2 * M * N + 4 * M * K + 4 * r * Ka + 4 * N * r + 4 * M * r), "byte"
+    raise KeyError(kernel)
 
 
 def main():
@@ -145,85 +171,116 @@ def main():
     dA = torch.empty((r, wl.k_a), dtype=torch.bfloat16, device=dev)
     dB = torch.empty((wl.d_out, r), dtype=torch.bfloat16, device=dev)
 
+    def fwd(i):
+        qb.qlin_fwd(weights[i % n_copies], x, A, B, r, s, pool, y=y, u_out=u, ws=ws)
+
+    def bwd(i):
+        qb.qlin_bwd(weights[i % n_copies], x, A, B, r, s, dy, pool, u_saved=u, dx=dx, dA=dA,
+                    dB=dB, ws=ws)
+
     def step(i):
-        w = weights[i % n_copies]
-        qb.qlin_fwd(w, x, A, B, r, s, pool, y=y, u_out=u, ws=ws)
-        qb.qlin_bwd(w, x, A, B, r, s, dy, pool, u_saved=u, dx=dx, dA=dA, dB=dB, ws=ws)
+        fwd(i)
+        bwd(i)
 
-    def fwd_only(i):
-        qb.qlin_fwd(weights[i % n_copies], x, A, B, r, 0.0, pool, y=y, u_out=None, ws=ws,
-                    want_u=False)
-
-    class Eager:
-        def __init__(self, fn, n, offset):
-            self.fn, self.n, self.offset = fn, n, offset
-
-        def replay(self):
-            for i in range(self.n):
-                self.fn(self.offset + i)
+    def new_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()   # creates the device event, so its handle can be passed on
+        return e
 
     def capture(fn, n, offset=0):
         """One HIP graph holding exactly n calls of fn (host launch cost is
         paid once at capture, not in the timed region)."""
-        if args.eager:
-            return Eager(fn, n, offset)
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
             fn(offset)  # eager warm call outside the capture
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
             for i in range(n):
                 fn(offset + i)
-        return g
+        return gr
 
-    def timed(g):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def timed_graph(gr):
+        e0, e1 = new_event(), new_event()
         torch.cuda.synchronize()
         e0.record()
-        g.replay()
+        gr.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
-    if args.warmup > 0:
-        gw = capture(step, args.warmup)
-        gw.replay()
+    kernel_ms = {}
+    if hbm_bound:
+        # few tokens: each step is a few microseconds, so steps replay from a
+        # captured graph; qlin_fwd and qlin_bwd are one launch each here
+        # (k_gemv_fwd, k_gemv_dx), so a graph of either call alone times that
+        # kernel exactly as the step launches it
+        if args.warmup > 0:
+            gw = capture(step, args.warmup)
+            gw.replay()
+            torch.cuda.synchronize()
+        gt = capture(step, args.steps, offset=args.warmup)
+        ms_per_step = timed_graph(gt) / args.steps
+        for name, fn in (("k_gemv_fwd", fwd), ("k_gemv_dx", bwd)):
+            gk = capture(fn, args.kernel_iters)
+            gk.replay()
+            kernel_ms[name] = timed_graph(gk) / args.kernel_iters
+        dominant = max(kernel_ms, key=kernel_ms.get)
+        k_ms = kernel_ms[dominant]
+        timing = "graph replay"
+    else:
+        # large M: milliseconds per step, launched directly.  In warm-up the
+        # candidates are timed once each; in every timed step the library
+        # records events around the dominant kernel's launch.
+        candidates = ("k_fwd_gemm", "k_dx_gemm")
+        for i in range(max(args.warmup, len(candidates))):
+            if i < len(candidates):
+                ev = (new_event(), new_event())
+                qb.qlin_profile_next_launch(candidates[i], *ev)
+                step(i)
+                torch.cuda.synchronize()
+                kernel_ms[candidates[i]] = ev[0].elapsed_time(ev[1])
+            else:
+                step(i)
         torch.cuda.synchronize()
-    gt = capture(step, args.steps, offset=args.warmup)
-    ms_per_step = timed(gt) / args.steps
+        dominant = max(kernel_ms, key=kernel_ms.get)
+        evs = [(new_event(), new_event()) for _ in range(args.steps)]
+        e0, e1 = new_event(), new_event()
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(args.steps):
+            qb.qlin_profile_next_launch(dominant, *evs[i])
+            step(args.warmup + i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_per_step = e0.elapsed_time(e1) / args.steps
+        k_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        timing = "launched directly; kernel bracketed by events inside each timed step"
 
     flops = wl.flops_fwd() + wl.flops_bwd()
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     weight_gbs = 2 * wbytes / (ms_per_step * 1e-3) / 1e9
 
-    # dominant kernel timed alone on the stream it runs on: the forward with the
-    # adapter off and no u is exactly one launch of the weight-streaming (few
-    # tokens) or the MFMA kernel.
-    kit = args.kernel_iters
-    gk = capture(fwd_only, kit)
-    gk.replay()
-    k_ms = timed(gk) / kit
-    if hbm_bound:
-        k_bytes = wbytes + wl.M * wl.d_in * 2 + wl.M * wl.d_out * 2
-        achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    work, kind = kernel_work(wl, dominant)
+    if kind == "byte":
+        achieved = work / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic("k_gemv_fwd", args.workload),
-                "kernel": "k_gemv_fwd", "bytes_per_launch": k_bytes,
-                "avg_launch_us": round(k_ms * 1e3, 3)}
+                "traffic": recorded_traffic(dominant, args.workload),
+                "kernel": dominant, "bytes_per_launch": work}
         value, unit = weight_gbs, "GB/s"
     else:
-        k_flops = 2 * wl.M * wl.d_out * wl.d_in
-        achieved = k_flops / (k_ms * 1e-3) / 1e12
+        achieved = work / (k_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": recorded_traffic("k_fwd_gemm", args.workload),
-                "kernel": "k_fwd_gemm", "flops_per_launch": k_flops,
-                "avg_launch_us": round(k_ms * 1e3, 3)}
+                "traffic": recorded_traffic(dominant, args.workload),
+                "kernel": dominant, "flops_per_launch": work}
         value, unit = tflops, "TFLOP/s"
+    roof["avg_launch_us"] = round(k_ms * 1e3, 3)
+    roof["timing"] = timing
+    roof["candidates_us"] = {k: round(v * 1e3, 3) for k, v in kernel_ms.items()}
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
@@ -234,6 +291,7 @@ def main():
                    "s": wl.s, "format": wl.fmt, "block": wl.block, "dq_block": wl.dq_block,
                    "pool": wl.pool, "weight_copies": n_copies},
         "tflops": round(tflops, 3), "weight_gbs": round(weight_gbs, 1),
+        "frac_of_bf16_peak_step": round(tflops / BF16_PEAK_TFLOPS, 4),
         "packed_weight_bytes": wbytes, "flops_per_step": flops,
         "roofline": roof, "setup_s": round(setup_s, 2),
     }
@@ -244,8 +302,6 @@ def main():
 
 def cpu_baseline(wl, inp, hbm_bound, wbytes, flops):
     """The CPU oracle (float64 numpy) on a bounded sample of the same layer."""
-    import numpy as np
-
     from oracle import qlin_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -253,8 +309,8 @@ def cpu_baseline(wl, inp, hbm_bound, wbytes, flops):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     # sample: the whole layer when it is small; otherwise the first rows of W
-    # and a proportional share of the work
-    rows = wl.d_out if wl.d_out * wl.d_in <= (1 << 24) else max(256, (1 << 24) // wl.d_in)
+    # (whole double-quantization groups) and a proportional share of the work
+    rows = wl.d_out if wl.d_out * wl.d_in <= (1 << 24) else max(256, (1 << 24) // wl.d_in // 4 * 4)
     M = min(wl.M, 256)
     W = inp.W[:rows]
     t0 = time.time()

@@ -87,9 +87,10 @@ typedef enum {
  *         with c the 16 NF4 levels (qlin_nf4_codebook).
  *   dq_block = 0:   absmax = float[n_blocks], a_hat_b = absmax[b].
  *   dq_block = 256: absmax = int8[n_blocks] (values 0..127), absmax2 =
- *         float[ceil(n_blocks/256)] and
- *             step_g  = fl32( absmax2[g] * fl32(1/127) ),  g = b/256,
- *             a_hat_b = fl32( absmax[b] * step_g ).
+ *         float[ceil(n_blocks/256)] and, with g = b/256,
+ *             a_hat_b = RN32( absmax[b] * absmax2[g] / 127 ),
+ *         the exact quotient rounded once to fp32 (ties to even), so a code
+ *         of 127 reconstructs absmax2[g] itself.
  *         [QLoRA "Innovation 2: Double Quantization"]
  * INT4 (block = group = 32): scale, zero = fp16[d_out][d_in/32]; element
  *         (n, k) with q = its index decodes to
@@ -101,7 +102,7 @@ typedef struct {
   int32_t block;           /* NF4: 64; INT4: group size, 32                  */
   int32_t dq_block;        /* NF4: 256 or 0; INT4: 0                         */
   int32_t reserved;        /* must be 0                                      */
-  int64_t d_out, d_in;     /* d_in % block == 0                              */
+  int64_t d_out, d_in;     /* d_out % 16 == 0; d_in % 64 == 0 (both formats) */
   const uint8_t *codes;    /* uint8[d_out][d_in/2]                           */
   const void *absmax;      /* NF4: int8[n_blocks] (dq) or float[n_blocks]    */
   const float *absmax2;    /* NF4 with dq: float[ceil(n_blocks/dq_block)]    */
@@ -126,7 +127,8 @@ int qlin_nf4_codebook(float out[16]);
  * "Innovation 2: Double Quantization", "The same idea in code"]
  *
  *   W        fp32[d_out][d_in] (device, read only)
- *   block    must be 64;  d_in % 64 == 0;  d_out >= 1
+ *   block    must be 64;  d_in % 64 == 0;  d_out % 16 == 0 (the shapes
+ *            qlin_fwd / qlin_bwd accept)
  *   dq_block 256 (absmax int8[n_blocks], absmax2 float[ceil(n_blocks/256)])
  *            or 0 (absmax float[n_blocks]; absmax2 may be NULL)
  *   codes    uint8[d_out][d_in/2]  (output)
@@ -136,7 +138,10 @@ int qlin_nf4_codebook(float out[16]);
  * index 7 with absmax 0).  With dq_block = 256 each absmax becomes
  * round_half_even(127 * absmax_b / absmax2_g) and absmax2_g is the group's
  * fp32 maximum.  Synchronises `stream`; returns QLIN_E_NONFINITE if W holds
- * NaN or Inf (outputs are then unspecified).
+ * NaN or Inf (outputs are then unspecified).  Non-finite input is detected
+ * on the GPU and reported through one flag word per device that the
+ * library owns; quantizer calls of one process therefore run one at a time
+ * (a host mutex), and only the flag word crosses back to the host.
  */
 int qlin_quantize_nf4(const float *W, int64_t d_out, int64_t d_in, int32_t block,
                       int32_t dq_block, uint8_t *codes, void *absmax, float *absmax2,
@@ -145,12 +150,15 @@ int qlin_quantize_nf4(const float *W, int64_t d_out, int64_t d_in, int32_t block
 /*
  * Group-wise asymmetric INT4 quantization.  [QA-LoRA abstract]
  *
- *   W      fp32[d_out][d_in] (device); group must be 32; d_in % 32 == 0
+ *   W      fp32[d_out][d_in] (device); group must be 32; d_in % 64 == 0 and
+ *          d_out % 16 == 0 (the shapes qlin_fwd / qlin_bwd accept)
  *   codes  uint8[d_out][d_in/2]; scale, zero fp16[d_out][d_in/32] (outputs)
  *
- * Per (row, group): zero = fp16(min), scale = fp16(fl32(fl32(max-min)/15)),
- * q = 0 if scale == 0 else clamp(round_half_even(fl32(fl32(w-zero)/scale)), 0, 15).
- * Synchronises `stream`; QLIN_E_NONFINITE if W holds NaN/Inf or |w| > 65504.
+ * Per (row, group), with every rounding taken on the exact real value:
+ *   zero  = RN16(min),   scale = RN16((max - min) / 15),
+ *   q     = clamp(round_half_even((w - zero) / scale), 0, 15), 0 if scale == 0.
+ * Synchronises `stream`; QLIN_E_NONFINITE if W holds NaN/Inf or |w| > 65504
+ * (reported as for qlin_quantize_nf4, through the device flag word).
  */
 int qlin_quantize_int4_group(const float *W, int64_t d_out, int64_t d_in, int32_t group,
                              uint8_t *codes, uint16_t *scale, uint16_t *zero,
@@ -158,11 +166,15 @@ int qlin_quantize_int4_group(const float *W, int64_t d_out, int64_t d_in, int32_
 
 /*
  * Bytes of device workspace qlin_fwd / qlin_bwd need for this weight, token
- * count M, adapter rank r and pool.  The workspace must be zero-filled once
- * before its first use with the library; every completed call leaves its
- * synchronisation counters at zero again, so it can be reused as is.  Two
- * calls in flight at the same time must not share a workspace.  Returns 0
- * for invalid arguments.  Host only; needs no GPU.
+ * count M, adapter rank r and pool.  The first 64 KiB of every workspace hold
+ * the ticket counters of the split reductions; the workspace must be
+ * zero-filled once before its first use with the library.  Every completed
+ * call leaves the counters at zero and no call writes anything else into
+ * those 64 KiB, so one workspace can be reused by later calls of any shape
+ * (given enough bytes).  Two calls in flight at the same time must not share
+ * a workspace.  Returns 0 for invalid arguments, and for shapes whose split
+ * reductions would need more than 16384 counters (d_in > 2 097 152 or d_out
+ * > 262 144 at M <= 16).  Host only; needs no GPU.
  */
 size_t qlin_workspace_bytes(const qlin_qweight *w, int64_t M, int32_t r, int32_t pool);
 
@@ -170,9 +182,11 @@ size_t qlin_workspace_bytes(const qlin_qweight *w, int64_t M, int32_t r, int32_t
  * Forward pass of the adapted layer.  [QLoRA "Background: how LoRA works",
  * "The QLoRA recipe" stage 3, "The same idea in code"; QA-LoRA abstract]
  *
- *   w      packed weight (see qlin_qweight)
+ *   w      packed weight (see qlin_qweight: d_out % 16 == 0, d_in % 64 == 0)
  *   x      bf16[M][d_in];  1 <= M
- *   A      bf16[r][d_in/pool];  B bf16[d_out][r];  1 <= r <= 128
+ *   A      bf16[r][d_in/pool];  B bf16[d_out][r];  0 <= r <= 128; r = 0 is
+ *          the layer without an adapter (A, B may be NULL, u_out must be
+ *          NULL), e.g. an INT4 weight whose adapter qlin_qa_merge folded in
  *   s      adapter scale (any finite float; 0 disables the adapter term)
  *   pool   1 for a plain adapter, or the INT4 group size (32) for the
  *          QA-LoRA pooled adapter, whose input is the sum of each group of
@@ -207,11 +221,45 @@ int qlin_bwd(const qlin_qweight *w, const uint16_t *x, int64_t M, const uint16_t
              size_t ws_bytes, hipStream_t stream);
 
 /*
+ * QA-LoRA merge: folds a trained pooled adapter into the INT4 zero points,
+ * so that the quantized layer alone computes the adapted layer.  [QA-LoRA
+ * abstract, point (ii)]  With the adapter acting on the sum of each group of
+ * 32 inputs, s (P A^T) B^T adds s (B A)[n][g] to every weight of group g in
+ * row n, i.e. shifts that group's additive zero point:
+ *     zero_out[n][g] = RN16( zero[n][g] + s * sum_j B[n][j] A[j][g] ),
+ * the exact sum rounded once to fp16 (ties to even; exact whenever the
+ * terms span fewer than ~99 bits).  Then qlin_fwd(merged weight, r = 0)
+ * equals qlin_fwd(original, adapter, pool = 32) up to that fp16 rounding.
+ *
+ *   w         INT4 weight (QLIN_FMT_INT4_GROUP, group 32); its zero is read
+ *   A         bf16[r][d_in/32];  B bf16[d_out][r];  1 <= r <= 128; s finite
+ *   zero_out  fp16[d_out][d_in/32] (output; may be w->zero itself)
+ * Asynchronous on `stream`.
+ */
+int qlin_qa_merge(const qlin_qweight *w, const uint16_t *A, const uint16_t *B, int32_t r,
+                  float s, uint16_t *zero_out, hipStream_t stream);
+
+/*
  * Test helper: writes the dequantized weight W_bf16 (bf16[d_out][d_in]) using
  * the same in-register lookup-table decode as the fused kernels.  Never
  * called by qlin_fwd / qlin_bwd, which do not materialise W.  Asynchronous.
  */
 int qlin_dequant_bf16(const qlin_qweight *w, uint16_t *W_out, hipStream_t stream);
+
+/*
+ * Profiling aid; takes no part in the computation.  Arms a one-shot hook:
+ * the next launch of the kernel named `kernel` made by any qlin_* call of
+ * this process records `start` on that call's stream just before the launch
+ * and `stop` just after it, and the hook disarms itself.  Kernel names:
+ * "k_gemv_fwd", "k_fwd_gemm" (forward products), "k_gemv_dx", "k_dx_gemm"
+ * (input gradient), "k_nt_skinny", "k_tn2", "k_split_hl", "k_transpose16",
+ * "k_qa_pool_u", "k_qa_dA" (adapter products).  `start` and `stop` are HIP
+ * events created by the caller; the elapsed time between them is the
+ * kernel's duration on the device.  kernel = NULL disarms.  One hook per
+ * process (a later call replaces an armed one).  Host only; QLIN_E_NULL for
+ * a missing event, QLIN_E_SHAPE for a name of 64 or more characters.
+ */
+int qlin_profile_next_launch(const char *kernel, hipEvent_t start, hipEvent_t stop);
 
 /* Static, human-readable name of a status code (host only). */
 const char *qlin_status_string(int status);

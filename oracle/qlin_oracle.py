@@ -35,12 +35,24 @@ Parity status per function
                              tie rule on a dyadic codebook, DQ accounting)
 * dequant_nf4_bf16 ........ pinned (bf16 rounding vs torch, c_i*2^e blocks,
                              reconstruction error bound)
-* quantize_int4_group ..... pinned (range/bounds, min->0, max->15, error
-                             bound, Gaussian error level)
+* dq_absmax ............... pinned (exact rational RN32(q s2 / 127) on
+                             random and edge codes; q = 127 gives s2)
+* quantize_int4_group ..... pinned (codes against the exact nearest integer
+                             in rationals, constructed exact ties and
+                             one-ulp near-ties, scale against the exact
+                             rational RN16, bounds, min->0, max->15,
+                             Gaussian error level)
 * dequant_int4_bf16 ....... pinned (error bound vs the input)
 * lora_forward / backward . pinned (finite differences, B=0 / W=0 / s=0
                              reductions to plain products, M=1)
+* nf_codebook / quantize_nf / dequant_nf_bf16 (NormalFloat-k, k = 2, 3, 4,
+  blocks 32..256) ........ pinned (k = 4 reproduces NF4; quantile spacing
+                             via the forward CDF; independent inverse CDFs;
+                             bin occupancy; exact argmin; special cases;
+                             bit-plane packing by hand; storage accounting)
 * qa_merge_zero ........... pinned (merged == unmerged forward)
+* qa_merge_zero_f16 ....... pinned (exact rational RN16 of beta + s B A,
+                             fp16 boundary ties, merged forward error)
 * The absolute values of the NF4 levels beyond the stated construction are
   "parity unpinned": the pages print no table of levels.
 """
@@ -202,19 +214,31 @@ def double_quantize(absmax: np.ndarray, dq_block: int = 256):
     return q.astype(np.int8), s2
 
 
-#: fp32 constant multiplying a group's s2 to give the 8-bit grid step.  [R5]
-DQ_INV127 = F32(1.0 / 127.0)
-
-
 def dq_absmax(q: np.ndarray, s2: np.ndarray, dq_block: int = 256) -> np.ndarray:
     """fp32 first-level constants reconstructed from their 8-bit codes.  [R5]
 
-    step_g = fl32(s2_g * fl32(1/127)); a_hat_b = fl32(q_b * step_g)."""
-    q = np.asarray(q, dtype=np.int8).astype(F32)
-    s2 = np.asarray(s2, dtype=F32)
-    step = (s2 * DQ_INV127).astype(F32)
-    step_b = np.repeat(step, dq_block)[: q.size]
-    return (q * step_b).astype(F32)
+    The 8-bit grid of a group runs from 0 to its maximum s2 in 127 equal
+    steps, so code q stands for the real number q * s2 / 127.  The stored
+    constant is that number rounded once to fp32 (ties to even):
+    a_hat = RN32(q * s2 / 127).  Here q * s2 is exact in float64 (7 + 24
+    significant bits) and the float64 quotient is rounded again to fp32;
+    the quotient either is an fp32 number or lies at least 1/254 of an fp32
+    ulp away from every fp32 rounding boundary, far more than the float64
+    rounding error, so the two roundings give the single exact one.  For
+    q = 127 this returns s2 itself."""
+    q = np.asarray(q, dtype=np.int8).astype(F64)
+    s2 = np.asarray(s2, dtype=F32).astype(F64)
+    s2_b = np.repeat(s2, dq_block)[: q.size]
+    return ((q * s2_b) / 127.0).astype(F32)
+
+
+def _dq_absmax_of_blocks(absmax, absmax2, bids, dq_block: int) -> np.ndarray:
+    """dq_absmax for the flat block indices ``bids`` only (same rule)."""
+    if not dq_block:
+        return np.asarray(absmax, F32)[bids]
+    q = np.asarray(absmax, np.int8)[bids].astype(F64)
+    s2 = np.asarray(absmax2, F32)[bids // dq_block].astype(F64)
+    return ((q * s2) / 127.0).astype(F32)
 
 
 def quantize_nf4(W, block: int = 64, dq_block: int = 256, codebook=None):
@@ -281,12 +305,7 @@ def dequant_nf4_rows(codes, absmax, absmax2, rows, block=64, dq_block=256):
     nbr = k // block
     idx = unpack_nibbles(codes[rows])
     bids = (rows[:, None] * nbr + np.arange(nbr)[None, :]).reshape(-1)
-    if dq_block:
-        g = bids // dq_block
-        step = (np.asarray(absmax2, F32)[g] * DQ_INV127).astype(F32)
-        sc = (np.asarray(absmax, np.int8)[bids].astype(F32) * step).astype(F32)
-    else:
-        sc = np.asarray(absmax, F32)[bids]
+    sc = _dq_absmax_of_blocks(absmax, absmax2, bids, dq_block)
     sc = np.repeat(sc.reshape(len(rows), nbr), block, axis=1)
     return bf16_bits_to_f64(f32_to_bf16_bits((c[idx] * sc).astype(F32)))
 
@@ -301,12 +320,118 @@ def dequant_nf4_cols(codes, absmax, absmax2, cols, block=64, dq_block=256):
     byte = codes[:, (cols // 8) * 4 + cols % 4]
     nib = np.where((cols % 8)[None, :] < 4, byte & 0x0F, byte >> 4)
     bids = np.arange(n)[:, None] * nbr + (cols // block)[None, :]
-    if dq_block:
-        step = (np.asarray(absmax2, F32)[bids // dq_block] * DQ_INV127).astype(F32)
-        sc = (np.asarray(absmax, np.int8)[bids].astype(F32) * step).astype(F32)
-    else:
-        sc = np.asarray(absmax, F32)[bids]
+    sc = _dq_absmax_of_blocks(absmax, absmax2, bids, dq_block)
     return bf16_bits_to_f64(f32_to_bf16_bits((c[nib] * sc).astype(F32)))
+
+
+# ---------------------------------------------------------------------------
+# NormalFloat-k with any block size  [LQ-LoRA abstract: per-matrix bit-width
+# and block size; QLoRA "Innovation 1: 4-bit NormalFloat (NF4)" for the
+# construction]
+# ---------------------------------------------------------------------------
+
+
+def nf_levels_f64(bits: int, inv_cdf=None) -> list[float]:
+    """The 2^bits NormalFloat levels in float64, before rounding to fp32.
+
+    The NF4 construction [R1] with 2^bits levels [R22]: with
+    delta = 1 - 1/2^(bits+1) (the sketch's outermost quantile
+    (2^bits - 1/2)/2^bits) and t = Phi^-1(delta), the positive levels are
+    Phi^-1(1/2 + j (delta - 1/2)/P)/t for j = 1..P and the negative levels
+    -Phi^-1(1/2 + j (delta - 1/2)/Q)/t for j = 1..Q, with P = 2^(bits-1)
+    above and Q = 2^(bits-1) - 1 below an exact zero."""
+    if inv_cdf is None:
+        inv_cdf = NormalDist().inv_cdf
+    delta = 1.0 - 1.0 / 2 ** (bits + 1)
+    P, Q = 2 ** (bits - 1), 2 ** (bits - 1) - 1
+    t = inv_cdf(delta)
+    half = delta - 0.5
+    pos = [inv_cdf(0.5 + j * half / P) / t for j in range(1, P + 1)]
+    neg = [-inv_cdf(0.5 + j * half / Q) / t for j in range(1, Q + 1)]
+    return sorted(neg + [0.0] + pos)
+
+
+def nf_codebook(bits: int, inv_cdf=None) -> np.ndarray:
+    """fp32[2^bits] NormalFloat levels, ascending; c[0] = -1, c[-1] = +1 and
+    c[2^(bits-1) - 1] = 0."""
+    return np.array(nf_levels_f64(bits, inv_cdf), dtype=F32)
+
+
+def pack_bitplanes(idx: np.ndarray, bits: int) -> np.ndarray:
+    """k-bit indices packed as bit planes along each row [R23]: every run of
+    32 elements fills `bits` little-endian 32-bit words, word p holding bit p
+    of element i in its bit i.  Rows hold a multiple of 32 elements; the
+    result is uint8[rows][d_in * bits / 8]."""
+    idx = np.asarray(idx, dtype=np.uint32)
+    n = idx.shape[-1]
+    assert n % 32 == 0, "rows must hold a multiple of 32 elements"
+    runs = idx.reshape(idx.shape[:-1] + (n // 32, 32))
+    shifts = np.arange(32, dtype=np.uint32)
+    words = np.stack([(((runs >> p) & 1) << shifts).sum(axis=-1, dtype=np.uint64).astype(np.uint32)
+                      for p in range(bits)], axis=-1)
+    return words.reshape(idx.shape[:-1] + (n // 32 * bits,)).view(np.uint8)
+
+
+def unpack_bitplanes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_bitplanes."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    words = codes.view(np.uint32)
+    nw = words.shape[-1]
+    w = words.reshape(words.shape[:-1] + (nw // bits, bits))
+    shifts = np.arange(32, dtype=np.uint32)
+    out = np.zeros(w.shape[:-1] + (32,), dtype=np.uint32)
+    for p in range(bits):
+        out |= ((w[..., p:p + 1] >> shifts) & 1) << p
+    return out.reshape(words.shape[:-1] + (nw // bits * 32,)).astype(np.uint8)
+
+
+def quantize_nf(W, bits: int, block: int, dq_block: int = 256, codebook=None):
+    """NormalFloat-k blockwise quantization of an fp32 W[d_out][d_in].
+
+    As quantize_nf4 (nearest level of w / absmax with an exact comparison,
+    ties to the lower index, an all-zero block to the zero level, double
+    quantization of the fp32 constants in groups of ``dq_block``), with
+    2^bits levels and blocks of ``block`` consecutive elements of a row, and
+    the codes packed as bit planes [R22, R23].  Returns
+    ``(codes uint8[d_out][d_in*bits/8], absmax, absmax2)`` as for
+    quantize_nf4."""
+    W = np.asarray(W, dtype=F32)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D [d_out][d_in]")
+    n, k = W.shape
+    if k % block or k % 32:
+        raise ValueError("d_in must be a multiple of the block size and of 32")
+    if not np.all(np.isfinite(W)):
+        raise ValueError("W holds a non-finite value")
+    c = nf_codebook(bits) if codebook is None else np.asarray(codebook, dtype=F32)
+    blocks = W.reshape(-1, block)
+    a = np.abs(blocks).max(axis=1).astype(F32)
+    idx = nearest_level_index(blocks, a, c).reshape(n, k)
+    zero_idx = 2 ** (bits - 1) - 1
+    idx.reshape(-1, block)[a == 0.0] = zero_idx
+    codes = pack_bitplanes(idx, bits)
+    if dq_block:
+        q, s2 = double_quantize(a, dq_block)
+        return codes, q, s2
+    return codes, a, None
+
+
+def dequant_nf_bf16(codes, absmax, absmax2, bits: int, block: int, dq_block: int = 256,
+                    codebook=None) -> np.ndarray:
+    """W_bf16 bit patterns: bf16(fl32(c[idx] * a_hat)) for NormalFloat-k."""
+    c = nf_codebook(bits) if codebook is None else np.asarray(codebook, dtype=F32)
+    idx = unpack_bitplanes(codes, bits)
+    n, k = idx.shape
+    scale = nf4_block_scales(absmax, absmax2, dq_block)
+    scale_e = np.repeat(scale, block).reshape(n, k)
+    return f32_to_bf16_bits((c[idx].astype(F32) * scale_e).astype(F32))
+
+
+def nf_packed_nbytes(d_out: int, d_in: int, bits: int, block: int, dq_block: int = 256) -> int:
+    n_el = d_out * d_in
+    nb = n_el // block
+    consts = nb + 4 * (-(-nb // dq_block)) if dq_block else 4 * nb
+    return n_el * bits // 8 + consts
 
 
 # ---------------------------------------------------------------------------
@@ -314,15 +439,84 @@ def dequant_nf4_cols(codes, absmax, absmax2, cols, block=64, dq_block=256):
 # ---------------------------------------------------------------------------
 
 
+def nearest_f16_of_rational(x) -> np.float16:
+    """The fp16 value nearest to the rational ``x`` (a ``Fraction``), ties to
+    the even significand.  ``float(x)`` rounds once to float64; its fp16
+    image is within one fp16 step of the answer, so the nearest of that value
+    and its two fp16 neighbours, compared in exact rationals, is the answer.
+    Finite results only."""
+    from fractions import Fraction
+    h = np.float16(float(x))
+    cands = [np.nextafter(h, np.float16(-np.inf)), h, np.nextafter(h, np.float16(np.inf))]
+    best = None
+    for c in cands:
+        if not np.isfinite(c):
+            continue
+        d = abs(Fraction(float(c)) - x)
+        even = (int(np.array(c).view(np.uint16)) & 1) == 0
+        key = (d, not even)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float16(best[1])
+
+
+def int4_group_scale(lo, hi) -> np.ndarray:
+    """fp16 bits of the group scale alpha = RN16((max - min) / 15).  [R16]
+
+    The difference of two fp32 values is computed in float64 together with
+    its rounding error (the two-sum error term).  Where the difference is
+    exact, the float64 quotient by 15 rounded to fp16 is the exactly rounded
+    value: the quotient is either an fp16 rounding boundary itself or lies
+    further from every boundary than one float64 rounding can move it.
+    Where the difference is not exact (operands of very different
+    magnitudes), the rational value is rounded directly."""
+    from fractions import Fraction
+    lo = np.asarray(lo, dtype=F32).astype(F64)
+    hi = np.asarray(hi, dtype=F32).astype(F64)
+    d = hi - lo
+    bv = d - hi
+    err = (hi - (d - bv)) + (-lo - bv)          # hi - lo == d + err exactly
+    out = (d / 15.0).astype(np.float16)
+    for i in zip(*np.nonzero(err != 0.0)):
+        exact = (Fraction(float(hi[i])) - Fraction(float(lo[i]))) / 15
+        out[i] = nearest_f16_of_rational(exact)
+    return out.view(np.uint16)
+
+
+def int4_codes(w, alpha, beta) -> np.ndarray:
+    """Codes q = clamp(round_half_even((w - beta) / alpha), 0, 15), and q = 0
+    where alpha = 0.  [R16]
+
+    ``w`` is fp32, ``alpha`` and ``beta`` fp16 values broadcast against it.
+    The rounding is decided exactly: q counts the boundaries
+    T_k = beta + (k + 1/2) alpha (k = 0..14) that w exceeds, plus the
+    boundaries it equals for odd k (a tie k + 1/2 goes to the even
+    neighbour: down for even k, up for odd k).  Each T_k is exact in float64
+    (an fp16 value plus (2k + 1) times half an fp16 value), so every
+    comparison is exact."""
+    w = np.asarray(w, dtype=F32).astype(F64)
+    alpha = np.asarray(alpha, dtype=F64)
+    beta = np.asarray(beta, dtype=F64)
+    q = np.zeros(np.broadcast(w, alpha, beta).shape, dtype=np.int64)
+    for k in range(15):
+        t = beta + (k + 0.5) * alpha
+        q += w > t
+        if k % 2 == 1:
+            q += w == t
+    q[np.broadcast_to(alpha == 0.0, q.shape)] = 0
+    return q
+
+
 def quantize_int4_group(W, group: int = 32):
     """Asymmetric min-max INT4 per (row, group of ``group`` consecutive d_in).
     [R16]
 
-    beta  = fp16(min)                      (the group's additive zero point)
-    alpha = fp16(fl32(fl32(max - min) / 15))
-    q     = 0 if alpha == 0 else clamp(round_half_even(fl32(fl32(w - beta) / alpha)), 0, 15)
+    beta  = RN16(min)                       (the group's additive zero point)
+    alpha = RN16((max - min) / 15)          (exact quotient, rounded once)
+    q     = 0 if alpha == 0 else clamp(round_half_even((w - beta) / alpha), 0, 15)
 
-    Returns ``(codes uint8[d_out][d_in/2], scale_bits uint16[d_out][d_in/group],
+    with every rounding taken on the exact real value.  Returns
+    ``(codes uint8[d_out][d_in/2], scale_bits uint16[d_out][d_in/group],
     zero_bits uint16[d_out][d_in/group])`` with fp16 bit patterns."""
     W = np.asarray(W, dtype=F32)
     n, k = W.shape
@@ -334,13 +528,10 @@ def quantize_int4_group(W, group: int = 32):
     lo = g.min(axis=2).astype(F32)
     hi = g.max(axis=2).astype(F32)
     beta_b = f32_to_f16_bits(lo)
-    alpha_b = f32_to_f16_bits(((hi - lo).astype(F32) / F32(15.0)).astype(F32))
+    alpha_b = int4_group_scale(lo, hi)
     beta = f16_bits_to_f32(beta_b)[..., None]
     alpha = f16_bits_to_f32(alpha_b)[..., None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        r = ((g - beta).astype(F32) / alpha).astype(F32)
-        q = np.clip(np.rint(r), 0, 15)
-    q = np.where(alpha == 0, 0, q).astype(np.uint8).reshape(n, k)
+    q = int4_codes(g, alpha, beta).astype(np.uint8).reshape(n, k)
     return pack_nibbles(q), alpha_b, beta_b
 
 
@@ -411,6 +602,48 @@ def qa_merge_zero(zero_bits, A, B, s) -> np.ndarray:
     [QA-LoRA abstract, point (ii); R17]"""
     beta = f16_bits_to_f32(zero_bits).astype(F64)
     return beta + s * (np.asarray(B, dtype=F64) @ np.asarray(A, dtype=F64))
+
+
+def qa_merge_zero_f16(zero_bits, A_bits, B_bits, s) -> np.ndarray:
+    """fp16 bits of the merged zero points RN16(beta + s * sum_j B[n][j] A[j][g]),
+    the exact sum rounded once (ties to even).  [QA-LoRA abstract, point
+    (ii); R17]
+
+    ``A_bits`` [r][G] and ``B_bits`` [d_out][r] are bf16 bit patterns and s a
+    float32.  Every term s * B * A is exact in float64 (24 + 8 + 8
+    significant bits); math.fsum returns the correctly rounded float64 of the
+    exact sum, whose fp16 image is within one fp16 step of the answer, and the
+    sign of the exact sum minus an fp16 rounding boundary (another fsum, with
+    the boundary as one more exact term) decides between the neighbours.
+    Slow (pure Python per entry): for test-sized layers."""
+    beta = f16_bits_to_f32(zero_bits).astype(F64)
+    A = bf16_bits_to_f64(A_bits)
+    B = bf16_bits_to_f64(B_bits)
+    s = float(np.float32(s))
+    n_rows, G = beta.shape
+    r = A.shape[0]
+    out = np.empty((n_rows, G), dtype=np.uint16)
+    inf16 = np.float16(np.inf)
+    for n in range(n_rows):
+        for g in range(G):
+            terms = [float(beta[n, g])] + [s * B[n, j] * A[j, g] for j in range(r)]
+            h = np.float16(math.fsum(terms))
+            # step down while the exact sum lies below the boundary under h,
+            # up while it lies above the boundary over h (ties: even bits)
+            for _ in range(2):
+                lo = np.nextafter(h, -inf16)
+                m = (float(lo) + float(h)) / 2.0
+                d = math.fsum(terms + [-m])
+                if d < 0 or (d == 0 and int(np.array(h).view(np.uint16)) & 1):
+                    h = lo
+            for _ in range(2):
+                hi = np.nextafter(h, inf16)
+                m = (float(h) + float(hi)) / 2.0
+                d = math.fsum(terms + [-m])
+                if d > 0 or (d == 0 and int(np.array(h).view(np.uint16)) & 1):
+                    h = hi
+            out[n, g] = np.array(h).view(np.uint16)
+    return out
 
 
 def rel_fro(got, ref) -> float:

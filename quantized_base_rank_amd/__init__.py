@@ -20,7 +20,7 @@ from ._lib import (EXPORTS, LIB_PATH, QLIN_FMT_INT4_GROUP, QLIN_FMT_NF4, QlinErr
 __all__ = [
     "QWeight", "QlinError", "qlin_nf4_codebook", "qlin_quantize_nf4",
     "qlin_quantize_int4_group", "qlin_workspace_bytes", "qlin_fwd", "qlin_bwd",
-    "qlin_dequant_bf16", "EXPORTS", "LIB_PATH",
+    "qlin_dequant_bf16", "qlin_qa_merge", "qlin_profile_next_launch", "EXPORTS", "LIB_PATH",
 ]
 
 
@@ -137,13 +137,17 @@ def workspace(device, nbytes: int):
 
 def qlin_fwd(w: QWeight, x, A, B, r: int, s: float, pool: int = 1, y=None, u_out=None,
              ws=None, want_u: bool = True):
-    """y = x W_bf16^T + s (P A^T) B^T.  Returns (y, u) (u is None unless wanted)."""
+    """y = x W_bf16^T + s (P A^T) B^T.  Returns (y, u) (u is None unless wanted).
+    r = 0 is the layer without an adapter (A and B may be None; no u)."""
     torch = _torch()
     M = x.shape[0]
     dev = x.device
     _need(x, torch.bfloat16, (M, w.d_in), "x")
-    _need(A, torch.bfloat16, (r, w.d_in // pool), "A")
-    _need(B, torch.bfloat16, (w.d_out, r), "B")
+    if r > 0:
+        _need(A, torch.bfloat16, (r, w.d_in // pool), "A")
+        _need(B, torch.bfloat16, (w.d_out, r), "B")
+    else:
+        want_u = False
     if y is None:
         y = torch.empty((M, w.d_out), dtype=torch.bfloat16, device=dev)
     if u_out is None and want_u:
@@ -152,7 +156,7 @@ def qlin_fwd(w: QWeight, x, A, B, r: int, s: float, pool: int = 1, y=None, u_out
     if ws is None:
         ws = workspace(dev, nbytes)
     s_ = w.struct()
-    check(lib().qlin_fwd(ctypes.byref(s_), x.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
+    check(lib().qlin_fwd(ctypes.byref(s_), x.data_ptr(), M, _ptr(A), _ptr(B), r,
                          float(s), pool, y.data_ptr(), _ptr(u_out), ws.data_ptr(), ws.numel(),
                          _stream(dev)), "qlin_fwd")
     return y, u_out
@@ -183,6 +187,21 @@ def qlin_bwd(w: QWeight, x, A, B, r: int, s: float, dy, pool: int = 1, u_saved=N
     return dx, dA, dB
 
 
+def qlin_qa_merge(w: QWeight, A, B, r: int, s: float, zero_out=None):
+    """Merged fp16 zero points RN16(zero + s B A) of an INT4 weight; returns
+    a new QWeight sharing codes and scales with ``w`` and holding them."""
+    torch = _torch()
+    G = w.d_in // w.block
+    _need(A, torch.bfloat16, (r, G), "A")
+    _need(B, torch.bfloat16, (w.d_out, r), "B")
+    if zero_out is None:
+        zero_out = torch.empty((w.d_out, G), dtype=torch.float16, device=w.device)
+    s_ = w.struct()
+    check(lib().qlin_qa_merge(ctypes.byref(s_), A.data_ptr(), B.data_ptr(), r, float(s),
+                              zero_out.data_ptr(), _stream(w.device)), "qlin_qa_merge")
+    return dataclasses.replace(w, zero=zero_out)
+
+
 def qlin_dequant_bf16(w: QWeight):
     torch = _torch()
     out = torch.empty((w.d_out, w.d_in), dtype=torch.bfloat16, device=w.device)
@@ -190,3 +209,14 @@ def qlin_dequant_bf16(w: QWeight):
     check(lib().qlin_dequant_bf16(ctypes.byref(s_), out.data_ptr(), _stream(w.device)),
           "qlin_dequant_bf16")
     return out
+
+
+def qlin_profile_next_launch(kernel: Optional[str], start=None, stop=None) -> None:
+    """Record torch.cuda.Event ``start`` / ``stop`` around the next launch of
+    ``kernel`` (None disarms).  The events must already exist on the device
+    (record each once before arming)."""
+    if kernel is None:
+        check(lib().qlin_profile_next_launch(None, None, None), "qlin_profile_next_launch")
+        return
+    check(lib().qlin_profile_next_launch(kernel.encode(), start.cuda_event, stop.cuda_event),
+          "qlin_profile_next_launch")

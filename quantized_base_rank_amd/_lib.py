@@ -21,6 +21,8 @@ EXPORTS = (
     "qlin_fwd",
     "qlin_bwd",
     "qlin_dequant_bf16",
+    "qlin_qa_merge",
+    "qlin_profile_next_launch",
     "qlin_status_string",
 )
 
@@ -66,6 +68,8 @@ def lib() -> ctypes.CDLL:
         "qlin_bwd": (ctypes.c_int,
                      [qp, vp, i64, vp, vp, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "qlin_dequant_bf16": (ctypes.c_int, [qp, vp, vp]),
+        "qlin_profile_next_launch": (ctypes.c_int, [ctypes.c_char_p, vp, vp]),
+        "qlin_qa_merge": (ctypes.c_int, [qp, vp, vp, i32, f32, vp, vp]),
         "qlin_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():

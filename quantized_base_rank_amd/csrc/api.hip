@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "host_codebook.hpp"
@@ -61,11 +62,12 @@ int check_weight(const qlin_qweight* w) {
   return QLIN_E_UNSUPPORTED;
 }
 
-int check_layer(const qlin_qweight* w, int64_t M, int32_t r, float s, int32_t pool) {
+// r_min = 0 admits the adapter-free layer (forward only).
+int check_layer(const qlin_qweight* w, int64_t M, int32_t r, float s, int32_t pool, int32_t r_min = 1) {
   const int st = check_weight(w);
   if (st != QLIN_OK) return st;
   if (M < 1 || M > (int64_t{1} << 31)) return QLIN_E_SHAPE;
-  if (r < 1 || r > kMaxRank) return QLIN_E_SHAPE;
+  if (r < r_min || r > kMaxRank) return QLIN_E_SHAPE;
   if (!std::isfinite(s)) return QLIN_E_SHAPE;
   if (pool != 1) {
     if (w->format != QLIN_FMT_INT4_GROUP || pool != w->block) return QLIN_E_UNSUPPORTED;
@@ -92,9 +94,19 @@ int fmt_of(const qlin_qweight* w) { return w->format == QLIN_FMT_NF4 ? kFmtNF4 :
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Ticket counters of the split reductions live in a fixed region at the
+// start of every workspace, the same for every layer shape, and nothing else
+// is ever written there.  Every completed call leaves its counters at zero,
+// so a workspace zero-filled once can be reused by calls of any shape (a
+// counter region whose length followed the shape would overlap, for a later
+// call of another shape, bytes where an earlier call left u or partial sums).
+constexpr size_t kCounterBytes = size_t{64} << 10;
+constexpr int64_t kCounterWords = static_cast<int64_t>(kCounterBytes / sizeof(uint32_t));
+
 // Work split of the reductions and the workspace layout for one layer shape.
 struct Plan {
   bool small = false;
+  bool fits = true;  // the shape's ticket counters fit the fixed region
   int fwd_splits = 1;
   int nt_splits_u = 1, nt_splits_du = 1;
   int tn2_splits_dB = 1, tn2_splits_dA = 1;
@@ -126,9 +138,16 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.gf_splits = gemv_fwd_splits(K);
   p.gd_splits = gemv_dx_splits(N);
 
-  int64_t counters = std::max<int64_t>({nt_tiles(M), gemv_fwd_tiles(N),
-                                        gemv_dx_tiles(K), int64_t{fwd_gemm_tiles(M, N)},
-                                        int64_t{tn2_tiles(N)}, int64_t{tn2_tiles(K)}});
+  // counters each kernel takes tickets on (only when it splits a reduction;
+  // the few-token backward always does)
+  int64_t counters = std::max<int64_t>({p.nt_splits_u > 1 || p.nt_splits_du > 1 ? nt_tiles(M) : 0,
+                                        p.tn2_splits_dB > 1 ? tn2_tiles(N) : 0,
+                                        p.tn2_splits_dA > 1 ? tn2_tiles(K) : 0});
+  if (p.small)
+    counters = std::max<int64_t>({counters, p.gf_splits > 1 ? gemv_fwd_tiles(N) : 0, gemv_dx_tiles(K)});
+  else if (p.fwd_splits > 1)
+    counters = std::max<int64_t>(counters, fwd_gemm_tiles(M, N));
+  p.fits = counters <= kCounterWords;
   int64_t partial = std::max<int64_t>({nt_partial_floats(M, p.nt_splits_u),
                                        nt_partial_floats(M, p.nt_splits_du),
                                        tn2_partial_floats(N, r, p.tn2_splits_dB),
@@ -142,7 +161,7 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
     if (pool > 1) partial = std::max<int64_t>(partial, qa_dA_partial_floats(M, r, G));
   }
   size_t off = 0;
-  p.off_counters = off; off = align256(off + counters * sizeof(uint32_t));
+  p.off_counters = off; off = kCounterBytes;
   p.off_u = off;        off = align256(off + static_cast<size_t>(M) * r * sizeof(float));
   p.off_du = off;       off = align256(off + static_cast<size_t>(M) * r * sizeof(float));
   p.off_Bt = off;       off = align256(off + static_cast<size_t>(N) * r * sizeof(uint16_t));
@@ -154,30 +173,142 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   return p;
 }
 
+// Runs one quantizer launch between clearing and reading back the device's
+// non-finite flag, then synchronises `stream`.  The flag is one word per
+// device, so quantizer calls of this process take turns on a mutex.
+template <typename Launch>
+int run_flagged(hipStream_t stream, Launch launch) {
+  std::lock_guard<std::mutex> guard(quant_flag_lock());
+  uint32_t* flag = nullptr;
+  QLIN_TRY(quant_flag_ptr(&flag));
+  QLIN_TRY(hipMemsetAsync(flag, 0, sizeof(uint32_t), stream));
+  QLIN_TRY(launch(flag));
+  uint32_t bad = 0;
+  QLIN_TRY(hipMemcpyAsync(&bad, flag, sizeof(uint32_t), hipMemcpyDeviceToHost, stream));
+  QLIN_TRY(hipStreamSynchronize(stream));
+  return bad != 0 ? QLIN_E_NONFINITE : QLIN_OK;
+}
+
 template <typename T>
 T* ws_at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
 }
 
+// Profiling aid: qlin_profile_next_launch arms one (kernel name, start,
+// stop) triple; the next launch of that kernel records `start` just before
+// and `stop` just after itself on its stream, and disarms the hook.
+struct ProfileHook {
+  std::mutex m;
+  bool armed = false;
+  char name[64] = {};
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfileHook& profile_hook() {
+  static ProfileHook h;
+  return h;
+}
+
+template <typename Launch>
+hipError_t hooked(const char* name, hipStream_t stream, Launch launch) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  {
+    ProfileHook& h = profile_hook();
+    std::lock_guard<std::mutex> g(h.m);
+    if (h.armed && std::strcmp(h.name, name) == 0) {
+      start = h.start;
+      stop = h.stop;
+      h.armed = false;
+    }
+  }
+  if (start != nullptr) {
+    const hipError_t e = hipEventRecord(start, stream);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch();
+  if (e != hipSuccess || stop == nullptr) return e;
+  return hipEventRecord(stop, stream);
+}
+
 // u = P A^T (P = x, or the group sums of x) into `u` (fp32 [M][r]).
 int compute_u(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A, int32_t r,
-              int32_t pool, float* u, const Plan& p, void* ws, hipStream_t stream) {
+              int32_t pool, float* u, int splits_u, float* partial, uint32_t* counters,
+              hipStream_t stream) {
   if (pool == 1) {
     NtArgs a{};
     a.X = x; a.ldx = w->d_in;
     a.Y = A; a.ldy = w->d_in;
     a.C = u; a.ldc = r;
     a.M = M; a.K = w->d_in; a.J = r;
-    a.splits = p.nt_splits_u;
+    a.splits = splits_u;
     a.alpha = 1.0f;
-    a.partial = ws_at<float>(ws, p.off_partial);
-    a.counters = ws_at<uint32_t>(ws, p.off_counters);
-    return hip_status(launch_nt_skinny(a, stream));
+    a.partial = partial;
+    a.counters = counters;
+    return hip_status(hooked("k_nt_skinny", stream, [&] { return launch_nt_skinny(a, stream); }));
   }
   QaArgs q{};
   q.x = x; q.A = A; q.u_out = u; q.P_out = nullptr;
   q.M = M; q.K = w->d_in; q.G = w->d_in / pool; q.r = r; q.pool = pool;
-  return hip_status(launch_qa_pool_u(q, stream));
+  return hip_status(hooked("k_qa_pool_u", stream, [&] { return launch_qa_pool_u(q, stream); }));
+}
+
+// Whether the few-token forward forms u itself (plain adapter of rank <= 16).
+bool fwd_fuses_u(const Plan& p, int32_t r, int32_t pool) { return p.small && pool == 1 && r <= 16; }
+
+// The forward pass on explicit buffers: `u_tmp` (fp32 [M][r], used when
+// u_out is NULL), `partial` (split partial sums) and `counters` (ticket
+// counters, zero on entry and left at zero).
+int fwd_core(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
+             const uint16_t* B, int32_t r, float s, int32_t pool, uint16_t* y, float* u_out,
+             const Plan& p, float* u_tmp, float* partial, uint32_t* counters,
+             hipStream_t stream) {
+  const WeightView v = make_view(w);
+  const int fmt = fmt_of(w);
+  float* u = u_out != nullptr ? u_out : u_tmp;
+  const bool adapter = r > 0 && s != 0.0f;
+  const bool fuse_u = fwd_fuses_u(p, r, pool);
+  if (!fuse_u && (adapter || u_out != nullptr)) {
+    const int st = compute_u(w, x, M, A, r, pool, u, p.nt_splits_u, partial, counters, stream);
+    if (st != QLIN_OK) return st;
+  }
+  if (p.small) {
+    GemvFwdArgs a{};
+    a.w = v; a.x = x; a.M = M; a.A = A; a.B = B; a.r = r; a.s = s;
+    a.adapter = adapter ? 1 : 0;
+    a.fuse_u = (fuse_u && (adapter || u_out != nullptr)) ? 1 : 0;
+    a.u_in = u;
+    a.y = y; a.u_out = u_out;
+    a.splits = gemv_fwd_splits(w->d_in);
+    a.kshare = gemv_fwd_kshare(w->d_in);
+    a.partial = partial;
+    a.counters = counters;
+    return hip_status(hooked("k_gemv_fwd", stream, [&] { return launch_gemv_fwd(a, fmt, stream); }));
+  }
+  FwdArgs a{};
+  a.w = v; a.x = x; a.M = M; a.B = B; a.u = adapter ? u : nullptr; a.r = r; a.s = s; a.y = y;
+  a.splits = p.fwd_splits;
+  a.partial = partial;
+  a.counters = counters;
+  return hip_status(hooked("k_fwd_gemm", stream, [&] { return launch_fwd_gemm(a, fmt, stream); }));
+}
+
+// Argument checks shared by qlin_fwd and qlin_fwd_noalloc.
+int check_fwd_args(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                   const uint16_t* B, int32_t r, float s, int32_t pool, const uint16_t* y,
+                   const float* u_out) {
+  const int st = check_layer(w, M, r, s, pool, 0);
+  if (st != QLIN_OK) return st;
+  if (r == 0) {
+    // no adapter: A and B are not read, and there is no u to return
+    if (u_out != nullptr) return QLIN_E_SHAPE;
+    if (x == nullptr || y == nullptr) return QLIN_E_NULL;
+    if (!aligned16(x) || !aligned16(y)) return QLIN_E_ALIGN;
+    return QLIN_OK;
+  }
+  if (x == nullptr || A == nullptr || B == nullptr || y == nullptr) return QLIN_E_NULL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
+      (u_out != nullptr && !aligned16(u_out)))
+    return QLIN_E_ALIGN;
+  return QLIN_OK;
 }
 
 }  // namespace
@@ -214,7 +345,7 @@ int qlin_quantize_nf4(const float* W, int64_t d_out, int64_t d_in, int32_t block
   if (dq_block != 0 && absmax2 == nullptr) return QLIN_E_NULL;
   if (block != 64) return QLIN_E_UNSUPPORTED;
   if (dq_block != 0 && dq_block != 256) return QLIN_E_UNSUPPORTED;
-  if (d_out < 1 || d_in < 1 || d_in % 64 != 0) return QLIN_E_SHAPE;
+  if (d_out < 1 || d_in < 1 || d_in % 64 != 0 || d_out % 16 != 0) return QLIN_E_SHAPE;
   if (d_out > (int64_t{1} << 40) / d_in) return QLIN_E_SHAPE;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax) ||
       (dq_block != 0 && !aligned16(absmax2)))
@@ -224,87 +355,45 @@ int qlin_quantize_nf4(const float* W, int64_t d_out, int64_t d_in, int32_t block
   double mids[15];
   for (int i = 0; i < 15; ++i) mids[i] = (static_cast<double>(cb[i]) + static_cast<double>(cb[i + 1])) / 2.0;
   const int64_t n_blocks = d_out * d_in / 64;
-  QLIN_TRY(launch_quant_nf4(W, n_blocks, dq_block != 0 ? 1 : 0, mids, codes, absmax, absmax2, stream));
-  QLIN_TRY(hipStreamSynchronize(stream));
-  // non-finite input is reported through NaN constants
-  if (dq_block != 0) {
-    std::vector<float> s2(static_cast<size_t>((n_blocks + 255) / 256));
-    QLIN_TRY(hipMemcpy(s2.data(), absmax2, s2.size() * sizeof(float), hipMemcpyDeviceToHost));
-    for (float v : s2)
-      if (std::isnan(v)) return QLIN_E_NONFINITE;
-  } else {
-    std::vector<float> am(static_cast<size_t>(n_blocks));
-    QLIN_TRY(hipMemcpy(am.data(), absmax, am.size() * sizeof(float), hipMemcpyDeviceToHost));
-    for (float v : am)
-      if (std::isnan(v)) return QLIN_E_NONFINITE;
-  }
-  return QLIN_OK;
+  return run_flagged(stream, [&](uint32_t* flag) {
+    return launch_quant_nf4(W, n_blocks, dq_block != 0 ? 1 : 0, mids, codes, absmax, absmax2,
+                            flag, stream);
+  });
 }
 
 int qlin_quantize_int4_group(const float* W, int64_t d_out, int64_t d_in, int32_t group,
                              uint8_t* codes, uint16_t* scale, uint16_t* zero, hipStream_t stream) {
   if (W == nullptr || codes == nullptr || scale == nullptr || zero == nullptr) return QLIN_E_NULL;
   if (group != 32) return QLIN_E_UNSUPPORTED;
-  if (d_out < 1 || d_in < 1 || d_in % 32 != 0) return QLIN_E_SHAPE;
+  // the layer streams INT4 weights 64 columns (two groups) at a time and
+  // tiles rows by 16, so the quantizer accepts exactly the shapes it can use
+  if (d_out < 1 || d_in < 1 || d_in % 64 != 0 || d_out % 16 != 0) return QLIN_E_SHAPE;
   if (d_out > (int64_t{1} << 40) / d_in) return QLIN_E_SHAPE;
   if (!aligned16(W) || !aligned16(codes) || !aligned16(scale) || !aligned16(zero)) return QLIN_E_ALIGN;
   const int64_t n_groups = d_out * d_in / 32;
-  QLIN_TRY(launch_quant_int4(W, n_groups, codes, scale, zero, stream));
-  QLIN_TRY(hipStreamSynchronize(stream));
-  std::vector<uint16_t> sc(static_cast<size_t>(n_groups));
-  QLIN_TRY(hipMemcpy(sc.data(), scale, sc.size() * sizeof(uint16_t), hipMemcpyDeviceToHost));
-  for (uint16_t v : sc)
-    if ((v & 0x7C00u) == 0x7C00u) return QLIN_E_NONFINITE;
-  return QLIN_OK;
+  return run_flagged(stream, [&](uint32_t* flag) {
+    return launch_quant_int4(W, n_groups, codes, scale, zero, flag, stream);
+  });
 }
 
 size_t qlin_workspace_bytes(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
-  if (check_layer(w, M, r, 0.0f, pool) != QLIN_OK) return 0;
-  return make_plan(w, M, r, pool).total;
+  if (check_layer(w, M, r, 0.0f, pool, 0) != QLIN_OK) return 0;
+  const Plan p = make_plan(w, M, r, pool);
+  return p.fits ? p.total : 0;
 }
 
 int qlin_fwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
              const uint16_t* B, int32_t r, float s, int32_t pool, uint16_t* y, float* u_out,
              void* workspace, size_t ws_bytes, hipStream_t stream) {
-  int st = check_layer(w, M, r, s, pool);
+  const int st = check_fwd_args(w, x, M, A, B, r, s, pool, y, u_out);
   if (st != QLIN_OK) return st;
-  if (x == nullptr || A == nullptr || B == nullptr || y == nullptr) return QLIN_E_NULL;
-  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
-      (u_out != nullptr && !aligned16(u_out)))
-    return QLIN_E_ALIGN;
   const Plan p = make_plan(w, M, r, pool);
+  if (!p.fits) return QLIN_E_SHAPE;
   if (workspace == nullptr || ws_bytes < p.total) return QLIN_E_WORKSPACE;
   if (!aligned16(workspace)) return QLIN_E_ALIGN;
-
-  const WeightView v = make_view(w);
-  const int fmt = fmt_of(w);
-  float* u = u_out != nullptr ? u_out : ws_at<float>(workspace, p.off_u);
-  const bool adapter = s != 0.0f;
-  // the few-token kernel forms u itself for a plain adapter of rank <= 16
-  const bool fuse_u = p.small && pool == 1 && r <= 16;
-  if (!fuse_u && (adapter || u_out != nullptr)) {
-    st = compute_u(w, x, M, A, r, pool, u, p, workspace, stream);
-    if (st != QLIN_OK) return st;
-  }
-  if (p.small) {
-    GemvFwdArgs a{};
-    a.w = v; a.x = x; a.M = M; a.A = A; a.B = B; a.r = r; a.s = s;
-    a.adapter = adapter ? 1 : 0;
-    a.fuse_u = (fuse_u && (adapter || u_out != nullptr)) ? 1 : 0;
-    a.u_in = u;
-    a.y = y; a.u_out = u_out;
-    a.splits = gemv_fwd_splits(w->d_in);
-    a.kshare = gemv_fwd_kshare(w->d_in);
-    a.partial = ws_at<float>(workspace, p.off_partial);
-    a.counters = ws_at<uint32_t>(workspace, p.off_counters);
-    return hip_status(launch_gemv_fwd(a, fmt, stream));
-  }
-  FwdArgs a{};
-  a.w = v; a.x = x; a.M = M; a.B = B; a.u = adapter ? u : nullptr; a.r = r; a.s = s; a.y = y;
-  a.splits = p.fwd_splits;
-  a.partial = ws_at<float>(workspace, p.off_partial);
-  a.counters = ws_at<uint32_t>(workspace, p.off_counters);
-  return hip_status(launch_fwd_gemm(a, fmt, stream));
+  return fwd_core(w, x, M, A, B, r, s, pool, y, u_out, p, ws_at<float>(workspace, p.off_u),
+                  ws_at<float>(workspace, p.off_partial), ws_at<uint32_t>(workspace, p.off_counters),
+                  stream);
 }
 
 int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -321,6 +410,7 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
       (u_saved != nullptr && !aligned16(u_saved)))
     return QLIN_E_ALIGN;
   const Plan p = make_plan(w, M, r, pool);
+  if (!p.fits) return QLIN_E_SHAPE;
   if (workspace == nullptr || ws_bytes < p.total) return QLIN_E_WORKSPACE;
   if (!aligned16(workspace)) return QLIN_E_ALIGN;
 
@@ -336,7 +426,7 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   const float* u = u_saved;
   if (u == nullptr) {
     float* uw = ws_at<float>(workspace, p.off_u);
-    st = compute_u(w, x, M, A, r, pool, uw, p, workspace, stream);
+    st = compute_u(w, x, M, A, r, pool, uw, p.nt_splits_u, partial, counters, stream);
     if (st != QLIN_OK) return st;
     u = uw;
   }
@@ -349,56 +439,85 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     a.partial = partial;
     a.du_part = partial + gemv_dx_partial_floats(N, K);
     a.counters = counters;
-    return hip_status(launch_gemv_dx(a, fmt, stream));
+    return hip_status(hooked("k_gemv_dx", stream, [&] { return launch_gemv_dx(a, fmt, stream); }));
   }
   // du = s dY B  (B^T staged so both operands are contiguous along n)
-  QLIN_TRY(launch_transpose16(B, N, r, Bt, stream));
+  QLIN_TRY(hooked("k_transpose16", stream, [&] { return launch_transpose16(B, N, r, Bt, stream); }));
   {
     NtArgs a{};
     a.X = dy; a.ldx = N; a.Y = Bt; a.ldy = N; a.C = du; a.ldc = r;
     a.M = M; a.K = N; a.J = r; a.splits = p.nt_splits_du; a.alpha = s;
     a.partial = partial; a.counters = counters;
-    QLIN_TRY(launch_nt_skinny(a, stream));
+    QLIN_TRY(hooked("k_nt_skinny", stream, [&] { return launch_nt_skinny(a, stream); }));
   }
   // dB = s dY^T u  (u as bf16 hi/lo planes)
   const int64_t jp = tn2_jp(r);
   uint16_t* zp = ws_at<uint16_t>(workspace, p.off_z);
   {
-    QLIN_TRY(launch_split_hl(u, M, r, r, zp, zp + M * jp, stream));
+    QLIN_TRY(hooked("k_split_hl", stream, [&] { return launch_split_hl(u, M, r, r, zp, zp + M * jp, stream); }));
     Tn2Args a{};
     a.X = dy; a.ldx = N; a.Zh = zp; a.Zl = zp + M * jp; a.C = dB; a.ldc = r;
     a.M = M; a.P = N; a.J = r; a.splits = p.tn2_splits_dB; a.out_transposed = 0; a.alpha = s;
     a.partial = partial; a.counters = counters;
-    QLIN_TRY(launch_tn2(a, stream));
+    QLIN_TRY(hooked("k_tn2", stream, [&] { return launch_tn2(a, stream); }));
   }
   // dA = du^T P
   if (pool == 1) {
-    QLIN_TRY(launch_split_hl(du, M, r, r, zp + 2 * M * jp, zp + 3 * M * jp, stream));
+    QLIN_TRY(hooked("k_split_hl", stream, [&] { return launch_split_hl(du, M, r, r, zp + 2 * M * jp, zp + 3 * M * jp, stream); }));
     Tn2Args a{};
     a.X = x; a.ldx = K; a.Zh = zp + 2 * M * jp; a.Zl = zp + 3 * M * jp; a.C = dA; a.ldc = K;
     a.M = M; a.P = K; a.J = r; a.splits = p.tn2_splits_dA; a.out_transposed = 1; a.alpha = 1.0f;
     a.partial = partial; a.counters = counters;
-    QLIN_TRY(launch_tn2(a, stream));
+    QLIN_TRY(hooked("k_tn2", stream, [&] { return launch_tn2(a, stream); }));
   } else {
     QaArgs q{};
     q.x = x; q.A = A; q.du = du; q.M = M; q.K = K; q.G = G; q.r = r; q.pool = pool;
     q.P_out = ws_at<float>(workspace, p.off_P);
-    QLIN_TRY(launch_qa_pool_u(q, stream));
+    QLIN_TRY(hooked("k_qa_pool_u", stream, [&] { return launch_qa_pool_u(q, stream); }));
     q.P_in = q.P_out;
     q.dA_out = dA;
     q.part = partial;
-    QLIN_TRY(launch_qa_dA(q, stream));
+    QLIN_TRY(hooked("k_qa_dA", stream, [&] { return launch_qa_dA(q, stream); }));
   }
   if (dx == nullptr) return QLIN_OK;
   // dX = dY W_bf16 + du A; with the pooled adapter A^T has one row per group
   // and column k of dX reads row k >> log2(pool)
   uint16_t* At = ws_at<uint16_t>(workspace, p.off_At);
-  QLIN_TRY(launch_transpose16(A, r, G, At, stream));
+  QLIN_TRY(hooked("k_transpose16", stream, [&] { return launch_transpose16(A, r, G, At, stream); }));
   DxArgs a{};
   a.w = v; a.dy = dy; a.M = M; a.At = At; a.du = du; a.r = r;
   a.pool = pool; a.pool_shift = __builtin_ctz(static_cast<unsigned>(pool));
   a.dx = dx;
-  return hip_status(launch_dx_gemm(a, fmt, stream));
+  return hip_status(hooked("k_dx_gemm", stream, [&] { return launch_dx_gemm(a, fmt, stream); }));
+}
+
+int qlin_qa_merge(const qlin_qweight* w, const uint16_t* A, const uint16_t* B, int32_t r, float s,
+                  uint16_t* zero_out, hipStream_t stream) {
+  const int st = check_weight(w);
+  if (st != QLIN_OK) return st;
+  if (w->format != QLIN_FMT_INT4_GROUP) return QLIN_E_UNSUPPORTED;
+  if (r < 1 || r > kMaxRank) return QLIN_E_SHAPE;
+  if (!std::isfinite(s)) return QLIN_E_SHAPE;
+  if (A == nullptr || B == nullptr || zero_out == nullptr) return QLIN_E_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(zero_out)) return QLIN_E_ALIGN;
+  const int64_t G = w->d_in / w->block;
+  return hip_status(launch_qa_merge(w->zero, A, B, w->d_out, G, r, s, zero_out, stream));
+}
+
+int qlin_profile_next_launch(const char* kernel, hipEvent_t start, hipEvent_t stop) {
+  ProfileHook& h = profile_hook();
+  std::lock_guard<std::mutex> g(h.m);
+  if (kernel == nullptr) {
+    h.armed = false;
+    return QLIN_OK;
+  }
+  if (start == nullptr || stop == nullptr) return QLIN_E_NULL;
+  if (std::strlen(kernel) >= sizeof(h.name)) return QLIN_E_SHAPE;
+  std::strcpy(h.name, kernel);
+  h.start = start;
+  h.stop = stop;
+  h.armed = true;
+  return QLIN_OK;
 }
 
 int qlin_dequant_bf16(const qlin_qweight* w, uint16_t* W_out, hipStream_t stream) {

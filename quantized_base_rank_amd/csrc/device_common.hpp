@@ -133,11 +133,18 @@ __device__ __forceinline__ u32x4 lut_decode8(const Lut16& t, uint32_t w) {
 
 // ------------------------------------------------------- per-block scales
 
-// Double-quantized NF4 block scale: step = fl32(s2 * fl32(1/127)),
-// a_hat = fl32(q * step).  [QLoRA "Innovation 2: Double Quantization"]
+// Double-quantized NF4 block scale a_hat = RN32(q * s2 / 127): the 8-bit
+// grid of a group runs from 0 to its maximum s2 in 127 equal steps, and the
+// stored constant is the grid value rounded once to fp32.
+// [QLoRA "Innovation 2: Double Quantization"]
+// q * s2 is exact in fp64 (7 + 24 significant bits); multiplying it by
+// fl64(1/127) stays within 2^-52 relative of the quotient.  A quotient by
+// 127 that is not itself an fp32 number lies at least 1/254 of an fp32 ulp
+// from every fp32 rounding boundary, so the final fp64 -> fp32 rounding
+// yields the correctly rounded quotient (and q = 127 gives s2 exactly).
 __device__ __forceinline__ float nf4_dq_scale(int8_t q, float s2) {
-  const float step = s2 * (1.0f / 127.0f);
-  return static_cast<float>(q) * step;
+  const double p = static_cast<double>(q) * static_cast<double>(s2);
+  return static_cast<float>(p * (1.0 / 127.0));
 }
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {

@@ -109,20 +109,26 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   // dY tile of a step by direct-to-LDS loads: instruction i of wave w
   // covers rows 32 i + 8 w .. +7 (1 KB), the swizzle applied to the source
   // chunk.  Rows past M fall outside the resource (their outputs are never
-  // stored); columns past N read the next row's values, which meet weight
-  // rows past N that decode to zero.
+  // stored).  In the last step of a d_out that is not a multiple of 64, the
+  // pieces past N would be the next token's first values: their offsets are
+  // moved past the resource (bit 31) so they load zeros, and a non-finite
+  // dY value never reaches another token's dX through the zero weights there.
   const int64_t dy_rows = M - m0 < kTMx ? M - m0 : kTMx;
   const rsrc_t dyr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.dy + m0 * N), 0, static_cast<int>(dy_rows * N * 2), 0x00020000);
   const int dlrow = wave * 8 + (lane >> 3);
-  const uint32_t dyvoff = static_cast<uint32_t>(dlrow * N * 2 + (((lane & 7) ^ dsw(dlrow)) << 4));
+  const int dpiece = (lane & 7) ^ dsw(dlrow);  // 16-byte piece of the step's 64 columns
+  const uint32_t dyvoff = static_cast<uint32_t>(dlrow * N * 2 + (dpiece << 4));
+  const int n_tail = static_cast<int>(N % kNS);  // valid columns of the last step (0: all)
+  const uint32_t dtail_oob = (n_tail != 0 && dpiece * 8 >= n_tail) ? 0x80000000u : 0u;
   auto load_dy = [&](int64_t st, int stage) {
     const int64_t stc = st < nsteps ? st : nsteps - 1;
     const uint32_t nb = static_cast<uint32_t>(stc * kNS * 2);
+    const uint32_t voff = dyvoff | (dtail_oob & (stc == nsteps - 1 ? 0xFFFFFFFFu : 0u));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          dyr, (lds_ptr_t)(s_dy[stage] + (i * 4 + wave) * 1024), 16, dyvoff,
+          dyr, (lds_ptr_t)(s_dy[stage] + (i * 4 + wave) * 1024), 16, voff,
           static_cast<int>(static_cast<uint32_t>(i * 32 * N * 2) + nb), 0, 0);
   };
 

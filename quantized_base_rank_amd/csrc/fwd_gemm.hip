@@ -185,19 +185,26 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   // Token tile source: a buffer resource over this tile's rows of x, so a
   // load is one instruction with a fixed per-lane offset and a scalar
   // per-step offset.  Rows past M fall outside the resource (their output
-  // rows are never stored); columns past K in the last step meet weights
-  // masked to zero.
+  // rows are never stored).  When the last K step holds only 64 columns
+  // (K % 128 == 64), its upper eight 16-byte pieces of a row would be the
+  // next token's first columns: their offsets are moved past the resource
+  // (bit 31), so they load zeros and a non-finite value in one token never
+  // reaches another token's output through the zero weights there.
   const int64_t rows_here = M - m0 < kTM ? M - m0 : kTM;
   const rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.x + m0 * K), 0, static_cast<int>(rows_here * K * 2), 0x00020000);
   const int lrow = wave * 4 + (lane >> 4);  // row within each group of 16
-  const uint32_t xvoff = static_cast<uint32_t>(lrow * K * 2 + (((lane & 15) ^ lrow) << 4));
+  const int xpiece = (lane & 15) ^ lrow;    // 16-byte piece of the step's 128 columns
+  const uint32_t xvoff = static_cast<uint32_t>(lrow * K * 2 + (xpiece << 4));
+  const uint32_t xtail_oob = xpiece >= 8 ? 0x80000000u : 0u;
+  const int64_t ks_tail = (K % kKS) != 0 ? ksteps - 1 : -1;
   auto load_x = [&](int64_t ks, int buf) {
     const uint32_t kb2 = static_cast<uint32_t>(ks * kKS * 2);
+    const uint32_t voff = xvoff | (xtail_oob & (ks == ks_tail ? 0xFFFFFFFFu : 0u));
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (lds_ptr_t)(&s_x[buf][(i * 4 + wave) * 1024]), 16, xvoff,
+          xr, (lds_ptr_t)(&s_x[buf][(i * 4 + wave) * 1024]), 16, voff,
           static_cast<int>(static_cast<uint32_t>(i * 16 * K * 2) + kb2), 0, 0);
   };
   // Packed codes of a K step: 256 rows x 64 B into LDS next to the token

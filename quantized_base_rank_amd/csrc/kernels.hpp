@@ -5,16 +5,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.hpp"
 
 namespace qlin {
 
+constexpr int kMaxDevices = 64;
+
 // ---------------------------------------------------------------- quantizers
+// The quantizers report non-finite input through a per-device flag word
+// (quant_flag_ptr, on the current device); callers hold quant_flag_lock()
+// from clearing the flag until they have read it back.
+std::mutex& quant_flag_lock();
+hipError_t quant_flag_ptr(uint32_t** out);
 hipError_t launch_quant_nf4(const float* W, int64_t n_blocks, int dq, const double* mids15,
-                            uint8_t* codes, void* absmax, float* absmax2, hipStream_t stream);
+                            uint8_t* codes, void* absmax, float* absmax2, uint32_t* flag,
+                            hipStream_t stream);
 hipError_t launch_quant_int4(const float* W, int64_t n_groups, uint8_t* codes, uint16_t* scale,
-                             uint16_t* zero, hipStream_t stream);
+                             uint16_t* zero, uint32_t* flag, hipStream_t stream);
 hipError_t launch_dequant(const WeightView& w, int fmt, uint16_t* out, hipStream_t stream);
+// zero'[n][g] = RN16(zero[n][g] + s sum_j B[n][j] A[j][g]) (QA-LoRA merge)
+hipError_t launch_qa_merge(const uint16_t* zero, const uint16_t* A, const uint16_t* B, int64_t N,
+                           int64_t G, int r, float s, uint16_t* out, hipStream_t stream);
 
 // ------------------------------------------------------------ adapter ops
 struct NtArgs {  // C[m][j] = alpha * sum_k X[m][k] Y[j][k]

@@ -7,6 +7,8 @@
 // Every decision that yields an integer (nearest level, the 8-bit absmax
 // code, the INT4 code) is taken with exact or correctly rounded IEEE
 // arithmetic, so codes and constants are reproducible bit for bit.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -28,7 +30,8 @@ __global__ __launch_bounds__(256) void k_quant_nf4(const float* __restrict__ W, 
                                                    int dq, Midpoints mids,
                                                    uint8_t* __restrict__ codes,
                                                    void* __restrict__ absmax_out,
-                                                   float* __restrict__ absmax2_out) {
+                                                   float* __restrict__ absmax2_out,
+                                                   uint32_t* __restrict__ bad_flag) {
   __shared__ float s_abs[256];
   __shared__ int s_bad[256];
   const int tid = threadIdx.x;
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(256) void k_quant_nf4(const float* __restrict__ W, 
         s_abs[local] = a;
         s_bad[local] = bad;
         if (!dq) static_cast<float*>(absmax_out)[b] = bad ? __builtin_nanf("") : a;
+        if (bad) __hip_atomic_fetch_or(bad_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else if (li == 0) {
       s_abs[local] = 0.0f;
@@ -120,11 +124,62 @@ __global__ __launch_bounds__(256) void k_quant_nf4(const float* __restrict__ W, 
   if (tid == 0) absmax2_out[g] = gbad ? __builtin_nanf("") : s2;
 }
 
+// fp16 value nearest to (hi - lo) / 15 in exact arithmetic, ties to the even
+// significand (hi >= lo, both finite fp32 within the fp16 range).
+//
+// The difference is formed in fp64 together with its rounding error
+// (two-sum), so hi - lo == d + e exactly.  A first candidate comes from the
+// fp64 quotient rounded to fp32 and then fp16, which is at most one fp16
+// step away from the answer.  The candidate is then checked against the two
+// rounding boundaries next to it: a boundary m (the midpoint of neighbouring
+// fp16 values) has at most 12 significant bits, so 15 m is exact in fp64,
+// and the sign of (d - 15 m) + e is the sign of hi - lo - 15 m: either
+// d - 15 m is exact (the two are within a factor of two) or it is far larger
+// than e.
+__device__ double qs_f16_value(uint32_t bits) {
+  return static_cast<double>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+// -1, 0, +1: the sign of (d + e) - t
+__device__ int qs_cmp(double d, double e, double t) {
+  const double v = (d - t) + e;
+  return v > 0.0 ? 1 : (v < 0.0 ? -1 : 0);
+}
+__device__ uint16_t int4_scale_bits(float hi, float lo) {
+  const double h = static_cast<double>(hi), l = -static_cast<double>(lo);
+  const double d = h + l;
+  const double bv = d - h;
+  const double e = (h - (d - bv)) + (l - bv);
+  const _Float16 c0 = static_cast<_Float16>(static_cast<float>(d / 15.0));
+  uint32_t c = __builtin_bit_cast(uint16_t, c0);
+  if (c != 0) {
+    // boundary below the candidate
+    const double m = 0.5 * (qs_f16_value(c - 1) + qs_f16_value(c));
+    const int s = qs_cmp(d, e, 15.0 * m);
+    if (s < 0 || (s == 0 && (c & 1u))) c -= 1;
+  }
+  {
+    // boundary above the candidate (the range of fp16 inputs keeps
+    // (hi - lo)/15 far below the largest fp16 value)
+    const double m = 0.5 * (qs_f16_value(c) + qs_f16_value(c + 1));
+    const int s = qs_cmp(d, e, 15.0 * m);
+    if (s > 0 || (s == 0 && (c & 1u))) c += 1;
+  }
+  return static_cast<uint16_t>(c);
+}
+
 // Group-wise asymmetric INT4: 8 lanes per group of 32, 4 weights per lane.
+//   zero  = RN16(min),  scale = RN16((max - min) / 15),
+//   q     = clamp(round_half_even((w - zero) / scale), 0, 15)  (0 if scale == 0)
+// each rounding taken on the exact value.  The code counts the boundaries
+// t_k = zero + (k + 1/2) scale (k = 0..14) below w, plus those equal to w
+// for odd k (a half-way value goes to the even neighbour); every t_k is exact
+// in fp64 (an fp16 value plus an odd multiple of half an fp16 value), so
+// each comparison is exact.
 __global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ W, int64_t n_groups,
                                                     uint8_t* __restrict__ codes,
                                                     uint16_t* __restrict__ scale,
-                                                    uint16_t* __restrict__ zero) {
+                                                    uint16_t* __restrict__ zero,
+                                                    uint32_t* __restrict__ bad_flag) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t grp = t >> 3;
   const int li = threadIdx.x & 7;
@@ -143,19 +198,21 @@ __global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ W,
     bad |= __shfl_xor(bad, o, 64);
   }
   const _Float16 beta_h = static_cast<_Float16>(lo);
-  const float range = hi - lo;
-  const _Float16 alpha_h = static_cast<_Float16>(range / 15.0f);
-  const float beta = static_cast<float>(beta_h);
-  const float alpha = static_cast<float>(alpha_h);
+  const uint16_t alpha_bits = bad ? static_cast<uint16_t>(0) : int4_scale_bits(hi, lo);
+  const double beta = static_cast<double>(beta_h);
+  const double alpha = qs_f16_value(alpha_bits);
   uint32_t nib[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    float q = 0.0f;
-    if (alpha != 0.0f) {
-      const float r = (w4[e] - beta) / alpha;
-      q = fminf(fmaxf(__builtin_rintf(r), 0.0f), 15.0f);
+    const double wd = static_cast<double>(w4[e]);
+    uint32_t q = 0;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+      const double tk = beta + (static_cast<double>(k) + 0.5) * alpha;
+      q += (wd > tk) ? 1u : 0u;
+      if (k & 1) q += (wd == tk) ? 1u : 0u;
     }
-    nib[e] = static_cast<uint32_t>(q);
+    nib[e] = alpha_bits == 0 ? 0u : q;
   }
   // the packed layout of the NF4 quantizer: byte j of each run of 8 holds
   // elements j (low nibble) and j + 4 (high nibble)
@@ -164,8 +221,9 @@ __global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ W,
   if (grp < n_groups) {
     if ((li & 1) == 0) reinterpret_cast<uint32_t*>(codes + grp * 16)[li >> 1] = word;
     if (li == 0) {
-      scale[grp] = bad ? static_cast<uint16_t>(0x7E00u) : __builtin_bit_cast(uint16_t, alpha_h);
+      scale[grp] = alpha_bits;
       zero[grp] = __builtin_bit_cast(uint16_t, beta_h);
+      if (bad) __hip_atomic_fetch_or(bad_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -184,24 +242,53 @@ __global__ __launch_bounds__(256) void k_dequant(WeightView w, uint16_t* __restr
   reinterpret_cast<u32x4*>(out)[t] = lut_decode8(lut, word);
 }
 
+// Non-finite-input flag of the quantizers: one word in each device's copy of
+// this code object.  The quantizer entry points clear it, run the kernel,
+// read it back and synchronise, holding quant_flag_lock() throughout.
+__device__ uint32_t g_quant_flag;
+
 }  // namespace
 
+std::mutex& quant_flag_lock() {
+  static std::mutex m;
+  return m;
+}
+
+hipError_t quant_flag_ptr(uint32_t** out) {
+  // device address of g_quant_flag on the current device, looked up once per
+  // device (callers hold quant_flag_lock())
+  static uint32_t* cache[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (cache[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_quant_flag));
+    if (e != hipSuccess) return e;
+    cache[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = cache[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_quant_nf4(const float* W, int64_t n_blocks, int dq, const double* mids15,
-                            uint8_t* codes, void* absmax, float* absmax2, hipStream_t stream) {
+                            uint8_t* codes, void* absmax, float* absmax2, uint32_t* flag,
+                            hipStream_t stream) {
   Midpoints m;
   for (int i = 0; i < 15; ++i) m.m[i] = mids15[i];
   const int64_t groups = (n_blocks + 255) / 256;
   hipLaunchKernelGGL(k_quant_nf4, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, stream, W,
-                     n_blocks, dq, m, codes, absmax, absmax2);
+                     n_blocks, dq, m, codes, absmax, absmax2, flag);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_int4(const float* W, int64_t n_groups, uint8_t* codes, uint16_t* scale,
-                             uint16_t* zero, hipStream_t stream) {
+                             uint16_t* zero, uint32_t* flag, hipStream_t stream) {
   const int64_t threads = n_groups * 8;
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(k_quant_int4, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream, W,
-                     n_groups, codes, scale, zero);
+                     n_groups, codes, scale, zero, flag);
   return hipGetLastError();
 }
 

@@ -60,7 +60,8 @@ def test_workspace_bytes_host_only():
         n = L.qlin_workspace_bytes(ctypes.byref(_qw()), M, 16, 1)
         assert n > 0 and n % 256 == 0
     assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 0, 16, 1) == 0
-    assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 0, 1) == 0
+    assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, -1, 1) == 0
+    assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 0, 1) > 0   # adapter-free forward
     assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 129, 1) == 0
     # pooled adapter needs the INT4 group format with pool == group
     assert L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 16, 32) == 0
@@ -78,7 +79,13 @@ def test_argument_errors_return_before_any_launch():
     # fwd: null input, misaligned input, bad rank, bad shape, bad pool, no workspace
     assert L.qlin_fwd(ctypes.byref(qw), None, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 1
     assert L.qlin_fwd(ctypes.byref(qw), bad, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 3
-    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, 0, 2.0, 1, ok, None, ws, big, None) == 2
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, -1, 2.0, 1, ok, None, ws, big, None) == 2
+    # r = 0 (no adapter) returns no u, and still needs x and y
+    assert L.qlin_fwd(ctypes.byref(qw), ok, 16, None, None, 0, 2.0, 1, ok, ok, ws, big, None) == 2
+    assert L.qlin_fwd(ctypes.byref(qw), None, 16, None, None, 0, 2.0, 1, ok, None, ws, big,
+                      None) == 1
+    assert L.qlin_bwd(ctypes.byref(qw), ok, 16, ok, ok, 0, 2.0, 1, ok, None, ok, ok, ok, ws,
+                      big, None) == 2
     assert L.qlin_fwd(ctypes.byref(qw), ok, 0, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 2
     assert L.qlin_fwd(ctypes.byref(qw), ok, 16, ok, ok, 16, float("nan"), 1, ok, None, ws, big,
                       None) == 2
@@ -108,10 +115,29 @@ def test_argument_errors_return_before_any_launch():
     assert L.qlin_quantize_nf4(ok, 4, 96, 64, 256, ok, ok, ok, None) == 2
     assert L.qlin_quantize_nf4(ok, 4, 64, 64, 128, ok, ok, ok, None) == 5
     assert L.qlin_quantize_nf4(ok, 4, 64, 64, 256, ok, ok, None, None) == 1
-    assert L.qlin_quantize_nf4(bad, 4, 64, 64, 256, ok, ok, ok, None) == 3
+    assert L.qlin_quantize_nf4(bad, 16, 64, 64, 256, ok, ok, ok, None) == 3
     assert L.qlin_quantize_int4_group(ok, 4, 64, 64, ok, ok, ok, None) == 5
     assert L.qlin_quantize_int4_group(ok, 4, 48, 32, ok, ok, ok, None) == 2
     assert L.qlin_quantize_int4_group(ok, 4, 64, 32, ok, None, ok, None) == 1
+    # the quantizers accept exactly the shapes the layer accepts: d_out a
+    # multiple of 16, d_in a multiple of 64 (also for INT4 groups of 32)
+    assert L.qlin_quantize_nf4(ok, 4, 64, 64, 256, ok, ok, ok, None) == 2
+    assert L.qlin_quantize_int4_group(ok, 16, 96, 32, ok, ok, ok, None) == 2
+    assert L.qlin_quantize_int4_group(ok, 8, 64, 32, ok, ok, ok, None) == 2
+    q96 = _qw(fmt=2, block=32, dq=0, d_out=16, d_in=96)
+    assert L.qlin_fwd(ctypes.byref(q96), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big,
+                      None) == 2
+    # QA-LoRA merge: INT4 weights only, rank 1..128, outputs aligned
+    q4 = _qw(fmt=2, block=32, dq=0, d_out=64, d_in=1024)
+    assert L.qlin_qa_merge(ctypes.byref(qw), ok, ok, 16, 2.0, ok, None) == 5
+    assert L.qlin_qa_merge(ctypes.byref(q4), ok, ok, 0, 2.0, ok, None) == 2
+    assert L.qlin_qa_merge(ctypes.byref(q4), ok, ok, 16, float("inf"), ok, None) == 2
+    assert L.qlin_qa_merge(ctypes.byref(q4), ok, None, 16, 2.0, ok, None) == 1
+    assert L.qlin_qa_merge(ctypes.byref(q4), ok, ok, 16, 2.0, bad, None) == 3
+    # profiling hook: host only
+    assert L.qlin_profile_next_launch(b"k_fwd_gemm", None, None) == 1
+    assert L.qlin_profile_next_launch(b"k" * 64, ok, ok) == 2
+    assert L.qlin_profile_next_launch(None, None, None) == 0
     # dequant helper
     assert L.qlin_dequant_bf16(ctypes.byref(qw), None, None) == 1
     assert L.qlin_nf4_codebook(None) == 1

@@ -263,3 +263,150 @@ def test_qa_merge_folds_adapter_into_zero_points(oracle):
     # average pooling would not fold the same way: the fold would be s B A / G
     assert oracle.rel_fro(x @ (alpha * q + np.repeat(oracle.f16_bits_to_f32(zp) + s * (B @ A) / G,
                                                       G, axis=1)).T, y_adapted) > 1e-3
+
+
+# ------------------------------------------- INT4 rounding in exact rationals
+
+
+def _int4_ref_codes(w, alpha, beta):
+    """clamp(round_half_even((w - beta)/alpha), 0, 15) in rationals; 0 if alpha = 0."""
+    from fractions import Fraction
+
+    from tests.exact_round import round_half_even_int
+    a = Fraction(float(alpha))
+    if a == 0:
+        return 0
+    v = round_half_even_int((Fraction(float(w)) - Fraction(float(beta))) / a)
+    return min(max(v, 0), 15)
+
+
+def _near_tie_groups():
+    """Groups whose min and max fix dyadic alpha and beta, and whose other
+    members sit exactly on the rounding boundaries beta + (k + 1/2) alpha or
+    one fp32 step either side of them."""
+    rows = []
+    for beta, alpha in ((-0.0625, 0.0078125), (-0.04, 0.005859375), (0.5, 0.0009765625),
+                        (-1.25, 0.1875)):
+        b16 = float(np.float16(beta))
+        a16 = float(np.float16(alpha))
+        ties = np.array([b16 + (k + 0.5) * a16 for k in range(15)], np.float32)
+        assert np.array_equal(ties.astype(np.float64),
+                              np.array([b16 + (k + 0.5) * a16 for k in range(15)]))
+        lo, hi = np.float32(b16), np.float32(b16 + 15 * a16)
+        for variant in (ties, np.nextafter(ties, np.float32(np.inf)),
+                        np.nextafter(ties, np.float32(-np.inf))):
+            g = np.full(32, lo, np.float32)
+            g[1] = hi
+            g[2:17] = variant
+            g[17:32] = variant
+            rows.append(g)
+    return np.stack(rows).reshape(-1, 64)
+
+
+def test_int4_codes_are_the_exact_nearest_integer(oracle):
+    """Random groups plus constructed exact ties and one-ulp near-ties: every
+    code is the rational round-half-even of (w - beta)/alpha, clamped."""
+    rng = np.random.default_rng(22)
+    W = np.concatenate([(rng.standard_normal((16, 256)) * 0.02).astype(np.float32).reshape(-1, 64),
+                        _near_tie_groups()])
+    codes, sc, zp = oracle.quantize_int4_group(W, 32)
+    q = oracle.unpack_nibbles(codes)
+    al = oracle.f16_bits_to_f32(sc)
+    be = oracle.f16_bits_to_f32(zp)
+    for n in range(W.shape[0]):
+        for k in range(W.shape[1]):
+            g = k // 32
+            assert q[n, k] == _int4_ref_codes(W[n, k], al[n, g], be[n, g]), (n, k)
+
+
+def test_int4_exact_ties_round_half_to_even(oracle):
+    g = _near_tie_groups()[:1]          # first group pair: members 2..16 are exact ties
+    codes, sc, zp = oracle.quantize_int4_group(g, 32)
+    q = oracle.unpack_nibbles(codes)[0]
+    assert q[0] == 0 and q[1] == 15
+    assert q[2:17].tolist() == [k if k % 2 == 0 else k + 1 for k in range(15)]
+
+
+def test_int4_pin_rejects_plausible_other_rules(oracle):
+    """The exact pins have teeth: the fp32 chain fl32(fl32(w - beta)/alpha)
+    with round-half-even, and the float64 quotient with round-half-up, each
+    give a different code somewhere on the near-tie groups."""
+    W = _near_tie_groups()
+    codes, sc, zp = oracle.quantize_int4_group(W, 32)
+    q = oracle.unpack_nibbles(codes).reshape(W.shape)
+    al = np.repeat(oracle.f16_bits_to_f32(sc), 32, axis=1)
+    be = np.repeat(oracle.f16_bits_to_f32(zp), 32, axis=1)
+    chain = np.clip(np.rint(((W - be).astype(np.float32) / al).astype(np.float32)), 0, 15)
+    half_up = np.clip(np.floor((W.astype(np.float64) - be) / al + 0.5), 0, 15)
+    assert np.any(chain != q)
+    assert np.any(half_up != q)
+
+
+def test_int4_scale_is_the_exactly_rounded_range_over_15(oracle):
+    """alpha = RN16((max - min)/15) in exact rationals: random groups, groups
+    whose fp64 difference is inexact (tiny min against a large max), and
+    groups whose quotient is exactly an fp16 rounding boundary (ties to the
+    even significand)."""
+    from fractions import Fraction
+
+    from tests.exact_round import FP16, round_rne
+    rng = np.random.default_rng(23)
+    lo = (rng.standard_normal(3000) * 0.05).astype(np.float32)
+    hi = (lo + np.abs(rng.standard_normal(3000)) * 0.1).astype(np.float32)
+    # inexact float64 differences
+    lo_x = np.array([-1e-30, 1e-30, -3e-25, 2.5e-38], np.float32)
+    hi_x = np.array([1.0, 7.5, 0.33, 1000.0], np.float32)
+    # exact fp16 boundaries: (hi - lo)/15 = midpoint of two neighbouring fp16
+    hs = np.float16(rng.uniform(1e-4, 10.0, 200))
+    mid = (hs.astype(np.float64) + np.nextafter(hs, np.float16(np.inf)).astype(np.float64)) / 2
+    lo_t = np.zeros(200, np.float32)
+    hi_t = (15 * mid).astype(np.float32)
+    assert np.array_equal(hi_t.astype(np.float64), 15 * mid)
+    L = np.concatenate([lo, lo_x, lo_t])
+    H = np.concatenate([hi, hi_x, hi_t])
+    got = oracle.f16_bits_to_f32(oracle.int4_group_scale(L, H))
+    for i in range(L.size):
+        exact = (Fraction(float(H[i])) - Fraction(float(L[i]))) / 15
+        assert Fraction(float(got[i])) == round_rne(exact, FP16), (float(L[i]), float(H[i]))
+    # and the boundary cases really are ties that went to the even neighbour
+    bits = oracle.int4_group_scale(lo_t, hi_t)
+    assert np.all(bits & 1 == 0)
+
+
+# ------------------------------------------------ QA-LoRA merge in fp16
+
+
+def test_qa_merge_f16_is_the_exactly_rounded_sum(oracle):
+    """beta' = RN16(beta + s sum_j B[n][j] A[j][g]) in exact rationals, on a
+    random pooled adapter and on constructed sums that land exactly on an fp16
+    rounding boundary (ties to the even significand)."""
+    from fractions import Fraction
+
+    from quantized_base_rank_amd.inputs import bf16_bits
+    from tests.exact_round import FP16, round_rne
+    rng = np.random.default_rng(31)
+    n, G, r, s = 24, 12, 8, np.float32(2.0)
+    zp = oracle.f32_to_f16_bits((rng.standard_normal((n, G)) * 0.03).astype(np.float32))
+    A = bf16_bits(rng.uniform(-0.2, 0.2, (r, G)).astype(np.float32))
+    B = bf16_bits((rng.standard_normal((n, r)) * 0.01).astype(np.float32))
+    got = oracle.qa_merge_zero_f16(zp, A, B, s)
+    Af, Bf = oracle.bf16_bits_to_f64(A), oracle.bf16_bits_to_f64(B)
+    beta = oracle.f16_bits_to_f32(zp)
+    for i in range(n):
+        for g in range(G):
+            exact = Fraction(float(beta[i, g])) + sum(
+                Fraction(float(s)) * Fraction(float(Bf[i, j])) * Fraction(float(Af[j, g]))
+                for j in range(r))
+            want = round_rne(exact, FP16)
+            assert Fraction(float(oracle.f16_bits_to_f32(got[i, g]))) == want, (i, g)
+    # ties: 1 + 2^-11 lies half-way between 1 and 1 + 2^-10 (even: 1);
+    # (1 + 2^-10) + 2^-11 half-way between it and 1 + 2^-9 (even: the latter)
+    zt = oracle.f32_to_f16_bits(np.array([[1.0, 1.0 + 2.0 ** -10]], np.float32))
+    At = bf16_bits(np.array([[2.0 ** -6, 2.0 ** -6]], np.float32))
+    Bt = bf16_bits(np.array([[2.0 ** -5]], np.float32))
+    tie = oracle.qa_merge_zero_f16(zt, At, Bt, np.float32(1.0))
+    assert oracle.f16_bits_to_f32(tie).tolist() == [[1.0, 1.0 + 2.0 ** -9]]
+    # and the float64 merge it rounds agrees to within half an fp16 step
+    ref = oracle.qa_merge_zero(zp, Af, Bf, float(s))
+    back = oracle.f16_bits_to_f32(got).astype(np.float64)
+    assert np.all(np.abs(back - ref) <= np.abs(ref) * 2.0 ** -11 + 2.0 ** -25)

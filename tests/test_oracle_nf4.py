@@ -230,7 +230,7 @@ def test_double_quant_codes_and_bound(oracle):
     s2b = np.repeat(s2, 256).astype(np.float64)
     assert np.all(np.abs(ahat - a) <= s2b / 254 * (1 + 1e-6))
     top = q == 127
-    assert np.all(np.abs(ahat[top] - s2b[top]) <= 2 * np.spacing(s2b[top].astype(np.float32)))
+    assert np.array_equal(ahat[top], s2b[top])  # the group maximum comes back exactly
 
 
 def test_double_quant_partial_last_group_and_zero_group(oracle):
@@ -276,3 +276,45 @@ def test_storage_accounting_matches_page_figures(oracle):
     assert n65 * bits_nf4 / 8 / 1e9 < fig["single_gpu_GB"]["value"]
     # LQ-LoRA's 70B at 2.85 bits/param fits its stated footprint
     assert 70e9 * fig["lqlora_70b_avg_bits"]["value"] / 8 / 1e9 < fig["lqlora_70b_GB"]["value"]
+
+
+def _dq_pairs():
+    """Random 8-bit codes against second-level constants over many binades,
+    plus edge values: powers of two, the largest fp32, fp32 subnormals."""
+    rng = np.random.default_rng(21)
+    n = 6000
+    q = rng.integers(0, 128, n)
+    s2 = (rng.uniform(1.0, 2.0, n) * 2.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    edge_s2 = np.array([1.0, 2.0 ** -20, 3.4028235e38, 1e-40, 1.17549435e-38, 0.0,
+                        np.nextafter(np.float32(1), np.float32(2))], np.float32)
+    q = np.concatenate([q, np.repeat(np.arange(128), edge_s2.size)])
+    s2 = np.concatenate([s2, np.tile(edge_s2, 128)]).astype(np.float32)
+    return q.astype(np.int8), s2
+
+
+def test_dq_reconstruction_is_the_exactly_rounded_quotient(oracle):
+    """a_hat = RN32(q s2 / 127) in exact rationals, ties to even [R5]; every
+    code 127 reconstructs s2 itself."""
+    from tests.exact_round import FP32, round_rne
+    q, s2 = _dq_pairs()
+    got = oracle.dq_absmax(q, s2, 1)
+    for i in range(q.size):
+        exact = Fraction(int(q[i])) * Fraction(float(s2[i])) / 127
+        assert Fraction(float(got[i])) == round_rne(exact, FP32), (int(q[i]), float(s2[i]))
+    top = q == 127
+    assert np.array_equal(got[top].view(np.uint32), s2[top].view(np.uint32))
+
+
+def test_dq_pin_rejects_plausible_other_rules(oracle):
+    """The exact-rounding pin above has teeth: rounding twice in fp32 (either
+    by a fp32 step 1/127 or by a fp32 product then a quotient) differs from it
+    on the same sample, so a mutated oracle would fail that pin."""
+    from tests.exact_round import FP32, round_rne
+    q, s2 = _dq_pairs()
+    step = (s2 * np.float32(1.0 / 127.0)).astype(np.float32)
+    alt1 = (q.astype(np.float32) * step).astype(np.float32)
+    alt2 = ((q.astype(np.float32) * s2).astype(np.float32) / np.float32(127)).astype(np.float32)
+    ref = np.array([float(round_rne(Fraction(int(a)) * Fraction(float(b)) / 127, FP32))
+                    for a, b in zip(q, s2)], np.float64)
+    assert np.any(alt1.astype(np.float64) != ref)
+    assert np.any(alt2.astype(np.float64) != ref)
