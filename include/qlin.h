@@ -203,6 +203,30 @@ int qlin_fwd(const qlin_qweight *w, const uint16_t *x, int64_t M, const uint16_t
              void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Forward pass that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, or
+ * harnesses that forbid hipMalloc.  Same arguments and results as qlin_fwd
+ * (bit-identical: the same kernels), without the workspace: the library
+ * uses its own 64 MiB device array (one per GPU it runs on, held until the
+ * process ends) for ticket counters, u and split partial sums.
+ *   - Returns QLIN_E_WORKSPACE, before any HIP call, when the layer needs
+ *     more than that array holds (64 KiB of counters + M*r*4 bytes of u +
+ *     the forward's split partials; e.g. the 4096 x 11008 INT4 layer at
+ *     M = 2048 does not fit, every few-token layer does).
+ *   - The first call on each GPU looks up the array's device address and
+ *     zeroes its counters with a kernel on `stream`; make that first call
+ *     outside graph capture.  Every completed call leaves the counters at
+ *     zero again.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (different streams, or threads) race and must not be
+ *     issued.
+ * Asynchronous on `stream`.
+ */
+int qlin_fwd_noalloc(const qlin_qweight *w, const uint16_t *x, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int32_t r, float s, int32_t pool, uint16_t *y,
+                     float *u_out, hipStream_t stream);
+
+/*
  * Backward pass: gradients of <dY, y> into the input and the adapter.  The
  * frozen weight gets none.  [QLoRA "The QLoRA recipe" stage 3 and the code
  * sketch's closing note; QA-LoRA abstract]

@@ -19,7 +19,7 @@ from ._lib import (EXPORTS, LIB_PATH, QLIN_FMT_INT4_GROUP, QLIN_FMT_NF4, QlinErr
 
 __all__ = [
     "QWeight", "QlinError", "qlin_nf4_codebook", "qlin_quantize_nf4",
-    "qlin_quantize_int4_group", "qlin_workspace_bytes", "qlin_fwd", "qlin_bwd",
+    "qlin_quantize_int4_group", "qlin_workspace_bytes", "qlin_fwd", "qlin_fwd_noalloc", "qlin_bwd",
     "qlin_dequant_bf16", "qlin_qa_merge", "qlin_profile_next_launch", "EXPORTS", "LIB_PATH",
 ]
 
@@ -159,6 +159,29 @@ def qlin_fwd(w: QWeight, x, A, B, r: int, s: float, pool: int = 1, y=None, u_out
     check(lib().qlin_fwd(ctypes.byref(s_), x.data_ptr(), M, _ptr(A), _ptr(B), r,
                          float(s), pool, y.data_ptr(), _ptr(u_out), ws.data_ptr(), ws.numel(),
                          _stream(dev)), "qlin_fwd")
+    return y, u_out
+
+
+def qlin_fwd_noalloc(w: QWeight, x, A, B, r: int, s: float, pool: int = 1, y=None, u_out=None,
+                     want_u: bool = True):
+    """qlin_fwd without a workspace (the library's own device array; see
+    include/qlin.h).  Output tensors are allocated here unless passed in."""
+    torch = _torch()
+    M = x.shape[0]
+    dev = x.device
+    _need(x, torch.bfloat16, (M, w.d_in), "x")
+    if r > 0:
+        _need(A, torch.bfloat16, (r, w.d_in // pool), "A")
+        _need(B, torch.bfloat16, (w.d_out, r), "B")
+    else:
+        want_u = False
+    if y is None:
+        y = torch.empty((M, w.d_out), dtype=torch.bfloat16, device=dev)
+    if u_out is None and want_u:
+        u_out = torch.empty((M, r), dtype=torch.float32, device=dev)
+    s_ = w.struct()
+    check(lib().qlin_fwd_noalloc(ctypes.byref(s_), x.data_ptr(), M, _ptr(A), _ptr(B), r, float(s),
+                                 pool, y.data_ptr(), _ptr(u_out), _stream(dev)), "qlin_fwd_noalloc")
     return y, u_out
 
 

@@ -19,6 +19,7 @@ EXPORTS = (
     "qlin_quantize_int4_group",
     "qlin_workspace_bytes",
     "qlin_fwd",
+    "qlin_fwd_noalloc",
     "qlin_bwd",
     "qlin_dequant_bf16",
     "qlin_qa_merge",
@@ -65,6 +66,7 @@ def lib() -> ctypes.CDLL:
         "qlin_quantize_int4_group": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, vp, vp]),
         "qlin_workspace_bytes": (sz, [qp, i64, i32, i32]),
         "qlin_fwd": (ctypes.c_int, [qp, vp, i64, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
+        "qlin_fwd_noalloc": (ctypes.c_int, [qp, vp, i64, vp, vp, i32, f32, i32, vp, vp, vp]),
         "qlin_bwd": (ctypes.c_int,
                      [qp, vp, i64, vp, vp, i32, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "qlin_dequant_bf16": (ctypes.c_int, [qp, vp, vp]),

@@ -311,6 +311,62 @@ int check_fwd_args(const qlin_qweight* w, const uint16_t* x, int64_t M, const ui
   return QLIN_OK;
 }
 
+// ------------------------------------------------- forward without allocation
+// qlin_fwd_noalloc runs qlin_fwd's kernels on a file-scope device array
+// instead of a caller workspace.  Layout: [0, 64 KiB) the ticket counters
+// (the same fixed region as in a workspace), then u (when not returned) and
+// the split partial sums of the forward kernels only.
+constexpr size_t kScratchBytes = size_t{64} << 20;  // per device, held until exit
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct FwdScratch {
+  size_t off_u = 0, off_partial = 0, total = 0;
+};
+
+FwdScratch fwd_scratch_layout(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool,
+                              const Plan& p) {
+  const int64_t N = w->d_out, K = w->d_in;
+  int64_t partial = 0;
+  if (pool == 1 && !fwd_fuses_u(p, r, pool)) partial = nt_partial_floats(M, p.nt_splits_u);
+  partial = std::max<int64_t>(partial, p.small ? gemv_fwd_partial_floats(N, K)
+                                               : fwd_gemm_partial_floats(M, N, p.fwd_splits));
+  FwdScratch f;
+  size_t off = kCounterBytes;
+  f.off_u = off;       off = align256(off + static_cast<size_t>(M) * (r > 0 ? r : 0) * sizeof(float));
+  f.off_partial = off; off = align256(off + static_cast<size_t>(partial) * sizeof(float));
+  f.total = off;
+  return f;
+}
+
+__global__ void k_zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Device address of `scratch` on the current device.  At the first call on
+// a device: looks the address up (the host-side name of a __device__ array
+// is not a device address) and zeroes the counter region with a kernel on
+// `stream`, ahead of that call's own kernels.
+int scratch_ptr(hipStream_t stream, uint8_t** out) {
+  static std::mutex m;
+  static uint8_t* ptr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> g(m);
+  int dev = 0;
+  QLIN_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return QLIN_E_UNSUPPORTED;
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    QLIN_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    constexpr int n = static_cast<int>(kCounterBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(p), n);
+    QLIN_TRY(hipGetLastError());
+    ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = ptr[dev];
+  return QLIN_OK;
+}
+
 }  // namespace
 
 }  // namespace qlin
@@ -393,6 +449,23 @@ int qlin_fwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   if (!aligned16(workspace)) return QLIN_E_ALIGN;
   return fwd_core(w, x, M, A, B, r, s, pool, y, u_out, p, ws_at<float>(workspace, p.off_u),
                   ws_at<float>(workspace, p.off_partial), ws_at<uint32_t>(workspace, p.off_counters),
+                  stream);
+}
+
+int qlin_fwd_noalloc(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float s, int32_t pool, uint16_t* y,
+                     float* u_out, hipStream_t stream) {
+  const int st = check_fwd_args(w, x, M, A, B, r, s, pool, y, u_out);
+  if (st != QLIN_OK) return st;
+  const Plan p = make_plan(w, M, r, pool);
+  if (!p.fits) return QLIN_E_SHAPE;
+  const FwdScratch f = fwd_scratch_layout(w, M, r, pool, p);
+  if (f.total > kScratchBytes) return QLIN_E_WORKSPACE;
+  uint8_t* base = nullptr;
+  const int sst = scratch_ptr(stream, &base);
+  if (sst != QLIN_OK) return sst;
+  return fwd_core(w, x, M, A, B, r, s, pool, y, u_out, p, reinterpret_cast<float*>(base + f.off_u),
+                  reinterpret_cast<float*>(base + f.off_partial), reinterpret_cast<uint32_t*>(base),
                   stream);
 }
 
