@@ -38,8 +38,11 @@
  *     synchronisation.  The two quantizers synchronise `stream` and report
  *     non-finite input.
  *   - Outputs are overwritten, never accumulated into.
- *   - Calls keep no global mutable state: concurrent calls on different
- *     streams are safe provided they do not share a workspace.
+ *   - State the library keeps, per process: the quantizers' non-finite flag
+ *     word (one per device; quantizer calls take turns on a mutex), the
+ *     profiling hook (qlin_profile_next_launch) and the device array of
+ *     qlin_fwd_noalloc.  Otherwise concurrent calls on different streams are
+ *     safe provided they do not share a workspace.
  */
 #ifndef QLIN_H_
 #define QLIN_H_
@@ -69,8 +72,11 @@ typedef enum {
 /* Packed weight formats. */
 typedef enum {
   QLIN_FMT_NF4 = 1,        /* NormalFloat-4, blockwise absmax [QLoRA NF4, DQ]  */
-  QLIN_FMT_INT4_GROUP = 2  /* asymmetric INT4, per-group fp16 scale and zero
+  QLIN_FMT_INT4_GROUP = 2, /* asymmetric INT4, per-group fp16 scale and zero
                               [QA-LoRA abstract]                              */
+  QLIN_FMT_NF = 3          /* NormalFloat-k, k = 2, 3 or 4 bits, blocks of 32,
+                              64, 128 or 256, bit-plane codes [LQ-LoRA
+                              abstract: bit-width and block size per matrix] */
 } qlin_format;
 
 /*
@@ -96,14 +102,25 @@ typedef enum {
  *         (n, k) with q = its index decodes to
  *             bf16( fl32( scale[n][k/32] * q + zero[n][k/32] ) ).
  *         [QA-LoRA abstract: group-wise quantization]
+ * NF (bits = k in 2..4, block in {32, 64, 128, 256}): codes =
+ *         uint8[d_out][d_in*k/8] as bit planes: every run of 32 elements of
+ *         a row fills k little-endian 32-bit words, word p holding bit p of
+ *         element i in its bit i.  Element (n, k) belongs to block
+ *         b = (n*d_in + k)/block and decodes to bf16(fl32(c[idx] * a_hat_b))
+ *         with c the 2^k levels of qlin_nf_codebook(k) and a_hat_b as for
+ *         NF4 (absmax, absmax2, dq_block 0 or 256).  qlin_fwd / qlin_bwd
+ *         first transcode such a weight, on their stream, into their
+ *         workspace (4-bit indices plus an fp32 scale per 32 elements:
+ *         d_in*d_out*(1/2 + 1/8) bytes), then run the same kernels.
+ *         [LQ-LoRA abstract; QLoRA "Innovation 1", "Innovation 2"]
  */
 typedef struct {
   int32_t format;          /* qlin_format                                    */
-  int32_t block;           /* NF4: 64; INT4: group size, 32                  */
+  int32_t block;           /* NF4: 64; INT4: group size, 32; NF: 32..256     */
   int32_t dq_block;        /* NF4: 256 or 0; INT4: 0                         */
-  int32_t reserved;        /* must be 0                                      */
+  int32_t bits;            /* NF: 2, 3 or 4; NF4 and INT4: 0                 */
   int64_t d_out, d_in;     /* d_out % 16 == 0; d_in % 64 == 0 (both formats) */
-  const uint8_t *codes;    /* uint8[d_out][d_in/2]                           */
+  const uint8_t *codes;    /* uint8[d_out][d_in/2] (NF: [d_out][d_in*bits/8]) */
   const void *absmax;      /* NF4: int8[n_blocks] (dq) or float[n_blocks]    */
   const float *absmax2;    /* NF4 with dq: float[ceil(n_blocks/dq_block)]    */
   const uint16_t *scale;   /* INT4: fp16[d_out][d_in/group]                  */
@@ -146,6 +163,37 @@ int qlin_nf4_codebook(float out[16]);
 int qlin_quantize_nf4(const float *W, int64_t d_out, int64_t d_in, int32_t block,
                       int32_t dq_block, uint8_t *codes, void *absmax, float *absmax2,
                       hipStream_t stream);
+
+/*
+ * The 2^bits NormalFloat levels (bits = 2, 3, 4) as fp32, ascending, into
+ * `out` (HOST memory, 2^bits floats): the NF4 construction with 2^(bits-1)
+ * levels above and 2^(bits-1) - 1 below an exact zero, the outermost at
+ * probability 1 - 1/2^(bits+1); bits = 4 gives qlin_nf4_codebook's levels.
+ * [QLoRA "Innovation 1: 4-bit NormalFloat (NF4)"; LQ-LoRA abstract]
+ * QLIN_E_NULL for out == NULL, QLIN_E_UNSUPPORTED for other bit counts.
+ */
+int qlin_nf_codebook(int32_t bits, float *out);
+
+/*
+ * NormalFloat-k blockwise quantization (format QLIN_FMT_NF).  [LQ-LoRA
+ * abstract: per-matrix bit-width and block size; QLoRA "Background: what is
+ * quantization?", "Innovation 2: Double Quantization"]
+ *
+ *   W        fp32[d_out][d_in] (device);  d_out % 16 == 0; d_in % 64 == 0
+ *            and d_in % block == 0
+ *   bits     2, 3 or 4;  block 32, 64, 128 or 256;  dq_block 0 or 256
+ *   codes    uint8[d_out][d_in*bits/8] bit planes (output);  absmax and
+ *            absmax2 as for qlin_quantize_nf4 with n_blocks = d_out*d_in/block
+ *
+ * Same rules as qlin_quantize_nf4 with the 2^bits levels of
+ * qlin_nf_codebook(bits): nearest level of w/absmax_b (exact comparison,
+ * ties to the lower index, an all-zero block to the zero level), 8-bit
+ * double quantization of the constants.  Synchronous; QLIN_E_NONFINITE as
+ * for qlin_quantize_nf4.
+ */
+int qlin_quantize_nf(const float *W, int64_t d_out, int64_t d_in, int32_t bits, int32_t block,
+                     int32_t dq_block, uint8_t *codes, void *absmax, float *absmax2,
+                     hipStream_t stream);
 
 /*
  * Group-wise asymmetric INT4 quantization.  [QA-LoRA abstract]

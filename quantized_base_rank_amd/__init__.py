@@ -14,11 +14,12 @@ from typing import Optional
 
 import numpy as np
 
-from ._lib import (EXPORTS, LIB_PATH, QLIN_FMT_INT4_GROUP, QLIN_FMT_NF4, QlinError,
+from ._lib import (EXPORTS, LIB_PATH, QLIN_FMT_INT4_GROUP, QLIN_FMT_NF, QLIN_FMT_NF4, QlinError,
                    QWeightStruct, check, lib)
 
 __all__ = [
-    "QWeight", "QlinError", "qlin_nf4_codebook", "qlin_quantize_nf4",
+    "QWeight", "QlinError", "qlin_nf4_codebook", "qlin_quantize_nf4", "qlin_nf_codebook",
+    "qlin_quantize_nf",
     "qlin_quantize_int4_group", "qlin_workspace_bytes", "qlin_fwd", "qlin_fwd_noalloc", "qlin_bwd",
     "qlin_dequant_bf16", "qlin_qa_merge", "qlin_profile_next_launch", "EXPORTS", "LIB_PATH",
 ]
@@ -58,9 +59,10 @@ class QWeight:
     absmax2: object = None        # NF4 dq: float32 [ceil(n_blocks/dq_block)]
     scale: object = None          # INT4: fp16 [d_out][d_in/group]
     zero: object = None
+    bits: int = 0                 # NF: 2, 3 or 4
 
     def struct(self) -> QWeightStruct:
-        return QWeightStruct(self.format, self.block, self.dq_block, 0, self.d_out, self.d_in,
+        return QWeightStruct(self.format, self.block, self.dq_block, self.bits, self.d_out, self.d_in,
                              _ptr(self.codes), _ptr(self.absmax), _ptr(self.absmax2),
                              _ptr(self.scale), _ptr(self.zero))
 
@@ -96,6 +98,30 @@ def qlin_quantize_nf4(W, block: int = 64, dq_block: int = 256) -> QWeight:
                                   absmax.data_ptr(), _ptr(absmax2), _stream(dev)),
           "qlin_quantize_nf4")
     return QWeight(QLIN_FMT_NF4, block, dq_block, d_out, d_in, codes, absmax, absmax2)
+
+
+def qlin_nf_codebook(bits: int) -> np.ndarray:
+    out = (ctypes.c_float * 16)()
+    check(lib().qlin_nf_codebook(bits, out), "qlin_nf_codebook")
+    return np.frombuffer(out, dtype=np.float32)[: 1 << bits].copy()
+
+
+def qlin_quantize_nf(W, bits: int, block: int, dq_block: int = 256) -> QWeight:
+    torch = _torch()
+    d_out, d_in = W.shape
+    _need(W, torch.float32, (d_out, d_in), "W")
+    nb = d_out * d_in // block
+    dev = W.device
+    codes = torch.empty((d_out, d_in * bits // 8), dtype=torch.uint8, device=dev)
+    if dq_block:
+        absmax = torch.empty(nb, dtype=torch.int8, device=dev)
+        absmax2 = torch.empty(-(-nb // dq_block), dtype=torch.float32, device=dev)
+    else:
+        absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+        absmax2 = None
+    check(lib().qlin_quantize_nf(W.data_ptr(), d_out, d_in, bits, block, dq_block, codes.data_ptr(),
+                                 absmax.data_ptr(), _ptr(absmax2), _stream(dev)), "qlin_quantize_nf")
+    return QWeight(QLIN_FMT_NF, block, dq_block, d_out, d_in, codes, absmax, absmax2, bits=bits)
 
 
 def qlin_quantize_int4_group(W, group: int = 32) -> QWeight:

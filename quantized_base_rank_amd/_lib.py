@@ -11,11 +11,14 @@ LIB_PATH = os.path.join(HERE, "libqlin.so")
 QLIN_OK = 0
 QLIN_FMT_NF4 = 1
 QLIN_FMT_INT4_GROUP = 2
+QLIN_FMT_NF = 3
 
 #: every symbol include/qlin.h declares
 EXPORTS = (
     "qlin_nf4_codebook",
     "qlin_quantize_nf4",
+    "qlin_nf_codebook",
+    "qlin_quantize_nf",
     "qlin_quantize_int4_group",
     "qlin_workspace_bytes",
     "qlin_fwd",
@@ -33,7 +36,7 @@ class QWeightStruct(ctypes.Structure):
         ("format", ctypes.c_int32),
         ("block", ctypes.c_int32),
         ("dq_block", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
         ("d_out", ctypes.c_int64),
         ("d_in", ctypes.c_int64),
         ("codes", ctypes.c_void_p),
@@ -64,6 +67,8 @@ def lib() -> ctypes.CDLL:
         "qlin_nf4_codebook": (ctypes.c_int, [vp]),
         "qlin_quantize_nf4": (ctypes.c_int, [vp, i64, i64, i32, i32, vp, vp, vp, vp]),
         "qlin_quantize_int4_group": (ctypes.c_int, [vp, i64, i64, i32, vp, vp, vp, vp]),
+        "qlin_nf_codebook": (ctypes.c_int, [i32, vp]),
+        "qlin_quantize_nf": (ctypes.c_int, [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]),
         "qlin_workspace_bytes": (sz, [qp, i64, i32, i32]),
         "qlin_fwd": (ctypes.c_int, [qp, vp, i64, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
         "qlin_fwd_noalloc": (ctypes.c_int, [qp, vp, i64, vp, vp, i32, f32, i32, vp, vp, vp]),

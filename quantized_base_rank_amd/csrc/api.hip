@@ -34,13 +34,20 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QLIN_OK : QLIN_E_HIP; }
 // alignment only; the library never dereferences device memory on the host).
 int check_weight(const qlin_qweight* w) {
   if (w == nullptr) return QLIN_E_NULL;
-  if (w->reserved != 0) return QLIN_E_UNSUPPORTED;
   if (w->d_out < 1 || w->d_in < 1) return QLIN_E_SHAPE;
   if (w->d_out % 16 != 0) return QLIN_E_SHAPE;
   if (w->codes == nullptr) return QLIN_E_NULL;
   if (!aligned16(w->codes)) return QLIN_E_ALIGN;
-  if (w->format == QLIN_FMT_NF4) {
-    if (w->block != 64) return QLIN_E_UNSUPPORTED;
+  if (w->format == QLIN_FMT_NF4 || w->format == QLIN_FMT_NF) {
+    if (w->format == QLIN_FMT_NF4) {
+      if (w->bits != 0) return QLIN_E_UNSUPPORTED;
+      if (w->block != 64) return QLIN_E_UNSUPPORTED;
+    } else {
+      if (w->bits < 2 || w->bits > 4) return QLIN_E_UNSUPPORTED;
+      if (w->block != 32 && w->block != 64 && w->block != 128 && w->block != 256)
+        return QLIN_E_UNSUPPORTED;
+      if (w->d_in % w->block != 0) return QLIN_E_SHAPE;
+    }
     if (w->dq_block != 0 && w->dq_block != 256) return QLIN_E_UNSUPPORTED;
     if (w->d_in % 64 != 0) return QLIN_E_SHAPE;
     if (w->absmax == nullptr) return QLIN_E_NULL;
@@ -52,6 +59,7 @@ int check_weight(const qlin_qweight* w) {
     return QLIN_OK;
   }
   if (w->format == QLIN_FMT_INT4_GROUP) {
+    if (w->bits != 0) return QLIN_E_UNSUPPORTED;
     if (w->block != 32) return QLIN_E_UNSUPPORTED;
     if (w->dq_block != 0) return QLIN_E_UNSUPPORTED;
     if (w->d_in % 64 != 0) return QLIN_E_SHAPE;
@@ -85,11 +93,27 @@ WeightView make_view(const qlin_qweight* w) {
   v.N = w->d_out;
   v.K = w->d_in;
   v.dq = w->dq_block != 0 ? 1 : 0;
-  nf4_levels(v.cb.c);
+  if (w->format == QLIN_FMT_NF)
+    nf_levels(w->bits, v.cb.c);  // (the rest of the 16 entries stay zero)
+  else
+    nf4_levels(v.cb.c);
   return v;
 }
 
-int fmt_of(const qlin_qweight* w) { return w->format == QLIN_FMT_NF4 ? kFmtNF4 : kFmtINT4; }
+// The layer kernels' format: NormalFloat-k weights are read through the
+// per-call transcoded form (kFmtNFG).
+int fmt_of(const qlin_qweight* w) {
+  return w->format == QLIN_FMT_NF4 ? kFmtNF4 : (w->format == QLIN_FMT_NF ? kFmtNFG : kFmtINT4);
+}
+
+NfTable nf_table(int bits) {
+  NfTable t{};
+  nf_levels(bits, t.c);
+  const int n = 1 << bits;
+  for (int i = 0; i + 1 < n; ++i)
+    t.mid[i] = (static_cast<double>(t.c[i]) + static_cast<double>(t.c[i + 1])) / 2.0;
+  return t;
+}
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -103,6 +127,8 @@ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > h
 constexpr size_t kCounterBytes = size_t{64} << 10;
 constexpr int64_t kCounterWords = static_cast<int64_t>(kCounterBytes / sizeof(uint32_t));
 
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
 // Work split of the reductions and the workspace layout for one layer shape.
 struct Plan {
   bool small = false;
@@ -112,10 +138,16 @@ struct Plan {
   int tn2_splits_dB = 1, tn2_splits_dA = 1;
   int gf_splits = 1, gd_splits = 1;
   size_t off_counters = 0, off_u = 0, off_du = 0, off_Bt = 0, off_At = 0, off_P = 0,
-         off_z = 0, off_partial = 0, total = 0;
+         off_z = 0, off_partial = 0, off_tc = 0, total = 0;
 };
 
-size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+// Bytes of the transcoded NormalFloat-k weight (4-bit indices, then the
+// low and high 16-bit planes of the per-32 scales); 0 for other formats.
+size_t transcode_bytes(const qlin_qweight* w) {
+  if (w->format != QLIN_FMT_NF) return 0;
+  const size_t n_el = static_cast<size_t>(w->d_out) * static_cast<size_t>(w->d_in);
+  return align256(n_el / 2) + 2 * align256(n_el / 32 * sizeof(uint16_t));
+}
 
 Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   Plan p;
@@ -169,8 +201,32 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.off_P = off;        off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
   p.off_z = off;        off = align256(off + (p.small ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
   p.off_partial = off;  off = align256(off + static_cast<size_t>(partial) * sizeof(float));
+  p.off_tc = off;       off += transcode_bytes(w);
   p.total = off;
   return p;
+}
+
+// The weight as the layer kernels read it.  NormalFloat-k weights are first
+// transcoded (on `stream`, into `tc`: transcode_bytes(w) bytes) to 4-bit
+// indices and per-32 fp32 scales; the levels stay in the view's codebook.
+int layer_view(const qlin_qweight* w, uint8_t* tc, hipStream_t stream, WeightView* out) {
+  WeightView v = make_view(w);
+  if (w->format == QLIN_FMT_NF) {
+    const size_t n_el = static_cast<size_t>(w->d_out) * static_cast<size_t>(w->d_in);
+    uint8_t* nib = tc;
+    uint16_t* lo = reinterpret_cast<uint16_t*>(tc + align256(n_el / 2));
+    uint16_t* hi = reinterpret_cast<uint16_t*>(tc + align256(n_el / 2) + align256(n_el / 32 * sizeof(uint16_t)));
+    QLIN_TRY(launch_transcode_nf(w->codes, w->absmax, w->absmax2, static_cast<int64_t>(n_el), w->bits,
+                                 w->block, w->dq_block != 0 ? 1 : 0, nib, lo, hi, stream));
+    v.codes = nib;
+    v.scale = lo;
+    v.zero = hi;
+    v.absmax = nullptr;
+    v.absmax2 = nullptr;
+    v.dq = 0;
+  }
+  *out = v;
+  return QLIN_OK;
 }
 
 // Runs one quantizer launch between clearing and reading back the device's
@@ -259,9 +315,11 @@ bool fwd_fuses_u(const Plan& p, int32_t r, int32_t pool) { return p.small && poo
 // counters, zero on entry and left at zero).
 int fwd_core(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
              const uint16_t* B, int32_t r, float s, int32_t pool, uint16_t* y, float* u_out,
-             const Plan& p, float* u_tmp, float* partial, uint32_t* counters,
+             const Plan& p, float* u_tmp, float* partial, uint32_t* counters, uint8_t* tc,
              hipStream_t stream) {
-  const WeightView v = make_view(w);
+  WeightView v;
+  const int vst = layer_view(w, tc, stream, &v);
+  if (vst != QLIN_OK) return vst;
   const int fmt = fmt_of(w);
   float* u = u_out != nullptr ? u_out : u_tmp;
   const bool adapter = r > 0 && s != 0.0f;
@@ -320,7 +378,7 @@ constexpr size_t kScratchBytes = size_t{64} << 20;  // per device, held until ex
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 struct FwdScratch {
-  size_t off_u = 0, off_partial = 0, total = 0;
+  size_t off_u = 0, off_partial = 0, off_tc = 0, total = 0;
 };
 
 FwdScratch fwd_scratch_layout(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool,
@@ -334,6 +392,7 @@ FwdScratch fwd_scratch_layout(const qlin_qweight* w, int64_t M, int32_t r, int32
   size_t off = kCounterBytes;
   f.off_u = off;       off = align256(off + static_cast<size_t>(M) * (r > 0 ? r : 0) * sizeof(float));
   f.off_partial = off; off = align256(off + static_cast<size_t>(partial) * sizeof(float));
+  f.off_tc = off;      off += transcode_bytes(w);
   f.total = off;
   return f;
 }
@@ -417,6 +476,35 @@ int qlin_quantize_nf4(const float* W, int64_t d_out, int64_t d_in, int32_t block
   });
 }
 
+int qlin_nf_codebook(int32_t bits, float* out) {
+  if (out == nullptr) return QLIN_E_NULL;
+  if (bits < 2 || bits > 4) return QLIN_E_UNSUPPORTED;
+  nf_levels(bits, out);
+  return QLIN_OK;
+}
+
+int qlin_quantize_nf(const float* W, int64_t d_out, int64_t d_in, int32_t bits, int32_t block,
+                     int32_t dq_block, uint8_t* codes, void* absmax, float* absmax2,
+                     hipStream_t stream) {
+  if (W == nullptr || codes == nullptr || absmax == nullptr) return QLIN_E_NULL;
+  if (dq_block != 0 && absmax2 == nullptr) return QLIN_E_NULL;
+  if (bits < 2 || bits > 4) return QLIN_E_UNSUPPORTED;
+  if (block != 32 && block != 64 && block != 128 && block != 256) return QLIN_E_UNSUPPORTED;
+  if (dq_block != 0 && dq_block != 256) return QLIN_E_UNSUPPORTED;
+  if (d_out < 1 || d_in < 1 || d_in % 64 != 0 || d_in % block != 0 || d_out % 16 != 0)
+    return QLIN_E_SHAPE;
+  if (d_out > (int64_t{1} << 40) / d_in) return QLIN_E_SHAPE;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax) ||
+      (dq_block != 0 && !aligned16(absmax2)))
+    return QLIN_E_ALIGN;
+  const NfTable tb = nf_table(bits);
+  const int64_t n_blocks = d_out * d_in / block;
+  return run_flagged(stream, [&](uint32_t* flag) {
+    return launch_quant_nf(W, n_blocks, bits, block, dq_block != 0 ? 1 : 0, tb, codes, absmax,
+                           absmax2, flag, stream);
+  });
+}
+
 int qlin_quantize_int4_group(const float* W, int64_t d_out, int64_t d_in, int32_t group,
                              uint8_t* codes, uint16_t* scale, uint16_t* zero, hipStream_t stream) {
   if (W == nullptr || codes == nullptr || scale == nullptr || zero == nullptr) return QLIN_E_NULL;
@@ -449,7 +537,7 @@ int qlin_fwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   if (!aligned16(workspace)) return QLIN_E_ALIGN;
   return fwd_core(w, x, M, A, B, r, s, pool, y, u_out, p, ws_at<float>(workspace, p.off_u),
                   ws_at<float>(workspace, p.off_partial), ws_at<uint32_t>(workspace, p.off_counters),
-                  stream);
+                  ws_at<uint8_t>(workspace, p.off_tc), stream);
 }
 
 int qlin_fwd_noalloc(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -466,7 +554,7 @@ int qlin_fwd_noalloc(const qlin_qweight* w, const uint16_t* x, int64_t M, const 
   if (sst != QLIN_OK) return sst;
   return fwd_core(w, x, M, A, B, r, s, pool, y, u_out, p, reinterpret_cast<float*>(base + f.off_u),
                   reinterpret_cast<float*>(base + f.off_partial), reinterpret_cast<uint32_t*>(base),
-                  stream);
+                  base + f.off_tc, stream);
 }
 
 int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -488,7 +576,9 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   if (!aligned16(workspace)) return QLIN_E_ALIGN;
 
   const int64_t N = w->d_out, K = w->d_in, G = K / pool;
-  const WeightView v = make_view(w);
+  WeightView v;
+  st = layer_view(w, ws_at<uint8_t>(workspace, p.off_tc), stream, &v);
+  if (st != QLIN_OK) return st;
   const int fmt = fmt_of(w);
   float* partial = ws_at<float>(workspace, p.off_partial);
   uint32_t* counters = ws_at<uint32_t>(workspace, p.off_counters);
@@ -598,6 +688,10 @@ int qlin_dequant_bf16(const qlin_qweight* w, uint16_t* W_out, hipStream_t stream
   if (st != QLIN_OK) return st;
   if (W_out == nullptr) return QLIN_E_NULL;
   if (!aligned16(W_out)) return QLIN_E_ALIGN;
+  if (w->format == QLIN_FMT_NF)
+    return hip_status(launch_dequant_nf(w->codes, w->absmax, w->absmax2, w->d_out * w->d_in, w->bits,
+                                        w->block, w->dq_block != 0 ? 1 : 0, nf_table(w->bits), W_out,
+                                        stream));
   const WeightView v = make_view(w);
   return hip_status(launch_dequant(v, fmt_of(w), W_out, stream));
 }

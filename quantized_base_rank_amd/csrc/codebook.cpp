@@ -1,12 +1,17 @@
-// NF4 levels computed on the host from their definition.
+// NormalFloat levels computed on the host from their definition.
 // [QLoRA "Innovation 1: 4-bit NormalFloat (NF4)": levels at quantiles of the
 //  standard normal so every bin holds an equal share of a normal weight;
-//  the code sketch's table uses the outermost quantile (15 + 1/2)/16.]
+//  the code sketch's table uses the outermost quantile (15 + 1/2)/16.
+//  LQ-LoRA abstract: the bit-width is chosen per matrix, so the same
+//  construction is used for 2 and 3 bits.]
 //
-// Construction: t = Phi^-1(31/32); positive levels Phi^-1(1/2 + j*(15/32)/8)/t
-// for j = 1..8, negative levels -Phi^-1(1/2 + j*(15/32)/7)/t for j = 1..7,
-// and an exact 0.  Phi^-1 is found by bisection on Phi(x) = erfc(-x/sqrt 2)/2
-// in long double, then each level is rounded once to fp32.
+// Construction for k bits: delta = 1 - 1/2^(k+1) (the outermost quantile
+// (2^k - 1/2)/2^k), t = Phi^-1(delta); positive levels
+// Phi^-1(1/2 + j (delta - 1/2)/P)/t for j = 1..P, negative levels
+// -Phi^-1(1/2 + j (delta - 1/2)/Q)/t for j = 1..Q, with P = 2^(k-1) and
+// Q = 2^(k-1) - 1, and an exact 0.  Phi^-1 is found by bisection on
+// Phi(x) = erfc(-x/sqrt 2)/2 in long double, then each level is rounded once
+// to fp32.
 #include <cmath>
 
 #include "host_codebook.hpp"
@@ -33,15 +38,18 @@ long double inv_phi(long double p) {
 
 }  // namespace
 
-void nf4_levels(float out[16]) {
-  const long double delta = 31.0L / 32.0L;
+void nf_levels(int bits, float* out) {
+  const int P = 1 << (bits - 1), Q = P - 1;
+  const long double delta = 1.0L - 1.0L / static_cast<long double>(1 << (bits + 1));
   const long double half = delta - 0.5L;
   const long double t = inv_phi(delta);
-  out[7] = 0.0f;
-  for (int j = 1; j <= 7; ++j)
-    out[7 - j] = static_cast<float>(-inv_phi(0.5L + j * half / 7.0L) / t);
-  for (int j = 1; j <= 8; ++j)
-    out[7 + j] = static_cast<float>(inv_phi(0.5L + j * half / 8.0L) / t);
+  out[Q] = 0.0f;
+  for (int j = 1; j <= Q; ++j)
+    out[Q - j] = static_cast<float>(-inv_phi(0.5L + j * half / Q) / t);
+  for (int j = 1; j <= P; ++j)
+    out[Q + j] = static_cast<float>(inv_phi(0.5L + j * half / P) / t);
 }
+
+void nf4_levels(float out[16]) { nf_levels(4, out); }
 
 }  // namespace qlin

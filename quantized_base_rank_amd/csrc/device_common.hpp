@@ -178,6 +178,26 @@ __device__ __forceinline__ Lut16 make_lut(const WeightView& w, int64_t row, int6
 
 constexpr int kFmtNF4 = 1;
 constexpr int kFmtINT4 = 2;
+// NormalFloat-k weights of any block size, as the layer kernels read them:
+// 4-bit level indices in the NF4 packing, the levels in WeightView::cb and
+// one fp32 scale per group of 32 elements, its low and high 16 bits held in
+// the `scale` and `zero` arrays (the INT4 group layout), so that the loads
+// of the INT4 path yield the scale's bits directly.
+constexpr int kFmtNFG = 3;
+
+// Lookup table of a group of 32 from its 32-bit group word `sz` (the INT4
+// path's scale | zero << 16): INT4 builds bf16(fl32(scale * i + zero)),
+// NormalFloat-k builds bf16(fl32(c[i] * scale)) with the word as the fp32
+// scale.
+template <int FMT>
+__device__ __forceinline__ Lut16 lut_group32(const Codebook& cb, uint32_t sz) {
+  if constexpr (FMT == kFmtNFG) {
+    return lut_nf4(cb, __uint_as_float(sz));
+  } else {
+    return lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
+                    half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
+  }
+}
 
 template <>
 __device__ __forceinline__ Lut16 make_lut<kFmtNF4>(const WeightView& w, int64_t row,
@@ -191,6 +211,13 @@ __device__ __forceinline__ Lut16 make_lut<kFmtINT4>(const WeightView& w, int64_t
   const int64_t g = row * (w.K >> 5) + grp_in_row;
   return lut_int4(half_bits_to_f32(w.scale[g]), half_bits_to_f32(w.zero[g]));
 }
+template <>
+__device__ __forceinline__ Lut16 make_lut<kFmtNFG>(const WeightView& w, int64_t row,
+                                                  int64_t grp_in_row) {
+  const int64_t g = row * (w.K >> 5) + grp_in_row;
+  return lut_group32<kFmtNFG>(w.cb, static_cast<uint32_t>(w.scale[g]) |
+                                        (static_cast<uint32_t>(w.zero[g]) << 16));
+}
 
 // Elements per lookup table for a format.
 template <int FMT>
@@ -201,6 +228,10 @@ struct FmtTraits<kFmtNF4> {
 };
 template <>
 struct FmtTraits<kFmtINT4> {
+  static constexpr int kBlock = 32;
+};
+template <>
+struct FmtTraits<kFmtNFG> {
   static constexpr int kBlock = 32;
 };
 
@@ -295,10 +326,8 @@ __device__ __forceinline__ void luts_from_params(const WeightView& w, BlockParam
     lut[0] = lut_nf4(w.cb, nf4_params_scale(w, p));
     lut[1] = lut[0];
   } else {
-    lut[0] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.a & 0xFFFFu)),
-                      half_bits_to_f32(static_cast<uint16_t>(p.a >> 16)));
-    lut[1] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(p.b & 0xFFFFu)),
-                      half_bits_to_f32(static_cast<uint16_t>(p.b >> 16)));
+    lut[0] = lut_group32<FMT>(w.cb, p.a);
+    lut[1] = lut_group32<FMT>(w.cb, p.b);
   }
 }
 

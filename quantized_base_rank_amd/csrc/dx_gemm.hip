@@ -65,6 +65,8 @@ template <>
 struct RowParams<kFmtINT4> {
   uint32_t s, z;  // fp16 scales and zeros of the two groups, low group first
 };
+template <>
+struct RowParams<kFmtNFG> : RowParams<kFmtINT4> {};  // the same group words
 
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
@@ -210,8 +212,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
       }
     } else {
       const uint32_t sz = valid ? perm(rc.z, rc.s, part == 0 ? 0x05040100u : 0x07060302u) : 0u;
-      lut[set][part] = lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
-                                half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
+      lut[set][part] = lut_group32<FMT>(a.w.cb, sz);
     }
   };
   // decoded word q (columns 8q .. 8q+7) of this lane's row into a slab stage
@@ -491,8 +492,10 @@ hipError_t launch_dx_gemm(const DxArgs& a, int fmt, hipStream_t stream) {
   const int grid = static_cast<int>(((a.M + kTMx - 1) / kTMx) * ((a.w.K + kTK - 1) / kTK));
   if (fmt == kFmtNF4)
     hipLaunchKernelGGL(k_dx_gemm<kFmtNF4>, dim3(grid), dim3(256), 0, stream, a);
-  else
+  else if (fmt == kFmtINT4)
     hipLaunchKernelGGL(k_dx_gemm<kFmtINT4>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_dx_gemm<kFmtNFG>, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -54,6 +54,8 @@ template <>
 struct StepParams<kFmtINT4> {
   uint32_t s[2], z[2];  // per row: fp16 scales and zeros of the two groups, low group first
 };
+template <>
+struct StepParams<kFmtNFG> : StepParams<kFmtINT4> {};  // the same group words
 
 // Where a lane's block constants live: buffer resources over the constant
 // arrays and per-lane offsets, so that a step's loads take only its scalar
@@ -71,6 +73,8 @@ struct ParamSrc<kFmtINT4> {
   rsrc_t rs, rz;
   uint32_t lg[2];    // byte offset of the lane's first group at step 0
 };
+template <>
+struct ParamSrc<kFmtNFG> : ParamSrc<kFmtINT4> {};
 
 template <int FMT>
 __device__ __forceinline__ ParamSrc<FMT> param_src(const WeightView& w, const int64_t (&nr)[2], int h);
@@ -96,6 +100,14 @@ __device__ __forceinline__ ParamSrc<kFmtINT4> param_src<kFmtINT4>(const WeightVi
   ps.rz = uniform_rsrc(w.zero, bytes);
 #pragma unroll
   for (int r = 0; r < 2; ++r) ps.lg[r] = static_cast<uint32_t>((nr[r] * (w.K >> 5) + 2 * h) * 2);
+  return ps;
+}
+
+template <>
+__device__ __forceinline__ ParamSrc<kFmtNFG> param_src<kFmtNFG>(const WeightView& w, const int64_t (&nr)[2],
+                                                                int h) {
+  ParamSrc<kFmtNFG> ps;
+  static_cast<ParamSrc<kFmtINT4>&>(ps) = param_src<kFmtINT4>(w, nr, h);
   return ps;
 }
 
@@ -125,6 +137,12 @@ __device__ __forceinline__ void load_params<kFmtINT4>(const ParamSrc<kFmtINT4>& 
   }
 }
 
+template <>
+__device__ __forceinline__ void load_params<kFmtNFG>(const ParamSrc<kFmtNFG>& ps, int64_t ks,
+                                                     StepParams<kFmtNFG>& p) {
+  load_params<kFmtINT4>(ps, ks, p);
+}
+
 template <int FMT>
 __device__ __forceinline__ Lut16 step_lut(const WeightView& w, const StepParams<FMT>& p, int r,
                                           int q, bool valid);
@@ -135,14 +153,24 @@ __device__ __forceinline__ Lut16 step_lut<kFmtNF4>(const WeightView& w,
   // an invalid block (past K) decodes to zeros through a zero scale
   return lut_nf4(w.cb, nf4_params_scale_sel(w, p.bp[r], valid));
 }
-template <>
-__device__ __forceinline__ Lut16 step_lut<kFmtINT4>(const WeightView&,
-                                                    const StepParams<kFmtINT4>& p, int r, int q,
-                                                    bool valid) {
+template <int FMT>
+__device__ __forceinline__ Lut16 step_lut_group32(const WeightView& w, const StepParams<kFmtINT4>& p,
+                                                  int r, int q, bool valid) {
   // scale (low 16 bits) | zero (high 16 bits) of group q
   const uint32_t sz = valid ? perm(p.z[r], p.s[r], q == 0 ? 0x05040100u : 0x07060302u) : 0u;
-  return lut_int4(half_bits_to_f32(static_cast<uint16_t>(sz & 0xFFFFu)),
-                  half_bits_to_f32(static_cast<uint16_t>(sz >> 16)));
+  return lut_group32<FMT>(w.cb, sz);
+}
+template <>
+__device__ __forceinline__ Lut16 step_lut<kFmtINT4>(const WeightView& w,
+                                                    const StepParams<kFmtINT4>& p, int r, int q,
+                                                    bool valid) {
+  return step_lut_group32<kFmtINT4>(w, p, r, q, valid);
+}
+template <>
+__device__ __forceinline__ Lut16 step_lut<kFmtNFG>(const WeightView& w,
+                                                   const StepParams<kFmtNFG>& p, int r, int q,
+                                                   bool valid) {
+  return step_lut_group32<kFmtNFG>(w, p, r, q, valid);
 }
 
 constexpr int kCTile = kTN * kKS / 2;  // packed codes of one K step: 16 KB
@@ -521,8 +549,10 @@ hipError_t launch_fwd_gemm(const FwdArgs& a, int fmt, hipStream_t stream) {
   const int grid = fwd_gemm_tiles(a.M, a.w.N) * a.splits;
   if (fmt == kFmtNF4)
     hipLaunchKernelGGL(k_fwd_gemm<kFmtNF4>, dim3(grid), dim3(256), 0, stream, a);
-  else
+  else if (fmt == kFmtINT4)
     hipLaunchKernelGGL(k_fwd_gemm<kFmtINT4>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_fwd_gemm<kFmtNFG>, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

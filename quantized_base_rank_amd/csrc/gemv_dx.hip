@@ -452,8 +452,10 @@ hipError_t launch_gemv_dx(const GemvDxArgs& a, int fmt, hipStream_t stream) {
   const int grid = gemv_dx_tiles(a.w.K) * a.splits;
   if (fmt == kFmtNF4)
     hipLaunchKernelGGL(k_gemv_dx<kFmtNF4>, dim3(grid), dim3(kGdThreads), 0, stream, a);
-  else
+  else if (fmt == kFmtINT4)
     hipLaunchKernelGGL(k_gemv_dx<kFmtINT4>, dim3(grid), dim3(kGdThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_gemv_dx<kFmtNFG>, dim3(grid), dim3(kGdThreads), 0, stream, a);
   return hipGetLastError();
 }
 

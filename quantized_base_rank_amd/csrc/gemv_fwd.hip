@@ -358,11 +358,16 @@ hipError_t launch_gemv_fwd(const GemvFwdArgs& a, int fmt, hipStream_t stream) {
       hipLaunchKernelGGL((k_gemv_fwd<kFmtNF4, true>), dim3(grid), block, 0, stream, a);
     else
       hipLaunchKernelGGL((k_gemv_fwd<kFmtNF4, false>), dim3(grid), block, 0, stream, a);
-  } else {
+  } else if (fmt == kFmtINT4) {
     if (a.fuse_u)
       hipLaunchKernelGGL((k_gemv_fwd<kFmtINT4, true>), dim3(grid), block, 0, stream, a);
     else
       hipLaunchKernelGGL((k_gemv_fwd<kFmtINT4, false>), dim3(grid), block, 0, stream, a);
+  } else {
+    if (a.fuse_u)
+      hipLaunchKernelGGL((k_gemv_fwd<kFmtNFG, true>), dim3(grid), block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemv_fwd<kFmtNFG, false>), dim3(grid), block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -25,6 +25,23 @@ hipError_t launch_quant_nf4(const float* W, int64_t n_blocks, int dq, const doub
 hipError_t launch_quant_int4(const float* W, int64_t n_groups, uint8_t* codes, uint16_t* scale,
                              uint16_t* zero, uint32_t* flag, hipStream_t stream);
 hipError_t launch_dequant(const WeightView& w, int fmt, uint16_t* out, hipStream_t stream);
+
+// NormalFloat-k (bits 2..4, blocks 32..256, bit-plane codes)
+struct NfTable {
+  float c[16];     // levels (2^bits used)
+  double mid[15];  // midpoints of neighbouring levels (2^bits - 1 used)
+};
+hipError_t launch_quant_nf(const float* W, int64_t n_blocks, int bits, int block, int dq,
+                           const NfTable& tb, uint8_t* codes, void* absmax, float* absmax2,
+                           uint32_t* flag, hipStream_t stream);
+hipError_t launch_dequant_nf(const uint8_t* codes, const void* absmax, const float* absmax2,
+                             int64_t n_el, int bits, int block, int dq, const NfTable& tb,
+                             uint16_t* out, hipStream_t stream);
+// bit planes -> 4-bit indices in the NF4 packing + per-32 fp32 scales split
+// into low / high 16-bit planes (the kFmtNFG layout read by the layer)
+hipError_t launch_transcode_nf(const uint8_t* codes, const void* absmax, const float* absmax2,
+                               int64_t n_el, int bits, int block, int dq, uint8_t* nib,
+                               uint16_t* scale_lo, uint16_t* scale_hi, hipStream_t stream);
 // zero'[n][g] = RN16(zero[n][g] + s sum_j B[n][j] A[j][g]) (QA-LoRA merge)
 hipError_t launch_qa_merge(const uint16_t* zero, const uint16_t* A, const uint16_t* B, int64_t N,
                            int64_t G, int r, float s, uint16_t* out, hipStream_t stream);

@@ -298,8 +298,11 @@ hipError_t launch_dequant(const WeightView& w, int fmt, uint16_t* out, hipStream
   if (fmt == kFmtNF4)
     hipLaunchKernelGGL(k_dequant<kFmtNF4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                        stream, w, out);
-  else
+  else if (fmt == kFmtINT4)
     hipLaunchKernelGGL(k_dequant<kFmtINT4>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                       stream, w, out);
+  else
+    hipLaunchKernelGGL(k_dequant<kFmtNFG>, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                        stream, w, out);
   return hipGetLastError();
 }

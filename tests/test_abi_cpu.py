@@ -42,6 +42,13 @@ def test_codebook_bit_identical_to_oracle(oracle):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_nf_codebook_bit_identical_to_oracle(oracle, bits):
+    from quantized_base_rank_amd import qlin_nf_codebook
+    got = qlin_nf_codebook(bits)
+    assert np.array_equal(got.view(np.uint32), oracle.nf_codebook(bits).view(np.uint32))
+
+
 def test_status_strings():
     L = _lib.lib()
     for st in range(8):
@@ -102,6 +109,10 @@ def test_argument_errors_return_before_any_launch():
                       None) == 5
     assert L.qlin_fwd(ctypes.byref(_qw(fmt=7)), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big,
                       None) == 5
+    # the NormalFloat-k workspace holds the transcoded weight as well
+    qnf = _lib.QWeightStruct(3, 64, 256, 3, 4096, 4096, 0x1000, 0x1000, 0x1000, 0, 0)
+    assert L.qlin_workspace_bytes(ctypes.byref(qnf), 16, 16, 1) >= \
+        L.qlin_workspace_bytes(ctypes.byref(_qw()), 16, 16, 1) + 4096 * 4096 * 5 // 8
     assert L.qlin_fwd(ctypes.byref(_qw(aligned=False)), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws,
                       big, None) == 3
     # bwd: missing gradient outputs
@@ -134,6 +145,20 @@ def test_argument_errors_return_before_any_launch():
     assert L.qlin_qa_merge(ctypes.byref(q4), ok, ok, 16, float("inf"), ok, None) == 2
     assert L.qlin_qa_merge(ctypes.byref(q4), ok, None, 16, 2.0, ok, None) == 1
     assert L.qlin_qa_merge(ctypes.byref(q4), ok, ok, 16, 2.0, bad, None) == 3
+    # NormalFloat-k quantizer and codebook
+    out16 = (ctypes.c_float * 16)()
+    assert L.qlin_nf_codebook(5, out16) == 5 and L.qlin_nf_codebook(3, None) == 1
+    assert L.qlin_quantize_nf(ok, 16, 256, 1, 64, 256, ok, ok, ok, None) == 5
+    assert L.qlin_quantize_nf(ok, 16, 256, 3, 48, 256, ok, ok, ok, None) == 5
+    assert L.qlin_quantize_nf(ok, 16, 256, 3, 64, 128, ok, ok, ok, None) == 5
+    assert L.qlin_quantize_nf(ok, 16, 384, 3, 256, 256, ok, ok, ok, None) == 2
+    assert L.qlin_quantize_nf(ok, 8, 256, 3, 64, 256, ok, ok, ok, None) == 2
+    assert L.qlin_quantize_nf(ok, 16, 256, 3, 64, 256, ok, ok, None, None) == 1
+    assert L.qlin_quantize_nf(bad, 16, 256, 3, 64, 256, ok, ok, ok, None) == 3
+    qn = _lib.QWeightStruct(3, 64, 256, 5, 64, 256, 0x1000, 0x1000, 0x1000, 0, 0)
+    assert L.qlin_fwd(ctypes.byref(qn), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 5
+    qn4 = _lib.QWeightStruct(1, 64, 256, 3, 64, 256, 0x1000, 0x1000, 0x1000, 0, 0)
+    assert L.qlin_fwd(ctypes.byref(qn4), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 5
     # profiling hook: host only
     assert L.qlin_profile_next_launch(b"k_fwd_gemm", None, None) == 1
     assert L.qlin_profile_next_launch(b"k" * 64, ok, ok) == 2
