@@ -137,6 +137,8 @@ def main():
     def quantize(Wt):
         if wl.fmt == "nf4":
             return qb.qlin_quantize_nf4(Wt, wl.block, wl.dq_block)
+        if wl.fmt == "nf":
+            return qb.qlin_quantize_nf(Wt, wl.bits, wl.block, wl.dq_block)
         return qb.qlin_quantize_int4_group(Wt, wl.block)
 
     hbm_bound = wl.M <= 16
@@ -214,37 +216,39 @@ def main():
     kernel_ms = {}
     if hbm_bound:
         # few tokens: each step is a few microseconds, so steps replay from a
-        # captured graph; qlin_fwd and qlin_bwd are one launch each here
-        # (k_gemv_fwd, k_gemv_dx), so a graph of either call alone times that
-        # kernel exactly as the step launches it
+        # captured graph.  qlin_bwd with u saved is one launch (k_gemv_dx),
+        # and so is qlin_fwd when the few-token kernel forms u itself (plain
+        # adapter, r <= 16): a graph of that call alone times that kernel
+        # exactly as the step launches it.
         if args.warmup > 0:
             gw = capture(step, args.warmup)
             gw.replay()
             torch.cuda.synchronize()
         gt = capture(step, args.steps, offset=args.warmup)
         ms_per_step = timed_graph(gt) / args.steps
-        for name, fn in (("k_gemv_fwd", fwd), ("k_gemv_dx", bwd)):
+        single = [("k_gemv_dx", bwd)]
+        if pool == 1 and r <= 16:
+            single.append(("k_gemv_fwd", fwd))
+        for name, fn in single:
             gk = capture(fn, args.kernel_iters)
             gk.replay()
             kernel_ms[name] = timed_graph(gk) / args.kernel_iters
         dominant = max(kernel_ms, key=kernel_ms.get)
         k_ms = kernel_ms[dominant]
-        timing = "graph replay"
+        timing = "graph replay of the single-launch call"
     else:
-        # large M: milliseconds per step, launched directly.  In warm-up the
-        # candidates are timed once each; in every timed step the library
-        # records events around the dominant kernel's launch.
-        candidates = ("k_fwd_gemm", "k_dx_gemm")
-        for i in range(max(args.warmup, len(candidates))):
-            if i < len(candidates):
-                ev = (new_event(), new_event())
-                qb.qlin_profile_next_launch(candidates[i], *ev)
-                step(i)
-                torch.cuda.synchronize()
-                kernel_ms[candidates[i]] = ev[0].elapsed_time(ev[1])
-            else:
-                step(i)
+        # large M: milliseconds per step, launched directly.  After warm-up,
+        # one further step per candidate times that candidate; in every timed
+        # step the library records events around the dominant kernel's launch.
+        for i in range(args.warmup):
+            step(i)
         torch.cuda.synchronize()
+        for name in ("k_fwd_gemm", "k_dx_gemm"):
+            ev = (new_event(), new_event())
+            qb.qlin_profile_next_launch(name, *ev)
+            step(0)
+            torch.cuda.synchronize()
+            kernel_ms[name] = ev[0].elapsed_time(ev[1])
         dominant = max(kernel_ms, key=kernel_ms.get)
         evs = [(new_event(), new_event()) for _ in range(args.steps)]
         e0, e1 = new_event(), new_event()
@@ -288,8 +292,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "d_out": wl.d_out, "d_in": wl.d_in, "M": wl.M, "r": wl.r,
-                   "s": wl.s, "format": wl.fmt, "block": wl.block, "dq_block": wl.dq_block,
-                   "pool": wl.pool, "weight_copies": n_copies},
+                   "s": wl.s, "format": wl.fmt, "bits": wl.bits, "block": wl.block,
+                   "dq_block": wl.dq_block, "pool": wl.pool, "weight_copies": n_copies},
         "tflops": round(tflops, 3), "weight_gbs": round(weight_gbs, 1),
         "frac_of_bf16_peak_step": round(tflops / BF16_PEAK_TFLOPS, 4),
         "packed_weight_bytes": wbytes, "flops_per_step": flops,
@@ -316,6 +320,8 @@ def cpu_baseline(wl, inp, hbm_bound, wbytes, flops):
     t0 = time.time()
     if wl.fmt == "nf4":
         codes, am, am2 = O.quantize_nf4(W, wl.block, wl.dq_block)
+    elif wl.fmt == "nf":
+        codes, am, am2 = O.quantize_nf(W, wl.bits, wl.block, wl.dq_block)
     else:
         codes, sc, zp = O.quantize_int4_group(W, wl.block)
     tq = time.time() - t0
@@ -328,6 +334,9 @@ def cpu_baseline(wl, inp, hbm_bound, wbytes, flops):
         t0 = time.time()
         if wl.fmt == "nf4":
             Wd = O.bf16_bits_to_f64(O.dequant_nf4_bf16(codes, am, am2, wl.block, wl.dq_block))
+        elif wl.fmt == "nf":
+            Wd = O.bf16_bits_to_f64(O.dequant_nf_bf16(codes, am, am2, wl.bits, wl.block,
+                                                      wl.dq_block))
         else:
             Wd = O.bf16_bits_to_f64(O.dequant_int4_bf16(codes, sc, zp, wl.block))
         y, u = O.lora_forward(Wd, xf, Af, Bf, wl.s, wl.pool)

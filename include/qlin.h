@@ -312,6 +312,26 @@ int qlin_qa_merge(const qlin_qweight *w, const uint16_t *A, const uint16_t *B, i
                   float s, uint16_t *zero_out, hipStream_t stream);
 
 /*
+ * Gradients of the INT4 group scales and zero points, for fine-tuning them
+ * as parameters.  [LoQA abstract: scale and zero point fine-tuned through a
+ * LoRA-compatible operator; QA-LoRA abstract for the INT4 groups]  With
+ * W[n][k] = scale[n][g] q[n][k] + zero[n][g] (g = k/32) and y = x W^T, the
+ * gradients of <dY, y>, the bf16 rounding of W passed straight through:
+ *     dscale[n][g] = sum_{k in g} q[n][k] dW[n][k],
+ *     dzero[n][g]  = sum_{k in g} dW[n][k],          dW = dY^T x,
+ * dW formed by bf16 MFMAs with fp32 accumulation, tile by tile, never
+ * stored.  (The page gives no formula: this is the plain reading.)
+ *
+ *   w        INT4 weight (QLIN_FMT_INT4_GROUP, group 32); its codes are read
+ *   x        bf16[M][d_in];  dy bf16[M][d_out];  1 <= M
+ *   dscale, dzero  fp32[d_out][d_in/32] (outputs)
+ * Asynchronous on `stream`.
+ */
+int qlin_int4_scale_zero_grad(const qlin_qweight *w, const uint16_t *x, int64_t M,
+                              const uint16_t *dy, float *dscale, float *dzero,
+                              hipStream_t stream);
+
+/*
  * Test helper: writes the dequantized weight W_bf16 (bf16[d_out][d_in]) using
  * the same in-register lookup-table decode as the fused kernels.  Never
  * called by qlin_fwd / qlin_bwd, which do not materialise W.  Asynchronous.
@@ -325,7 +345,7 @@ int qlin_dequant_bf16(const qlin_qweight *w, uint16_t *W_out, hipStream_t stream
  * and `stop` just after it, and the hook disarms itself.  Kernel names:
  * "k_gemv_fwd", "k_fwd_gemm" (forward products), "k_gemv_dx", "k_dx_gemm"
  * (input gradient), "k_nt_skinny", "k_tn2", "k_split_hl", "k_transpose16",
- * "k_qa_pool_u", "k_qa_dA" (adapter products).  `start` and `stop` are HIP
+ * "k_qa_pool_u", "k_qa_dA" (adapter products), "k_int4_scale_zero_grad".  `start` and `stop` are HIP
  * events created by the caller; the elapsed time between them is the
  * kernel's duration on the device.  kernel = NULL disarms.  One hook per
  * process (a later call replaces an armed one).  Host only; QLIN_E_NULL for

@@ -51,6 +51,12 @@ Parity status per function
                              bin occupancy; exact argmin; special cases;
                              bit-plane packing by hand; storage accounting)
 * qa_merge_zero ........... pinned (merged == unmerged forward)
+* int4_scale_zero_grads ... pinned (central differences of the real-valued
+                             layer in alpha and beta, brute-force loops,
+                             dbeta = dy^T pool_sum(x), constant codes); the
+                             formula itself is a reading (the page gives
+                             none), so its agreement with LoQA's own operator
+                             is "parity unpinned"
 * qa_merge_zero_f16 ....... pinned (exact rational RN16 of beta + s B A,
                              fp16 boundary ties, merged forward error)
 * The absolute values of the NF4 levels beyond the stated construction are
@@ -644,6 +650,26 @@ def qa_merge_zero_f16(zero_bits, A_bits, B_bits, s) -> np.ndarray:
                     h = hi
             out[n, g] = np.array(h).view(np.uint16)
     return out
+
+
+def int4_scale_zero_grads(codes, x, dy, group: int = 32):
+    """Gradients of <dy, y> with respect to the INT4 group scales and zero
+    points, for y = x W^T with W[n][k] = alpha[n][g] q[n][k] + beta[n][g]
+    (g = k / group): the trainable-quantization-parameter reading of LoQA's
+    operator [LoQA abstract: the scale and the zero point are fine-tuned;
+    R24].  The rounding of W to bf16 is passed straight through.  In float64:
+
+        dW[n][k]     = sum_m dy[m][n] x[m][k]
+        dalpha[n][g] = sum_{k in g} q[n][k] dW[n][k]
+        dbeta[n][g]  = sum_{k in g} dW[n][k]
+
+    Returns (dalpha, dbeta), each [d_out][d_in / group]."""
+    q = unpack_nibbles(codes).astype(F64)
+    dW = np.asarray(dy, dtype=F64).T @ np.asarray(x, dtype=F64)
+    n, k = dW.shape
+    dalpha = (q * dW).reshape(n, k // group, group).sum(axis=2)
+    dbeta = dW.reshape(n, k // group, group).sum(axis=2)
+    return dalpha, dbeta
 
 
 def rel_fro(got, ref) -> float:

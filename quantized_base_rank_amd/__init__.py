@@ -21,7 +21,7 @@ __all__ = [
     "QWeight", "QlinError", "qlin_nf4_codebook", "qlin_quantize_nf4", "qlin_nf_codebook",
     "qlin_quantize_nf",
     "qlin_quantize_int4_group", "qlin_workspace_bytes", "qlin_fwd", "qlin_fwd_noalloc", "qlin_bwd",
-    "qlin_dequant_bf16", "qlin_qa_merge", "qlin_profile_next_launch", "EXPORTS", "LIB_PATH",
+    "qlin_dequant_bf16", "qlin_qa_merge", "qlin_int4_scale_zero_grad", "qlin_profile_next_launch", "EXPORTS", "LIB_PATH",
 ]
 
 
@@ -249,6 +249,26 @@ def qlin_qa_merge(w: QWeight, A, B, r: int, s: float, zero_out=None):
     check(lib().qlin_qa_merge(ctypes.byref(s_), A.data_ptr(), B.data_ptr(), r, float(s),
                               zero_out.data_ptr(), _stream(w.device)), "qlin_qa_merge")
     return dataclasses.replace(w, zero=zero_out)
+
+
+def qlin_int4_scale_zero_grad(w: QWeight, x, dy, dscale=None, dzero=None):
+    """fp32 gradients (dscale, dzero) [d_out][d_in/32] of an INT4 weight's
+    group scales and zero points."""
+    torch = _torch()
+    M = x.shape[0]
+    dev = x.device
+    G = w.d_in // w.block
+    _need(x, torch.bfloat16, (M, w.d_in), "x")
+    _need(dy, torch.bfloat16, (M, w.d_out), "dy")
+    if dscale is None:
+        dscale = torch.empty((w.d_out, G), dtype=torch.float32, device=dev)
+    if dzero is None:
+        dzero = torch.empty((w.d_out, G), dtype=torch.float32, device=dev)
+    s_ = w.struct()
+    check(lib().qlin_int4_scale_zero_grad(ctypes.byref(s_), x.data_ptr(), M, dy.data_ptr(),
+                                          dscale.data_ptr(), dzero.data_ptr(), _stream(dev)),
+          "qlin_int4_scale_zero_grad")
+    return dscale, dzero
 
 
 def qlin_dequant_bf16(w: QWeight):

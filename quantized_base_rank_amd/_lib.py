@@ -26,6 +26,7 @@ EXPORTS = (
     "qlin_bwd",
     "qlin_dequant_bf16",
     "qlin_qa_merge",
+    "qlin_int4_scale_zero_grad",
     "qlin_profile_next_launch",
     "qlin_status_string",
 )
@@ -77,6 +78,7 @@ def lib() -> ctypes.CDLL:
         "qlin_dequant_bf16": (ctypes.c_int, [qp, vp, vp]),
         "qlin_profile_next_launch": (ctypes.c_int, [ctypes.c_char_p, vp, vp]),
         "qlin_qa_merge": (ctypes.c_int, [qp, vp, vp, i32, f32, vp, vp]),
+        "qlin_int4_scale_zero_grad": (ctypes.c_int, [qp, vp, i64, vp, vp, vp, vp]),
         "qlin_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():

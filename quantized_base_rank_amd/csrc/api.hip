@@ -667,6 +667,23 @@ int qlin_qa_merge(const qlin_qweight* w, const uint16_t* A, const uint16_t* B, i
   return hip_status(launch_qa_merge(w->zero, A, B, w->d_out, G, r, s, zero_out, stream));
 }
 
+int qlin_int4_scale_zero_grad(const qlin_qweight* w, const uint16_t* x, int64_t M,
+                              const uint16_t* dy, float* dscale, float* dzero,
+                              hipStream_t stream) {
+  const int st = check_weight(w);
+  if (st != QLIN_OK) return st;
+  if (w->format != QLIN_FMT_INT4_GROUP) return QLIN_E_UNSUPPORTED;
+  if (M < 1 || M > (int64_t{1} << 31)) return QLIN_E_SHAPE;
+  if (x == nullptr || dy == nullptr || dscale == nullptr || dzero == nullptr) return QLIN_E_NULL;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dscale) || !aligned16(dzero))
+    return QLIN_E_ALIGN;
+  LoqaArgs a{};
+  a.codes = w->codes; a.x = x; a.dy = dy; a.dscale = dscale; a.dzero = dzero;
+  a.M = M; a.N = w->d_out; a.K = w->d_in;
+  return hip_status(hooked("k_int4_scale_zero_grad", stream,
+                           [&] { return launch_int4_scale_zero_grad(a, stream); }));
+}
+
 int qlin_profile_next_launch(const char* kernel, hipEvent_t start, hipEvent_t stop) {
   ProfileHook& h = profile_hook();
   std::lock_guard<std::mutex> g(h.m);

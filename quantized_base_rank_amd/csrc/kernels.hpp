@@ -26,6 +26,19 @@ hipError_t launch_quant_int4(const float* W, int64_t n_groups, uint8_t* codes, u
                              uint16_t* zero, uint32_t* flag, hipStream_t stream);
 hipError_t launch_dequant(const WeightView& w, int fmt, uint16_t* out, hipStream_t stream);
 
+// Gradients of INT4 group scales and zero points: dscale[n][g] =
+// sum_{k in g} q[n][k] dW[n][k], dzero[n][g] = sum_{k in g} dW[n][k],
+// dW = dY^T x (fp32 outputs [N][K/32])
+struct LoqaArgs {
+  const uint8_t* codes;   // [N][K/2], the NF4 / INT4 nibble packing
+  const uint16_t* x;      // bf16 [M][K]
+  const uint16_t* dy;     // bf16 [M][N]
+  float* dscale;
+  float* dzero;
+  int64_t M, N, K;        // K % 64 == 0, N % 16 == 0
+};
+hipError_t launch_int4_scale_zero_grad(const LoqaArgs& a, hipStream_t stream);
+
 // NormalFloat-k (bits 2..4, blocks 32..256, bit-plane codes)
 struct NfTable {
   float c[16];     // levels (2^bits used)

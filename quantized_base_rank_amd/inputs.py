@@ -39,10 +39,11 @@ class Workload:
     M: int
     r: int
     s: float = 2.0
-    fmt: str = "nf4"          # "nf4" or "int4"
-    block: int = 64           # NF4 absmax block, or INT4 group size
-    dq_block: int = 256       # NF4 second-level group (0 = none)
+    fmt: str = "nf4"          # "nf4", "int4" or "nf" (NormalFloat-k, `bits` bits)
+    block: int = 64           # NF absmax block, or INT4 group size
+    dq_block: int = 256       # NF second-level group (0 = none)
     pool: int = 1             # 1 = plain LoRA; = group for QA-LoRA pooled adapter
+    bits: int = 4             # NormalFloat-k bit count (fmt "nf")
 
     @property
     def k_a(self) -> int:
@@ -61,11 +62,12 @@ class Workload:
 
     def packed_weight_bytes(self) -> int:
         n_el = self.d_out * self.d_in
-        if self.fmt == "nf4":
+        if self.fmt in ("nf4", "nf"):
             nb = n_el // self.block
+            codes = n_el * (4 if self.fmt == "nf4" else self.bits) // 8
             if self.dq_block:
-                return n_el // 2 + nb + 4 * (-(-nb // self.dq_block))
-            return n_el // 2 + 4 * nb
+                return codes + nb + 4 * (-(-nb // self.dq_block))
+            return codes + 4 * nb
         ng = n_el // self.block
         return n_el // 2 + 2 * 2 * ng
 
@@ -78,6 +80,10 @@ WORKLOADS = {
     "qa_int4": Workload("qalora-int4g32-4096x11008-r64", 4096, 11008, 2048, 64,
                         fmt="int4", block=32, dq_block=0, pool=32),
     "down_proj70b": Workload("llama2-70b-down_proj-8192x28672-r64", 8192, 28672, 4096, 64),
+    # the 70B down_proj with 3-bit NormalFloat weights (LQ-LoRA's sub-4-bit
+    # regime; the layer reads them through the per-call transcoded form)
+    "down_proj70b_nf3": Workload("llama2-70b-down_proj-8192x28672-r64-nf3", 8192, 28672, 4096, 64,
+                                 fmt="nf", bits=3),
 }
 
 

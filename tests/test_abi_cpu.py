@@ -159,6 +159,11 @@ def test_argument_errors_return_before_any_launch():
     assert L.qlin_fwd(ctypes.byref(qn), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 5
     qn4 = _lib.QWeightStruct(1, 64, 256, 3, 64, 256, 0x1000, 0x1000, 0x1000, 0, 0)
     assert L.qlin_fwd(ctypes.byref(qn4), ok, 16, ok, ok, 16, 2.0, 1, ok, None, ws, big, None) == 5
+    # INT4 scale / zero gradients
+    assert L.qlin_int4_scale_zero_grad(ctypes.byref(qw), ok, 16, ok, ok, ok, None) == 5
+    assert L.qlin_int4_scale_zero_grad(ctypes.byref(q4), ok, 0, ok, ok, ok, None) == 2
+    assert L.qlin_int4_scale_zero_grad(ctypes.byref(q4), ok, 16, None, ok, ok, None) == 1
+    assert L.qlin_int4_scale_zero_grad(ctypes.byref(q4), ok, 16, ok, bad, ok, None) == 3
     # profiling hook: host only
     assert L.qlin_profile_next_launch(b"k_fwd_gemm", None, None) == 1
     assert L.qlin_profile_next_launch(b"k" * 64, ok, ok) == 2

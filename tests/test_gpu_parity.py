@@ -380,3 +380,25 @@ def test_nonfinite_token_does_not_leak_backward(qb, oracle):
     (_, d0), (_, d1) = _poisoned_run(qb, oracle, 528, 256, M, 16, bad, "dy", slice(0, 48))
     keep = np.arange(M) != bad
     assert np.array_equal(d1[keep], d0[keep])
+
+
+@pytest.mark.parametrize("d_out,d_in,M", [
+    (256, 1024, 64),     # whole tiles
+    (272, 1088, 300),    # ragged tiles in n, k and tokens
+    (512, 2048, 1),      # a single token
+])
+def test_int4_scale_zero_grad(qb, oracle, d_out, d_in, M):
+    """Gradients of the INT4 group scales and zero points (fp32 outputs)
+    against the float64 oracle, with the fp32 bounds of tests/parity.py."""
+    from quantized_base_rank_amd.inputs import Workload, make_inputs
+    from tests import parity
+    wl = Workload("loqa", d_out, d_in, M, 16, 2.0, fmt="int4", block=32, dq_block=0, pool=32)
+    inp = make_inputs(wl, seed=17)
+    qw = qb.qlin_quantize_int4_group(to_dev_f32(inp.W), 32)
+    ds, dz = qb.qlin_int4_scale_zero_grad(qw, to_dev_bf16(inp.x), to_dev_bf16(inp.dy))
+    codes, _, _ = oracle.quantize_int4_group(inp.W, 32)
+    da_ref, db_ref = oracle.int4_scale_zero_grads(codes, oracle.bf16_bits_to_f64(inp.x),
+                                                  oracle.bf16_bits_to_f64(inp.dy), 32)
+    parity.check({"dscale": (host(ds).astype(np.float64), da_ref),
+                  "dzero": (host(dz).astype(np.float64), db_ref)},
+                 fmts={"dscale": "f32", "dzero": "f32"})

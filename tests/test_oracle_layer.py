@@ -410,3 +410,61 @@ def test_qa_merge_f16_is_the_exactly_rounded_sum(oracle):
     ref = oracle.qa_merge_zero(zp, Af, Bf, float(s))
     back = oracle.f16_bits_to_f32(got).astype(np.float64)
     assert np.all(np.abs(back - ref) <= np.abs(ref) * 2.0 ** -11 + 2.0 ** -25)
+
+
+# ------------------------------------- trainable INT4 scale and zero point
+
+
+def test_int4_scale_zero_grads_match_finite_differences(oracle):
+    """<dy, x W^T> with W = alpha q + beta is linear in every alpha and beta,
+    so central differences in float64 equal the gradients up to rounding."""
+    rng = np.random.default_rng(51)
+    M, N, K, G = 5, 6, 96, 32
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    codes, sc, zp = oracle.quantize_int4_group(W, G)
+    q = oracle.unpack_nibbles(codes).astype(np.float64)
+    alpha = oracle.f16_bits_to_f32(sc).astype(np.float64)
+    beta = oracle.f16_bits_to_f32(zp).astype(np.float64)
+    x = rng.standard_normal((M, K))
+    dy = rng.standard_normal((M, N))
+
+    def loss(al, be):
+        Wr = np.repeat(al, G, axis=1) * q + np.repeat(be, G, axis=1)
+        return float(np.sum(dy * (x @ Wr.T)))
+
+    da, db = oracle.int4_scale_zero_grads(codes, x, dy, G)
+    h = 1e-3
+    for arr, grad, which in ((alpha, da, 0), (beta, db, 1)):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p_, m_ = arr.copy(), arr.copy()
+            p_[idx] += h
+            m_[idx] -= h
+            lp = loss(p_, beta) if which == 0 else loss(alpha, p_)
+            lm = loss(m_, beta) if which == 0 else loss(alpha, m_)
+            fd[idx] = (lp - lm) / (2 * h)
+        assert np.allclose(grad, fd, rtol=1e-8, atol=1e-9)
+
+
+def test_int4_scale_zero_grads_loops_and_special_cases(oracle):
+    rng = np.random.default_rng(52)
+    M, N, K, G = 3, 4, 64, 32
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    codes, _, _ = oracle.quantize_int4_group(W, G)
+    q = oracle.unpack_nibbles(codes)
+    x = rng.standard_normal((M, K))
+    dy = rng.standard_normal((M, N))
+    da, db = oracle.int4_scale_zero_grads(codes, x, dy, G)
+    for n in range(N):
+        for g in range(K // G):
+            ks = range(g * G, (g + 1) * G)
+            dw = [sum(dy[m][n] * x[m][k] for m in range(M)) for k in ks]
+            assert abs(db[n][g] - sum(dw)) < 1e-12
+            assert abs(da[n][g] - sum(int(q[n][k]) * d for k, d in zip(ks, dw))) < 1e-12
+    # dbeta is the pooled product dy^T P
+    assert np.allclose(db, dy.T @ oracle.pool_sum(x, G), rtol=1e-13, atol=1e-13)
+    # every code equal to c: dalpha = c dbeta
+    c = 9
+    codes_c = oracle.pack_nibbles(np.full((N, K), c, np.uint8))
+    da_c, db_c = oracle.int4_scale_zero_grads(codes_c, x, dy, G)
+    assert np.allclose(da_c, c * db_c, rtol=1e-13, atol=1e-13)
