@@ -132,6 +132,8 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // Work split of the reductions and the workspace layout for one layer shape.
 struct Plan {
   bool small = false;
+  bool stream = false;  // few tokens, large weight: the streamed forward
+  int fs_splits = 1, uf_splits = 1;
   bool fits = true;  // the shape's ticket counters fit the fixed region
   int fwd_splits = 1;
   int nt_splits_u = 1, nt_splits_du = 1;
@@ -169,6 +171,11 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   }
   p.gf_splits = gemv_fwd_splits(K);
   p.gd_splits = gemv_dx_splits(N);
+  // few tokens on a weight above 32 M elements: streamed forward (the
+  // one-shot kernels are shaped for one round of workgroups at 4096 x 4096)
+  p.stream = p.small && N * K > (int64_t{1} << 25);
+  p.fs_splits = fwd_stream_splits(N, K);
+  p.uf_splits = u_few_splits(r > 0 ? r : 1, K);
 
   // counters each kernel takes tickets on (only when it splits a reduction;
   // the few-token backward always does)
@@ -176,7 +183,9 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
                                         p.tn2_splits_dB > 1 ? tn2_tiles(N) : 0,
                                         p.tn2_splits_dA > 1 ? tn2_tiles(K) : 0});
   if (p.small)
-    counters = std::max<int64_t>({counters, p.gf_splits > 1 ? gemv_fwd_tiles(N) : 0, gemv_dx_tiles(K)});
+    counters = std::max<int64_t>({counters, p.gf_splits > 1 ? gemv_fwd_tiles(N) : 0, gemv_dx_tiles(K),
+                                  p.fs_splits > 1 ? fwd_stream_row_groups(N) : 0,
+                                  p.uf_splits > 1 ? u_few_tiles(r > 0 ? r : 1) : 0});
   else if (p.fwd_splits > 1)
     counters = std::max<int64_t>(counters, fwd_gemm_tiles(M, N));
   p.fits = counters <= kCounterWords;
@@ -187,7 +196,9 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   if (p.small) {
     partial = std::max<int64_t>({partial,
                                  gemv_fwd_partial_floats(N, K),
-                                 gemv_dx_partial_floats(N, K) + gemv_dx_dupart_floats(N, K, r)});
+                                 gemv_dx_partial_floats(N, K) + gemv_dx_dupart_floats(N, K, r),
+                                 p.stream ? fwd_stream_partial_floats(N, K) : 0,
+                                 u_few_partial_floats(r > 0 ? r : 1, K)});
   } else {
     partial = std::max<int64_t>(partial, fwd_gemm_partial_floats(M, N, p.fwd_splits));
     if (pool > 1) partial = std::max<int64_t>(partial, qa_dA_partial_floats(M, r, G));
@@ -289,6 +300,18 @@ hipError_t hooked(const char* name, hipStream_t stream, Launch launch) {
 int compute_u(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t* A, int32_t r,
               int32_t pool, float* u, int splits_u, float* partial, uint32_t* counters,
               hipStream_t stream) {
+  if (pool == 1 && M <= kSmallM) {
+    UFewArgs a{};
+    a.X = x; a.ldx = w->d_in;
+    a.Y = A; a.ldy = w->d_in;
+    a.C = u; a.ldc = r;
+    a.M = M; a.K = w->d_in; a.J = r;
+    a.splits = u_few_splits(r, w->d_in);
+    a.alpha = 1.0f;
+    a.partial = partial;
+    a.counters = counters;
+    return hip_status(hooked("k_u_few", stream, [&] { return launch_u_few(a, stream); }));
+  }
   if (pool == 1) {
     NtArgs a{};
     a.X = x; a.ldx = w->d_in;
@@ -308,7 +331,9 @@ int compute_u(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_
 }
 
 // Whether the few-token forward forms u itself (plain adapter of rank <= 16).
-bool fwd_fuses_u(const Plan& p, int32_t r, int32_t pool) { return p.small && pool == 1 && r <= 16; }
+bool fwd_fuses_u(const Plan& p, int32_t r, int32_t pool) {
+  return p.small && !p.stream && pool == 1 && r <= 16;
+}
 
 // The forward pass on explicit buffers: `u_tmp` (fp32 [M][r], used when
 // u_out is NULL), `partial` (split partial sums) and `counters` (ticket
@@ -327,6 +352,17 @@ int fwd_core(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   if (!fuse_u && (adapter || u_out != nullptr)) {
     const int st = compute_u(w, x, M, A, r, pool, u, p.nt_splits_u, partial, counters, stream);
     if (st != QLIN_OK) return st;
+  }
+  if (p.stream) {
+    FwdStreamArgs a{};
+    a.w = v; a.x = x; a.M = M; a.B = B; a.u = u; a.r = r; a.s = s;
+    a.adapter = adapter ? 1 : 0;
+    a.y = y;
+    a.splits = p.fs_splits;
+    a.partial = partial;
+    a.counters = counters;
+    return hip_status(hooked("k_gemv_fwd_stream", stream,
+                             [&] { return launch_gemv_fwd_stream(a, fmt, stream); }));
   }
   if (p.small) {
     GemvFwdArgs a{};
@@ -385,9 +421,11 @@ FwdScratch fwd_scratch_layout(const qlin_qweight* w, int64_t M, int32_t r, int32
                               const Plan& p) {
   const int64_t N = w->d_out, K = w->d_in;
   int64_t partial = 0;
-  if (pool == 1 && !fwd_fuses_u(p, r, pool)) partial = nt_partial_floats(M, p.nt_splits_u);
-  partial = std::max<int64_t>(partial, p.small ? gemv_fwd_partial_floats(N, K)
-                                               : fwd_gemm_partial_floats(M, N, p.fwd_splits));
+  if (pool == 1 && !fwd_fuses_u(p, r, pool))
+    partial = p.small ? u_few_partial_floats(r > 0 ? r : 1, K) : nt_partial_floats(M, p.nt_splits_u);
+  partial = std::max<int64_t>(partial, p.stream ? fwd_stream_partial_floats(N, K)
+                                       : (p.small ? gemv_fwd_partial_floats(N, K)
+                                                  : fwd_gemm_partial_floats(M, N, p.fwd_splits)));
   FwdScratch f;
   size_t off = kCounterBytes;
   f.off_u = off;       off = align256(off + static_cast<size_t>(M) * (r > 0 ? r : 0) * sizeof(float));

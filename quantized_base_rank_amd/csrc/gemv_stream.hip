@@ -1,0 +1,370 @@
+// Few-token (M <= 16) kernels for large weights, bound by streaming the
+// packed weight from HBM.  [QLoRA "The QLoRA recipe" stage 3: each block is
+// decoded to bf16 on the fly; "Background: how LoRA works" for the adapter;
+// QA-LoRA abstract for INT4 groups]
+//
+// k_gemv_fwd_stream:  y = x W_bf16^T + s u B^T  (u given)
+//   A workgroup owns 128 output features (8 waves x 16) over a share of K
+//   and streams it in chunks of 256 columns.  Every lane owns one 64-column
+//   block of one row per chunk (32 bytes of codes, one lookup table), which
+//   it decodes into the MFMA operand of that block: in k-step t of a chunk,
+//   lane group g supplies columns 64 g + 8 t .. + 7, and the token operand
+//   is read in the same column order, so each v_mfma_f32_16x16x32_bf16 sums
+//   32 of the chunk's columns.  Codes and block constants run four chunks
+//   ahead in registers; the token chunk (16 x 256 bf16, shared by the eight
+//   waves) is staged in LDS two chunks ahead.  K shares publish fp32 partial
+//   sums (write-through stores) and the last workgroup of a row group
+//   (atomic ticket) adds them in fixed share order, adds s u B^T and stores
+//   y.  Work per workgroup is a long pipelined loop rather than one shot, so
+//   a grid of ~256 workgroups (one per compute unit) streams a weight of any
+//   size.
+//
+// k_u_few:  u = alpha X Y^T for M <= 16 rows of X (u = x A^T, du = s dY B)
+//   16 x 16 MFMA tiles over (adapter column, token), K split over
+//   workgroups with the same ticketed fixed-order fix-up.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace qlin {
+
+namespace {
+
+constexpr int kFsWaves = 8;
+constexpr int kFsThreads = 64 * kFsWaves;
+constexpr int kFsRows = 16 * kFsWaves;   // output features per workgroup
+#ifndef QLIN_FS_CHUNK
+#define QLIN_FS_CHUNK 512
+#endif
+#ifndef QLIN_FS_DEPTH
+#define QLIN_FS_DEPTH 2
+#endif
+#ifndef QLIN_FS_WGS_PER_CU
+#define QLIN_FS_WGS_PER_CU 1
+#endif
+constexpr int kFsChunk = QLIN_FS_CHUNK;  // columns per step: 256, 512 or 1024
+constexpr int kFsDepth = QLIN_FS_DEPTH;  // steps of loads in flight beyond the current one
+constexpr int kFsRun = kFsChunk / 4;     // columns of a lane's run per step (g = 0..3)
+constexpr int kFsBlk = kFsRun / 64;      // 64-column blocks per run
+constexpr int kFsRowBytes = kFsChunk * 2;
+
+// Steps per K share: a multiple of the ring depth, so that only the last
+// share runs masked steps.
+__host__ __device__ inline int fwd_stream_per(int nchk, int S) {
+  const int per = (nchk + S - 1) / S;
+  return (per + kFsDepth - 1) / kFsDepth * kFsDepth;
+}
+
+// Per lane and step: the run of codes of its row (columns kFsRun g ..
+// kFsRun (g + 1) - 1 of the step, kFsBlk 64-column blocks of 32 bytes), the
+// blocks' raw constants, and the token pieces this thread stages.
+constexpr int kFsXPer = kFsChunk / 256;  // 16-byte token pieces per thread and step (32 threads per token row)
+static_assert(kFsChunk % 256 == 0 && kFsChunk <= 1024, "step width: 256, 512 or 1024 columns");
+struct FsSlot {
+  u32x4 c[2 * kFsBlk];
+  BlockParams p[kFsBlk];
+  u32x4 x[kFsXPer];
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kFsThreads, QLIN_FS_WGS_PER_CU) void k_gemv_fwd_stream(FwdStreamArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][16 * kFsRowBytes];  // token steps
+  __shared__ uint32_t s_ticket;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t N = a.w.N, K = a.w.K, M = a.M;
+  const int n_rg = static_cast<int>((N + kFsRows - 1) / kFsRows);
+  const int rg = static_cast<int>(blockIdx.x) % n_rg;
+  const int ks = static_cast<int>(blockIdx.x) / n_rg;
+  const int S = a.splits;
+  const int nchk = static_cast<int>((K + kFsChunk - 1) / kFsChunk);
+  const int per = fwd_stream_per(nchk, S);
+  const int c0 = ks * per;
+  const int c1 = c0 + per < nchk ? c0 + per : nchk;
+  const int64_t n0 = static_cast<int64_t>(rg) * kFsRows;
+  const int64_t n = n0 + wave * 16 + l16;
+  const int64_t nc = n < N ? n : N - 1;
+
+  // token staging: thread t moves kFsXPer consecutive pieces of token row
+  // t >> 5 (rows past M repeat the last token, columns past K the last valid
+  // piece; both meet discarded outputs or zero weights)
+  const int xrow = tid >> 5, xp0 = (tid & 31) * kFsXPer;
+  const int64_t xrc = xrow < M ? xrow : M - 1;
+  auto clampc = [&](int c) { return c < nchk ? c : nchk - 1; };
+  // block j of this lane's run in step c: columns c kFsChunk + kFsRun g + 64 j
+  auto blk_col = [&](int c, int j) { return static_cast<int64_t>(c) * kFsChunk + kFsRun * g + 64 * j; };
+  auto blk_ok = [&](int c, int j) { return c < c1 && blk_col(c, j) < K; };
+  auto load_slot = [&](int c, FsSlot& sl) {
+    const int cc = clampc(c);
+    // codes: the run's bytes (a block past K reads the row's first bytes and
+    // is masked)
+#pragma unroll
+    for (int j = 0; j < kFsBlk; ++j) {
+      const int64_t col = blk_col(cc, j);
+      const u32x4* cp = reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (col < K ? col / 2 : 0));
+      sl.c[2 * j] = cp[0];
+      sl.c[2 * j + 1] = cp[1];
+    }
+#pragma unroll
+    for (int j = 0; j < kFsBlk; ++j) {
+      const int64_t col = blk_col(cc, j);
+      const int64_t blk = col < K ? col / 64 : 0;
+      if constexpr (FMT == kFmtNF4) {
+        sl.p[j] = load_block_params<FMT>(a.w, nc, blk, true);
+      } else {
+        // the two 32-bit words with the scales and the zeros of the block's
+        // two groups, split into tables at decode time
+        const int64_t g2 = nc * (K >> 5) + 2 * blk;
+        sl.p[j].a = *reinterpret_cast<const uint32_t*>(a.w.scale + g2);
+        sl.p[j].b = *reinterpret_cast<const uint32_t*>(a.w.zero + g2);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kFsXPer; ++i) {
+      int64_t k = static_cast<int64_t>(cc) * kFsChunk + (xp0 + i) * 8;
+      k = k < K ? k : K - 8;
+      sl.x[i] = *reinterpret_cast<const u32x4*>(a.x + xrc * K + k);
+    }
+  };
+  auto store_x = [&](int buf, const FsSlot& sl) {
+#pragma unroll
+    for (int i = 0; i < kFsXPer; ++i)
+      *reinterpret_cast<u32x4*>(&s_x[buf][xrow * kFsRowBytes + (((xp0 + i) ^ xrow) << 4)]) = sl.x[i];
+  };
+
+  // Ring of kFsDepth + 1 steps: all loads of a step are issued together, so
+  // waiting for the token pieces of step c + 1 (stored at the end of step c)
+  // waits only for loads issued kFsDepth steps ago.  The loop body has no
+  // branches (a branch join makes the compiler wait for every load in
+  // flight): steps past the share decode through all-zero tables.
+  constexpr int R = kFsDepth + 1;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  FsSlot ring[R];
+#pragma unroll
+  for (int d = 0; d < R; ++d) load_slot(c0 + d, ring[d]);
+  store_x(c0 & 1, ring[0]);
+  __syncthreads();
+
+  for (int cb = c0; cb < c1; cb += R) {
+#pragma unroll
+    for (int d = 0; d < R; ++d) {
+      const int c = cb + d;
+      const uint8_t* xs = s_x[c & 1];
+#pragma unroll
+      for (int j = 0; j < kFsBlk; ++j) {
+        Lut16 lut[2];
+        const bool ok = blk_ok(c, j);
+        if constexpr (FMT == kFmtNF4) {
+          lut[0] = lut_nf4(a.w.cb, nf4_params_scale_sel(a.w, ring[d].p[j], ok));
+          lut[1] = lut[0];
+        } else {
+          lut[0] = lut_group32<FMT>(a.w.cb, ok ? perm(ring[d].p[j].b, ring[d].p[j].a, 0x05040100u) : 0u);
+          lut[1] = lut_group32<FMT>(a.w.cb, ok ? perm(ring[d].p[j].b, ring[d].p[j].a, 0x07060302u) : 0u);
+        }
+        // k-step t of block j: columns kFsRun g + 64 j + 8 t .. + 7 of the step
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const u32x4 wf = lut_decode8(lut[t >> 2], ring[d].c[2 * j + (t >> 2)][t & 3]);
+          const int q = (kFsRun / 8) * g + 8 * j + t;
+          const u32x4 xf = *reinterpret_cast<const u32x4*>(xs + l16 * kFsRowBytes + ((q ^ l16) << 4));
+          acc = mfma16(wf, xf, acc);
+        }
+      }
+      // the next step's tokens into the other buffer (last read before the
+      // previous barrier), then this slot refills with step c + R
+      const int dn = (d + 1) % R;  // (a constant once the loop is unrolled)
+      store_x((c + 1) & 1, ring[dn]);
+      load_slot(c + R, ring[d]);
+      __syncthreads();
+    }
+  }
+
+  // lane (l16, g) holds y[m = l16][n = n0 + 16 wave + 4 g + v]
+  f32x4 sum = acc;
+  if (S > 1) {
+    const rsrc_t pr_ = make_rsrc(a.partial);
+    const uint32_t mine = static_cast<uint32_t>(((static_cast<int64_t>(ks) * n_rg + rg) * kFsThreads + tid) * 16);
+    st_sys16(pr_, mine, acc);
+    if (__builtin_amdgcn_readfirstlane(publish_and_ticket(a.counters + rg, &s_ticket)) !=
+        static_cast<uint32_t>(S - 1))
+      return;
+    f32x4 part[8];
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp) {
+      const int spc = sp < S ? sp : S - 1;
+      part[sp] = ld_sys16(pr_, static_cast<uint32_t>(((static_cast<int64_t>(spc) * n_rg + rg) * kFsThreads + tid) * 16));
+    }
+    sum = part[0];
+#pragma unroll
+    for (int sp = 1; sp < 8; ++sp)
+      if (sp < S) sum += part[sp];
+    for (int sp0 = 8; sp0 < S; sp0 += 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int spc = sp0 + q < S ? sp0 + q : S - 1;
+        part[q] = ld_sys16(pr_, static_cast<uint32_t>(((static_cast<int64_t>(spc) * n_rg + rg) * kFsThreads + tid) * 16));
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (sp0 + q < S) sum += part[q];
+    }
+    if (tid == 0) a.counters[rg] = 0u;
+  }
+
+  // adapter term s u B^T as MFMAs over the adapter columns, in the layout of
+  // the sums: A operand B[n][j .. j+7] (lane row n = n0 + 16 wave + l16), token
+  // operand s u[m][j .. j+7] split into bf16 hi + lo halves (fp32 accuracy)
+  const int r = a.r;
+  if (a.adapter) {
+    const int64_t nb = n0 + wave * 16 + l16;
+    const uint16_t* brow = a.B + (nb < N ? nb : N - 1) * r;
+    const float* urow = a.u + static_cast<int64_t>(l16 < M ? l16 : M - 1) * r;
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      uint32_t bw[4], hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + 8 * g + 2 * e;
+        const uint32_t b0 = j < r ? brow[j] : 0u, b1 = j + 1 < r ? brow[j + 1] : 0u;
+        bw[e] = b0 | (b1 << 16);
+        float h0, l0, h1, l1;
+        split_bf16(j < r ? a.s * urow[j] : 0.0f, h0, l0);
+        split_bf16(j + 1 < r ? a.s * urow[j + 1] : 0.0f, h1, l1);
+        hw[e] = pack_bf16x2(h0, h1);
+        lw[e] = pack_bf16x2(l0, l1);
+      }
+      const u32x4 bop = {bw[0], bw[1], bw[2], bw[3]};
+      sum = mfma16(bop, u32x4{hw[0], hw[1], hw[2], hw[3]}, sum);
+      sum = mfma16(bop, u32x4{lw[0], lw[1], lw[2], lw[3]}, sum);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t nn = n0 + wave * 16 + 4 * g + v;
+    if (l16 < M && nn < N) a.y[l16 * N + nn] = f32_to_bf16(sum[v]);
+  }
+}
+
+constexpr int kUfThreads = 256;
+
+__global__ __launch_bounds__(kUfThreads) void k_u_few(UFewArgs a) {
+  __shared__ f32x4 s_red[4][64];
+  __shared__ uint32_t s_ticket;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int jtiles = (a.J + 15) / 16;
+  const int jt = static_cast<int>(blockIdx.x) % jtiles;
+  const int sp = static_cast<int>(blockIdx.x) / jtiles;
+  const int S = a.splits;
+  const int64_t nst = a.K / 32;  // K % 32 == 0
+  const int64_t per = (nst + S - 1) / S;
+  const int64_t st0 = sp * per;
+  const int64_t st1 = st0 + per < nst ? st0 + per : nst;
+  const int j = jt * 16 + l16;
+  const uint16_t* yrow = a.Y + static_cast<int64_t>(j < a.J ? j : a.J - 1) * a.ldy;
+  const uint16_t* xrow = a.X + static_cast<int64_t>(l16 < a.M ? l16 : a.M - 1) * a.ldx;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // wave w takes steps st0 + w, st0 + w + 4, ...; eight steps in flight
+  for (int64_t s0 = st0 + wave; s0 < st1; s0 += 32) {
+    u32x4 ya[8], xb[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t st = s0 + 4 * q;
+      const int64_t k = (st < st1 ? st : s0) * 32 + 8 * g;
+      ya[q] = *reinterpret_cast<const u32x4*>(yrow + k);
+      xb[q] = *reinterpret_cast<const u32x4*>(xrow + k);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (s0 + 4 * q < st1) acc = mfma16(ya[q], xb[q], acc);
+  }
+  // lane (l16, g) holds u[m = l16][j = 16 jt + 4 g + v]; the four waves in order
+  s_red[wave][lane] = acc;
+  __syncthreads();
+  f32x4 sum = s_red[0][lane];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) sum += s_red[w][lane];
+  if (S > 1) {
+    const rsrc_t pr = make_rsrc(a.partial);
+    if (wave == 0) st_sys16(pr, static_cast<uint32_t>(((sp * jtiles + jt) * 64 + lane) * 16), sum);
+    if (__builtin_amdgcn_readfirstlane(publish_and_ticket(a.counters + jt, &s_ticket)) !=
+        static_cast<uint32_t>(S - 1))
+      return;
+    // wave w adds the shares q = w, w + 4, ... in order; then the four
+    // waves' sums in wave order
+    f32x4 ws = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = wave; q0 < S; q0 += 32) {
+      f32x4 part[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int qs = q0 + 4 * q;
+        const int qc = qs < S ? qs : wave;
+        part[q] = ld_sys16(pr, static_cast<uint32_t>(((qc * jtiles + jt) * 64 + lane) * 16));
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q0 + 4 * q < S) ws += part[q];
+    }
+    __syncthreads();
+    s_red[wave][lane] = ws;
+    __syncthreads();
+    sum = s_red[0][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) sum += s_red[w][lane];
+    if (tid == 0) a.counters[jt] = 0u;
+  }
+  if (wave != 0) return;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int jj = jt * 16 + 4 * g + v;
+    if (l16 < a.M && jj < a.J) a.C[l16 * a.ldc + jj] = a.alpha * sum[v];
+  }
+}
+
+}  // namespace
+
+int fwd_stream_row_groups(int64_t N) { return static_cast<int>((N + kFsRows - 1) / kFsRows); }
+int fwd_stream_splits(int64_t N, int64_t K) {
+  const int64_t nchk = (K + kFsChunk - 1) / kFsChunk;
+  const int64_t rg = fwd_stream_row_groups(N);
+  // about as many workgroups as the compute units hold at once
+  int64_t s = (256 * QLIN_FS_WGS_PER_CU + rg - 1) / rg;
+  if (s > nchk) s = nchk;
+  return static_cast<int>(s < 1 ? 1 : s);
+}
+int64_t fwd_stream_partial_floats(int64_t N, int64_t K) {
+  const int S = fwd_stream_splits(N, K);
+  return S > 1 ? static_cast<int64_t>(S) * fwd_stream_row_groups(N) * kFsThreads * 4 : 0;
+}
+
+hipError_t launch_gemv_fwd_stream(const FwdStreamArgs& a, int fmt, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(fwd_stream_row_groups(a.w.N) * a.splits));
+  if (fmt == kFmtNF4)
+    hipLaunchKernelGGL(k_gemv_fwd_stream<kFmtNF4>, grid, dim3(kFsThreads), 0, stream, a);
+  else if (fmt == kFmtINT4)
+    hipLaunchKernelGGL(k_gemv_fwd_stream<kFmtINT4>, grid, dim3(kFsThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_gemv_fwd_stream<kFmtNFG>, grid, dim3(kFsThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+int u_few_tiles(int J) { return (J + 15) / 16; }
+int u_few_splits(int J, int64_t K) {
+  const int64_t nst = K / 32;
+  int64_t s = (256 + u_few_tiles(J) - 1) / u_few_tiles(J);
+  // at least 16 k-steps (4 per wave) per workgroup
+  const int64_t cap = nst / 16 > 0 ? nst / 16 : 1;
+  if (s > cap) s = cap;
+  return static_cast<int>(s < 1 ? 1 : s);
+}
+int64_t u_few_partial_floats(int J, int64_t K) {
+  const int S = u_few_splits(J, K);
+  return S > 1 ? static_cast<int64_t>(S) * u_few_tiles(J) * 256 : 0;
+}
+
+hipError_t launch_u_few(const UFewArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_u_few, dim3(static_cast<uint32_t>(u_few_tiles(a.J) * a.splits)),
+                     dim3(kUfThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace qlin

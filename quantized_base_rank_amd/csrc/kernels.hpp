@@ -169,6 +169,44 @@ struct GemvFwdArgs {
   uint32_t* counters;  // gemv_fwd_tiles
 };
 hipError_t launch_gemv_fwd(const GemvFwdArgs& a, int fmt, hipStream_t stream);
+
+// Few-token forward for large weights (streamed, K split over workgroups):
+// y = x W^T + s u B^T with u given
+struct FwdStreamArgs {
+  WeightView w;
+  const uint16_t* x;   // [M][K], M <= 16
+  int64_t M;
+  const uint16_t* B;   // [N][r]
+  const float* u;      // [M][r] (adapter on)
+  int32_t r;
+  float s;
+  int32_t adapter;
+  uint16_t* y;         // [M][N]
+  int32_t splits;      // fwd_stream_splits(N, K)
+  float* partial;      // fwd_stream_partial_floats(N, K)
+  uint32_t* counters;  // fwd_stream_row_groups(N)
+};
+hipError_t launch_gemv_fwd_stream(const FwdStreamArgs& a, int fmt, hipStream_t stream);
+int fwd_stream_row_groups(int64_t N);
+int fwd_stream_splits(int64_t N, int64_t K);
+int64_t fwd_stream_partial_floats(int64_t N, int64_t K);
+
+// C[m][j] = alpha sum_k X[m][k] Y[j][k] for M <= 16 rows of X, J <= 128
+struct UFewArgs {
+  const uint16_t* X;  int64_t ldx;
+  const uint16_t* Y;  int64_t ldy;
+  float* C;           int64_t ldc;
+  int64_t M, K;       // M <= 16, K % 32 == 0
+  int32_t J;
+  int32_t splits;     // u_few_splits(J, K)
+  float alpha;
+  float* partial;     // u_few_partial_floats(J, K)
+  uint32_t* counters; // u_few_tiles(J)
+};
+hipError_t launch_u_few(const UFewArgs& a, hipStream_t stream);
+int u_few_tiles(int J);
+int u_few_splits(int J, int64_t K);
+int64_t u_few_partial_floats(int J, int64_t K);
 int gemv_fwd_splits(int64_t K);
 int gemv_fwd_tiles(int64_t N);
 int64_t gemv_fwd_kshare(int64_t K);

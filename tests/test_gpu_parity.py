@@ -402,3 +402,16 @@ def test_int4_scale_zero_grad(qb, oracle, d_out, d_in, M):
     parity.check({"dscale": (host(ds).astype(np.float64), da_ref),
                   "dzero": (host(dz).astype(np.float64), db_ref)},
                  fmts={"dscale": "f32", "dzero": "f32"})
+
+
+@pytest.mark.parametrize("d_out,d_in,M,r,fmt,pool", [
+    (4112, 8192, 16, 16, "nf4", 1),    # streamed forward: ragged last row group
+    (4096, 8256, 5, 64, "nf4", 1),     # ragged last chunk (K % 256 == 64), u by the few-token product
+    (4096, 8256, 16, 64, "int4", 32),  # INT4, pooled adapter
+    (2064, 16448, 1, 16, "nf4", 1),    # one token, 17 row groups
+])
+def test_layer_streamed_few_token(qb, oracle, d_out, d_in, M, r, fmt, pool):
+    """Weights above 32 M elements at <= 16 tokens take the streamed forward
+    (K split over ~256 workgroups, ticketed fixed-order fix-up)."""
+    _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r, fmt=fmt, pool=pool)
+    _check(oracle, got, ref)
