@@ -15,10 +15,11 @@ Cache) that every step streams its weight from HBM, and ``value`` is the
 weight-stream rate (2 x packed-weight bytes per step / step time).
 
 ``roofline`` describes the step's dominant kernel as the step launches it:
-its average device duration over the timed steps, measured with HIP events
-on the launch stream (for large M: events recorded by the library around
-that kernel's launch inside every timed step; for few tokens, where each
-call is a single launch, a replayed graph of the same call), against its
+its average device duration, measured with HIP events that the library
+records on the launch stream right around that kernel's launch (large M:
+inside every timed step; few tokens, whose steps are timed as a replayed
+graph: in as many eagerly run steps, each queued behind a spin kernel so that
+the events bracket the kernel and not host launch gaps), against its
 algorithmic flops (MFMA-bound) or bytes (HBM-bound) per launch.
 
 Prints one JSON line.
@@ -62,6 +63,8 @@ def parse():
 TRAFFIC_SOURCES = {
     "k_gemv_fwd": ("quantized_base_rank_amd/csrc/gemv_fwd.hip",),
     "k_gemv_dx": ("quantized_base_rank_amd/csrc/gemv_dx.hip",),
+    "k_gemv_fwd_stream": ("quantized_base_rank_amd/csrc/gemv_stream.hip",),
+    "k_gemv_dx_stream": ("quantized_base_rank_amd/csrc/gemv_dx_stream.hip",),
     "k_fwd_gemm": ("quantized_base_rank_amd/csrc/fwd_gemm.hip",),
     "k_dx_gemm": ("quantized_base_rank_amd/csrc/dx_gemm.hip",),
 }
@@ -107,7 +110,17 @@ def kernel_work(wl, kernel):
         return wbytes + 2 * M * K + 2 * r * Ka + 2 * N * r + 2 * M * N + 4 * M * r, "byte"
     if kernel == "k_gemv_dx":         # W, dY, x, dX, A, B, u, dA, dB
         return (wbytes + 2 * M * N + 4 * M * K + 4 * r * Ka + 4 * N * r + 4 * M * r), "byte"
+    if kernel == "k_gemv_fwd_stream":  # W, x, B, u, y
+        return wbytes + 2 * M * K + 2 * N * r + 4 * M * r + 2 * M * N, "byte"
+    if kernel == "k_gemv_dx_stream":  # W, dY, A, du, dX
+        return wbytes + 2 * M * N + 2 * r * Ka + 4 * M * r + 2 * M * K, "byte"
     raise KeyError(kernel)
+
+
+def streamed(wl):
+    """Few-token layers on weights above 32 M elements run the streamed
+    forward and input-gradient kernels (the library's own rule)."""
+    return wl.M <= 16 and wl.d_out * wl.d_in > (1 << 25)
 
 
 def main():
@@ -213,29 +226,41 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
 
+    def hooked_ms(name, i, lead_cycles):
+        """GPU time of kernel `name` as step i launches it: events recorded by
+        the library right around that launch.  A spin kernel queued first keeps
+        the GPU busy while the host queues the whole step, so the events
+        bracket the kernel alone and not host launch gaps."""
+        ev = (new_event(), new_event())
+        if lead_cycles:
+            torch.cuda._sleep(lead_cycles)
+        qb.qlin_profile_next_launch(name, *ev)
+        step(i)
+        return ev
+
     kernel_ms = {}
     if hbm_bound:
-        # few tokens: each step is a few microseconds, so steps replay from a
-        # captured graph.  qlin_bwd with u saved is one launch (k_gemv_dx),
-        # and so is qlin_fwd when the few-token kernel forms u itself (plain
-        # adapter, r <= 16): a graph of that call alone times that kernel
-        # exactly as the step launches it.
+        # few tokens: each step is tens to hundreds of microseconds, so the
+        # step time comes from a captured graph of steps; the kernels are
+        # timed by events the library records around their launch in
+        # eagerly run steps.
         if args.warmup > 0:
             gw = capture(step, args.warmup)
             gw.replay()
             torch.cuda.synchronize()
         gt = capture(step, args.steps, offset=args.warmup)
         ms_per_step = timed_graph(gt) / args.steps
-        single = [("k_gemv_dx", bwd)]
-        if pool == 1 and r <= 16:
-            single.append(("k_gemv_fwd", fwd))
-        for name, fn in single:
-            gk = capture(fn, args.kernel_iters)
-            gk.replay()
-            kernel_ms[name] = timed_graph(gk) / args.kernel_iters
+        cands = ("k_gemv_fwd_stream", "k_gemv_dx_stream") if streamed(wl) else ("k_gemv_fwd", "k_gemv_dx")
+        lead = 2_000_000  # ~1 ms of spinning at the shader clock
+        for name in cands:
+            ev = hooked_ms(name, 0, lead)
+            torch.cuda.synchronize()
+            kernel_ms[name] = ev[0].elapsed_time(ev[1])
         dominant = max(kernel_ms, key=kernel_ms.get)
-        k_ms = kernel_ms[dominant]
-        timing = "graph replay of the single-launch call"
+        evs = [hooked_ms(dominant, args.warmup + i, lead) for i in range(args.steps)]
+        torch.cuda.synchronize()
+        k_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        timing = "eager steps after a spin kernel; kernel bracketed by events inside each step"
     else:
         # large M: milliseconds per step, launched directly.  After warm-up,
         # one further step per candidate times that candidate; in every timed

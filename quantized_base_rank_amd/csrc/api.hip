@@ -134,6 +134,8 @@ struct Plan {
   bool small = false;
   bool stream = false;  // few tokens, large weight: the streamed forward
   int fs_splits = 1, uf_splits = 1;
+  bool dx_stream = false;  // few tokens, large weight: streamed input gradient
+  int ds_splits = 1;
   bool fits = true;  // the shape's ticket counters fit the fixed region
   int fwd_splits = 1;
   int nt_splits_u = 1, nt_splits_du = 1;
@@ -176,6 +178,8 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.stream = p.small && N * K > (int64_t{1} << 25);
   p.fs_splits = fwd_stream_splits(N, K);
   p.uf_splits = u_few_splits(r > 0 ? r : 1, K);
+  p.dx_stream = p.stream && dx_stream_fits(N, K, fmt_of(w));
+  p.ds_splits = dx_stream_splits(N, K, fmt_of(w));
 
   // counters each kernel takes tickets on (only when it splits a reduction;
   // the few-token backward always does)
@@ -185,6 +189,7 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   if (p.small)
     counters = std::max<int64_t>({counters, p.gf_splits > 1 ? gemv_fwd_tiles(N) : 0, gemv_dx_tiles(K),
                                   p.fs_splits > 1 ? fwd_stream_row_groups(N) : 0,
+                                  p.dx_stream && p.ds_splits > 1 ? dx_stream_panels(K) : 0,
                                   p.uf_splits > 1 ? u_few_tiles(r > 0 ? r : 1) : 0});
   else if (p.fwd_splits > 1)
     counters = std::max<int64_t>(counters, fwd_gemm_tiles(M, N));
@@ -198,6 +203,7 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
                                  gemv_fwd_partial_floats(N, K),
                                  gemv_dx_partial_floats(N, K) + gemv_dx_dupart_floats(N, K, r),
                                  p.stream ? fwd_stream_partial_floats(N, K) : 0,
+                                 p.dx_stream ? dx_stream_partial_floats(N, K, fmt_of(w)) : 0,
                                  u_few_partial_floats(r > 0 ? r : 1, K)});
   } else {
     partial = std::max<int64_t>(partial, fwd_gemm_partial_floats(M, N, p.fwd_splits));
@@ -210,7 +216,7 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.off_Bt = off;       off = align256(off + static_cast<size_t>(N) * r * sizeof(uint16_t));
   p.off_At = off;       off = align256(off + static_cast<size_t>(G) * r * sizeof(uint16_t));
   p.off_P = off;        off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
-  p.off_z = off;        off = align256(off + (p.small ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
+  p.off_z = off;        off = align256(off + (p.small && !p.dx_stream ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
   p.off_partial = off;  off = align256(off + static_cast<size_t>(partial) * sizeof(float));
   p.off_tc = off;       off += transcode_bytes(w);
   p.total = off;
@@ -631,7 +637,7 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     if (st != QLIN_OK) return st;
     u = uw;
   }
-  if (p.small) {
+  if (p.small && !p.dx_stream) {
     // one launch: du, dB, dA and dX folded into the weight-streaming kernel
     GemvDxArgs a{};
     a.w = v; a.x = x; a.dy = dy; a.M = M; a.A = A; a.B = B; a.u = u; a.r = r; a.pool = pool;
@@ -681,6 +687,18 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     QLIN_TRY(hooked("k_qa_dA", stream, [&] { return launch_qa_dA(q, stream); }));
   }
   if (dx == nullptr) return QLIN_OK;
+  if (p.dx_stream) {
+    // few tokens on a large weight: dX streamed, du A added in the fix-up
+    DxStreamArgs a{};
+    a.w = v; a.dy = dy; a.M = M; a.A = A; a.du = du; a.r = r;
+    a.pool_shift = __builtin_ctz(static_cast<unsigned>(pool));
+    a.adapter = (r > 0 && s != 0.0f) ? 1 : 0;
+    a.dx = dx;
+    a.splits = p.ds_splits;
+    a.partial = partial;
+    a.counters = counters;
+    return hip_status(hooked("k_gemv_dx_stream", stream, [&] { return launch_gemv_dx_stream(a, fmt, stream); }));
+  }
   // dX = dY W_bf16 + du A; with the pooled adapter A^T has one row per group
   // and column k of dX reads row k >> log2(pool)
   uint16_t* At = ws_at<uint16_t>(workspace, p.off_At);

@@ -33,46 +33,69 @@ constexpr int kFsWaves = 8;
 constexpr int kFsThreads = 64 * kFsWaves;
 constexpr int kFsRows = 16 * kFsWaves;   // output features per workgroup
 #ifndef QLIN_FS_CHUNK
-#define QLIN_FS_CHUNK 512
+#define QLIN_FS_CHUNK 256
 #endif
 #ifndef QLIN_FS_DEPTH
-#define QLIN_FS_DEPTH 2
+#define QLIN_FS_DEPTH 3
 #endif
 #ifndef QLIN_FS_WGS_PER_CU
-#define QLIN_FS_WGS_PER_CU 1
+#define QLIN_FS_WGS_PER_CU 2  // resident workgroups per compute unit (8 waves each)
 #endif
-constexpr int kFsChunk = QLIN_FS_CHUNK;  // columns per step: 256, 512 or 1024
+constexpr int kFsChunk = QLIN_FS_CHUNK;  // columns per step: 256 or 512
 constexpr int kFsDepth = QLIN_FS_DEPTH;  // steps of loads in flight beyond the current one
+constexpr int kFsR = kFsDepth + 1;       // ring slots = steps per phase of block constants
 constexpr int kFsRun = kFsChunk / 4;     // columns of a lane's run per step (g = 0..3)
 constexpr int kFsBlk = kFsRun / 64;      // 64-column blocks per run
 constexpr int kFsRowBytes = kFsChunk * 2;
+constexpr int kFsXPer = kFsChunk / 256;  // 16-byte token pieces per thread and step (32 threads per token row)
+static_assert(kFsChunk == 256 || kFsChunk == 512, "step width: 256 or 512 columns");
+// Block constants of a phase: kFsPhBlk 64-column blocks of each of the 128
+// rows; thread t fills kFsThBlk consecutive blocks of row t / 4.
+constexpr int kFsPhBlk = kFsR * kFsChunk / 64;
+constexpr int kFsThBlk = kFsPhBlk / 4;
+constexpr int kFsTabStride = kFsRows + 16;  // entries per block (+16: lane groups on other banks)
+static_assert(kFsThBlk % 4 == 0, "a thread's blocks span whole dwords of 8-bit constants");
 
-// Steps per K share: a multiple of the ring depth, so that only the last
-// share runs masked steps.
-__host__ __device__ inline int fwd_stream_per(int nchk, int S) {
-  const int per = (nchk + S - 1) / S;
-  return (per + kFsDepth - 1) / kFsDepth * kFsDepth;
-}
+// Steps per K share (the shares fill the resident workgroup slots evenly;
+// a share's last phase may be partial).
+__host__ __device__ inline int fwd_stream_per(int nchk, int S) { return (nchk + S - 1) / S; }
 
 // Per lane and step: the run of codes of its row (columns kFsRun g ..
-// kFsRun (g + 1) - 1 of the step, kFsBlk 64-column blocks of 32 bytes), the
-// blocks' raw constants, and the token pieces this thread stages.
-constexpr int kFsXPer = kFsChunk / 256;  // 16-byte token pieces per thread and step (32 threads per token row)
-static_assert(kFsChunk % 256 == 0 && kFsChunk <= 1024, "step width: 256, 512 or 1024 columns");
+// kFsRun (g + 1) - 1 of the step, kFsBlk 64-column blocks of 32 bytes) and
+// the token pieces this thread stages.
 struct FsSlot {
   u32x4 c[2 * kFsBlk];
-  BlockParams p[kFsBlk];
   u32x4 x[kFsXPer];
 };
 
-template <int FMT>
-__global__ __launch_bounds__(kFsThreads, QLIN_FS_WGS_PER_CU) void k_gemv_fwd_stream(FwdStreamArgs a) {
+// One table entry per (row, 64-column block): NF4 the fp32 block scale,
+// INT4 / NormalFloat-k groups the two 32-bit group words (scale | zero << 16
+// of groups 2b and 2b + 1).  Zero for blocks outside the share or past K,
+// which then decode to zeros.
+template <int FMT> struct FsEntry { typedef uint32_t type; };
+template <> struct FsEntry<kFmtINT4> { typedef uint2 type; };
+template <> struct FsEntry<kFmtNFG> { typedef uint2 type; };
+
+// Raw constants of one thread's kFsThBlk blocks, loaded one phase ahead.
+template <int FMT, bool DQ>
+struct FsRaw {
+  uint32_t v[FMT == kFmtNF4 ? (DQ ? kFsThBlk / 4 + 3 : kFsThBlk) : 2 * kFsThBlk];
+};
+
+// FMT: weight format.  DQ (NF4): 8-bit block constants with fp32 group
+// constants.  AL: rows of group words start on 16-byte boundaries
+// (K % 256 == 0), so a thread's words load four at a time.
+template <int FMT, bool DQ, bool AL>
+__global__ __launch_bounds__(kFsThreads, 2 * QLIN_FS_WGS_PER_CU) void k_gemv_fwd_stream(FwdStreamArgs a) {
+  typedef typename FsEntry<FMT>::type Entry;
   __shared__ __attribute__((aligned(16))) uint8_t s_x[2][16 * kFsRowBytes];  // token steps
+  __shared__ Entry s_tab[2][kFsPhBlk][kFsTabStride];                         // block constants
   __shared__ uint32_t s_ticket;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t N = a.w.N, K = a.w.K, M = a.M;
+  const int64_t Kb = K >> 6;  // 64-column blocks per row
   const int n_rg = static_cast<int>((N + kFsRows - 1) / kFsRows);
   const int rg = static_cast<int>(blockIdx.x) % n_rg;
   const int ks = static_cast<int>(blockIdx.x) / n_rg;
@@ -82,48 +105,36 @@ __global__ __launch_bounds__(kFsThreads, QLIN_FS_WGS_PER_CU) void k_gemv_fwd_str
   const int c0 = ks * per;
   const int c1 = c0 + per < nchk ? c0 + per : nchk;
   const int64_t n0 = static_cast<int64_t>(rg) * kFsRows;
-  const int64_t n = n0 + wave * 16 + l16;
-  const int64_t nc = n < N ? n : N - 1;
+  const int64_t rows_left = N - n0;  // >= 1
+  const int row = wave * 16 + l16;   // this lane's row in the group
+
+  // codes of the group's rows: rows past N and columns past the last row
+  // read as zeros (buffer range check); a lane's run past K reads the next
+  // row's codes, which meet zero tables
+  const uint32_t cbytes = static_cast<uint32_t>(
+      rows_left * (K >> 1) < 0xFFFFFFFFll ? rows_left * (K >> 1) : 0xFFFFFFFFll);
+  const rsrc_t rc = uniform_rsrc(a.w.codes + n0 * (K >> 1), cbytes);
+  const uint32_t voff_c = static_cast<uint32_t>(row * (K >> 1)) + static_cast<uint32_t>(g * (kFsRun / 2));
 
   // token staging: thread t moves kFsXPer consecutive pieces of token row
   // t >> 5 (rows past M repeat the last token, columns past K the last valid
   // piece; both meet discarded outputs or zero weights)
   const int xrow = tid >> 5, xp0 = (tid & 31) * kFsXPer;
   const int64_t xrc = xrow < M ? xrow : M - 1;
-  auto clampc = [&](int c) { return c < nchk ? c : nchk - 1; };
-  // block j of this lane's run in step c: columns c kFsChunk + kFsRun g + 64 j
-  auto blk_col = [&](int c, int j) { return static_cast<int64_t>(c) * kFsChunk + kFsRun * g + 64 * j; };
-  auto blk_ok = [&](int c, int j) { return c < c1 && blk_col(c, j) < K; };
+  const rsrc_t rx = uniform_rsrc(a.x, static_cast<uint32_t>(M * K * 2));
+  // steps past the share reload its last step (no extra HBM traffic)
+  const int clast = c1 > c0 ? c1 - 1 : nchk - 1;
+  auto clampc = [&](int c) { return c < clast ? c : clast; };
   auto load_slot = [&](int c, FsSlot& sl) {
-    const int cc = clampc(c);
-    // codes: the run's bytes (a block past K reads the row's first bytes and
-    // is masked)
+    const uint32_t off = voff_c + static_cast<uint32_t>(clampc(c) * (kFsChunk / 2));
 #pragma unroll
-    for (int j = 0; j < kFsBlk; ++j) {
-      const int64_t col = blk_col(cc, j);
-      const u32x4* cp = reinterpret_cast<const u32x4*>(a.w.codes + nc * (K >> 1) + (col < K ? col / 2 : 0));
-      sl.c[2 * j] = cp[0];
-      sl.c[2 * j + 1] = cp[1];
-    }
-#pragma unroll
-    for (int j = 0; j < kFsBlk; ++j) {
-      const int64_t col = blk_col(cc, j);
-      const int64_t blk = col < K ? col / 64 : 0;
-      if constexpr (FMT == kFmtNF4) {
-        sl.p[j] = load_block_params<FMT>(a.w, nc, blk, true);
-      } else {
-        // the two 32-bit words with the scales and the zeros of the block's
-        // two groups, split into tables at decode time
-        const int64_t g2 = nc * (K >> 5) + 2 * blk;
-        sl.p[j].a = *reinterpret_cast<const uint32_t*>(a.w.scale + g2);
-        sl.p[j].b = *reinterpret_cast<const uint32_t*>(a.w.zero + g2);
-      }
-    }
+    for (int j = 0; j < 2 * kFsBlk; ++j)
+      sl.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16 * j, 0, 0);
 #pragma unroll
     for (int i = 0; i < kFsXPer; ++i) {
-      int64_t k = static_cast<int64_t>(cc) * kFsChunk + (xp0 + i) * 8;
+      int64_t k = static_cast<int64_t>(clampc(c)) * kFsChunk + (xp0 + i) * 8;
       k = k < K ? k : K - 8;
-      sl.x[i] = *reinterpret_cast<const u32x4*>(a.x + xrc * K + k);
+      sl.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<uint32_t>((xrc * K + k) * 2), 0, 0);
     }
   };
   auto store_x = [&](int buf, const FsSlot& sl) {
@@ -132,34 +143,133 @@ __global__ __launch_bounds__(kFsThreads, QLIN_FS_WGS_PER_CU) void k_gemv_fwd_str
       *reinterpret_cast<u32x4*>(&s_x[buf][xrow * kFsRowBytes + (((xp0 + i) ^ xrow) << 4)]) = sl.x[i];
   };
 
-  // Ring of kFsDepth + 1 steps: all loads of a step are issued together, so
-  // waiting for the token pieces of step c + 1 (stored at the end of step c)
-  // waits only for loads issued kFsDepth steps ago.  The loop body has no
-  // branches (a branch join makes the compiler wait for every load in
-  // flight): steps past the share decode through all-zero tables.
-  constexpr int R = kFsDepth + 1;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  FsSlot ring[R];
+  // block constants: thread t fills blocks gb0 .. gb0 + kFsThBlk - 1 (in the
+  // row) of the phase for row frow of the group (clamped into the weight);
+  // resources start at the group's first row, so offsets stay 32-bit
+  const int frow = tid >> 2, fq = tid & 3;
+  const int64_t frl = n0 + frow < N ? frow : rows_left - 1;
+  auto first_blk = [&](int cb) { return static_cast<int64_t>(cb) * (kFsChunk / 64) + fq * kFsThBlk; };
+  auto cap32 = [](int64_t v) { return static_cast<uint32_t>(v < 0xFFFFFFFFll ? v : 0xFFFFFFFFll); };
+  auto load_raw = [&](int cb, FsRaw<FMT, DQ>& r) {
+    const int64_t gb0 = first_blk(cb);
+    const int64_t gbc = gb0 < Kb ? gb0 : 0;  // past the row: any in-row block (masked)
+    if constexpr (FMT == kFmtNF4 && DQ) {
+      // the aligned dwords holding the 8-bit constants (zeros past the
+      // array), then the group constants of the first and the last block
+      const rsrc_t ra = uniform_rsrc(static_cast<const int8_t*>(a.w.absmax) + n0 * Kb, cap32(rows_left * Kb));
+      const uint32_t a0 = static_cast<uint32_t>(frl * Kb + gbc) & ~3u;
 #pragma unroll
-  for (int d = 0; d < R; ++d) load_slot(c0 + d, ring[d]);
+      for (int i = 0; i <= kFsThBlk / 4; ++i)
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b32(ra, a0 + 4 * i, 0, 0);
+      const int64_t bf = (n0 + frl) * Kb + gbc;
+      const int64_t bl = (n0 + frl) * Kb + (gbc + kFsThBlk - 1 < Kb ? gbc + kFsThBlk - 1 : Kb - 1);
+      r.v[kFsThBlk / 4 + 1] = __float_as_uint(a.w.absmax2[bf >> 8]);
+      r.v[kFsThBlk / 4 + 2] = __float_as_uint(a.w.absmax2[bl >> 8]);
+    } else if constexpr (FMT == kFmtNF4) {
+      const float* am = static_cast<const float*>(a.w.absmax) + (n0 + frl) * Kb;
+#pragma unroll
+      for (int i = 0; i < kFsThBlk; ++i) r.v[i] = __float_as_uint(am[gbc + i < Kb ? gbc + i : Kb - 1]);
+    } else {
+      // 32-bit words holding the fp16 scales (zeros) of groups 2 i, 2 i + 1
+      // of the thread's blocks; past the array they read as zeros
+      const int64_t G = K >> 5;
+      const rsrc_t rs = uniform_rsrc(a.w.scale + n0 * G, cap32(rows_left * G * 2));
+      const rsrc_t rz = uniform_rsrc(a.w.zero + n0 * G, cap32(rows_left * G * 2));
+      const uint32_t off = static_cast<uint32_t>((frl * G + 2 * gbc) * 2);
+      if constexpr (AL) {
+#pragma unroll
+        for (int i = 0; i < kFsThBlk / 4; ++i) {
+          const u32x4 sv = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0);
+          const u32x4 zv = __builtin_amdgcn_raw_buffer_load_b128(rz, off + 16 * i, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r.v[4 * i + e] = sv[e];
+            r.v[kFsThBlk + 4 * i + e] = zv[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kFsThBlk; ++i) {
+          r.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * i, 0, 0);
+          r.v[kFsThBlk + i] = __builtin_amdgcn_raw_buffer_load_b32(rz, off + 4 * i, 0, 0);
+        }
+      }
+    }
+  };
+  auto write_tab = [&](int cb, const FsRaw<FMT, DQ>& r, int buf) {
+    const int64_t gb0 = first_blk(cb);
+    [[maybe_unused]] uint32_t q4[kFsThBlk / 4];
+    [[maybe_unused]] int64_t bf = 0;
+    if constexpr (FMT == kFmtNF4 && DQ) {
+      const int64_t gbc = gb0 < Kb ? gb0 : 0;
+      const uint32_t sh = static_cast<uint32_t>(frl * Kb + gbc) & 3u;  // first byte in r.v[0]
+#pragma unroll
+      for (int k = 0; k < kFsThBlk / 4; ++k) q4[k] = __builtin_amdgcn_alignbyte(r.v[k + 1], r.v[k], sh);
+      bf = (n0 + frl) * Kb + gbc;
+    }
+#pragma unroll
+    for (int i = 0; i < kFsThBlk; ++i) {
+      // the block's step lies in the share and the block in the row
+      const bool ok = cb + (fq * kFsThBlk + i) / (kFsChunk / 64) < c1 && gb0 + i < Kb;
+      Entry e;
+      if constexpr (FMT == kFmtNF4 && DQ) {
+        const int8_t q = static_cast<int8_t>((q4[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+        const bool first = ((bf + i) >> 8) == (bf >> 8);
+        const float s2 = __uint_as_float(first ? r.v[kFsThBlk / 4 + 1] : r.v[kFsThBlk / 4 + 2]);
+        e = ok ? __float_as_uint(nf4_dq_scale(q, s2)) : 0u;
+      } else if constexpr (FMT == kFmtNF4) {
+        e = ok ? r.v[i] : 0u;
+      } else {
+        // group words of the block's two groups: low / high halves of scale
+        // dword i and zero dword i
+        const uint32_t sv = r.v[i], zv = r.v[kFsThBlk + i];
+        e.x = ok ? perm(zv, sv, 0x05040100u) : 0u;
+        e.y = ok ? perm(zv, sv, 0x07060302u) : 0u;
+      }
+      s_tab[buf][fq * kFsThBlk + i][frow] = e;
+    }
+  };
+
+  // Ring of kFsR steps: all loads of a step are issued together, so waiting
+  // for the token pieces of step c + 1 (stored at the end of step c) waits
+  // only for loads issued kFsDepth steps ago.  The loop body has no branches
+  // (a branch join makes the compiler wait for every load in flight): steps
+  // past the share decode through zero tables.  The block constants of the
+  // next phase load at the start of a phase and enter the other table at its
+  // end.
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  FsSlot ring[kFsR];
+  {
+    FsRaw<FMT, DQ> raw;
+    load_raw(c0, raw);
+#pragma unroll
+    for (int d = 0; d < kFsR; ++d) load_slot(c0 + d, ring[d]);
+    write_tab(c0, raw, 0);
+  }
   store_x(c0 & 1, ring[0]);
   __syncthreads();
 
-  for (int cb = c0; cb < c1; cb += R) {
+  int tb = 0;
+  for (int cb = c0; cb < c1; cb += kFsR, tb ^= 1) {
+    FsRaw<FMT, DQ> raw;
+    load_raw(cb + kFsR, raw);
 #pragma unroll
-    for (int d = 0; d < R; ++d) {
+    for (int d = 0; d < kFsR; ++d) {
       const int c = cb + d;
       const uint8_t* xs = s_x[c & 1];
+      // steps past the share (the last phase's tail) skip the arithmetic;
+      // the branch is uniform and holds no loads, so waits are unaffected
+      if (c < c1) {
 #pragma unroll
       for (int j = 0; j < kFsBlk; ++j) {
+        const Entry e = s_tab[tb][d * (kFsChunk / 64) + g * kFsBlk + j][row];
         Lut16 lut[2];
-        const bool ok = blk_ok(c, j);
         if constexpr (FMT == kFmtNF4) {
-          lut[0] = lut_nf4(a.w.cb, nf4_params_scale_sel(a.w, ring[d].p[j], ok));
+          lut[0] = lut_nf4(a.w.cb, __uint_as_float(e));
           lut[1] = lut[0];
         } else {
-          lut[0] = lut_group32<FMT>(a.w.cb, ok ? perm(ring[d].p[j].b, ring[d].p[j].a, 0x05040100u) : 0u);
-          lut[1] = lut_group32<FMT>(a.w.cb, ok ? perm(ring[d].p[j].b, ring[d].p[j].a, 0x07060302u) : 0u);
+          lut[0] = lut_group32<FMT>(a.w.cb, e.x);
+          lut[1] = lut_group32<FMT>(a.w.cb, e.y);
         }
         // k-step t of block j: columns kFsRun g + 64 j + 8 t .. + 7 of the step
 #pragma unroll
@@ -170,11 +280,14 @@ __global__ __launch_bounds__(kFsThreads, QLIN_FS_WGS_PER_CU) void k_gemv_fwd_str
           acc = mfma16(wf, xf, acc);
         }
       }
+      }
       // the next step's tokens into the other buffer (last read before the
-      // previous barrier), then this slot refills with step c + R
-      const int dn = (d + 1) % R;  // (a constant once the loop is unrolled)
+      // previous barrier), then this slot refills with step c + kFsR
+      const int dn = (d + 1) % kFsR;  // (a constant once the loop is unrolled)
       store_x((c + 1) & 1, ring[dn]);
-      load_slot(c + R, ring[d]);
+      if (d == kFsR - 1) write_tab(cb + kFsR, raw, tb ^ 1);
+      load_slot(c + kFsR, ring[d]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the refill here, ahead of later steps' work
       __syncthreads();
     }
   }
@@ -326,8 +439,9 @@ int fwd_stream_row_groups(int64_t N) { return static_cast<int>((N + kFsRows - 1)
 int fwd_stream_splits(int64_t N, int64_t K) {
   const int64_t nchk = (K + kFsChunk - 1) / kFsChunk;
   const int64_t rg = fwd_stream_row_groups(N);
-  // about as many workgroups as the compute units hold at once
-  int64_t s = (256 * QLIN_FS_WGS_PER_CU + rg - 1) / rg;
+  // no more workgroups than the compute units hold at once, so that every
+  // share runs in the first (and only) round
+  int64_t s = 256 * QLIN_FS_WGS_PER_CU / rg;
   if (s > nchk) s = nchk;
   return static_cast<int>(s < 1 ? 1 : s);
 }
@@ -337,13 +451,24 @@ int64_t fwd_stream_partial_floats(int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemv_fwd_stream(const FwdStreamArgs& a, int fmt, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(fwd_stream_row_groups(a.w.N) * a.splits));
-  if (fmt == kFmtNF4)
-    hipLaunchKernelGGL(k_gemv_fwd_stream<kFmtNF4>, grid, dim3(kFsThreads), 0, stream, a);
-  else if (fmt == kFmtINT4)
-    hipLaunchKernelGGL(k_gemv_fwd_stream<kFmtINT4>, grid, dim3(kFsThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_gemv_fwd_stream<kFmtNFG>, grid, dim3(kFsThreads), 0, stream, a);
+  const dim3 grid(static_cast<uint32_t>(fwd_stream_row_groups(a.w.N) * a.splits)), block(kFsThreads);
+  const bool al = a.w.K % 256 == 0;
+  if (fmt == kFmtNF4) {
+    if (a.w.dq)
+      hipLaunchKernelGGL((k_gemv_fwd_stream<kFmtNF4, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemv_fwd_stream<kFmtNF4, false, false>), grid, block, 0, stream, a);
+  } else if (fmt == kFmtINT4) {
+    if (al)
+      hipLaunchKernelGGL((k_gemv_fwd_stream<kFmtINT4, false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemv_fwd_stream<kFmtINT4, false, false>), grid, block, 0, stream, a);
+  } else {
+    if (al)
+      hipLaunchKernelGGL((k_gemv_fwd_stream<kFmtNFG, false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_gemv_fwd_stream<kFmtNFG, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -191,6 +191,26 @@ int fwd_stream_row_groups(int64_t N);
 int fwd_stream_splits(int64_t N, int64_t K);
 int64_t fwd_stream_partial_floats(int64_t N, int64_t K);
 
+// dX = dY W_bf16 + expand(du A) for M <= 16 tokens on a large weight
+struct DxStreamArgs {
+  WeightView w;
+  const uint16_t* dy;   // [M][N], M <= 16
+  int64_t M;
+  const uint16_t* A;    // [r][K >> pool_shift] (adapter on)
+  const float* du;      // [M][r] (adapter on)
+  int32_t r, pool_shift;
+  int32_t adapter;
+  uint16_t* dx;         // [M][K]
+  int32_t splits;       // dx_stream_splits(N, K, fmt)
+  float* partial;       // dx_stream_partial_floats(N, K, fmt)
+  uint32_t* counters;   // dx_stream_panels(K)
+};
+hipError_t launch_gemv_dx_stream(const DxStreamArgs& a, int fmt, hipStream_t stream);
+int dx_stream_panels(int64_t K);
+int dx_stream_splits(int64_t N, int64_t K, int fmt);
+int64_t dx_stream_partial_floats(int64_t N, int64_t K, int fmt);
+bool dx_stream_fits(int64_t N, int64_t K, int fmt);
+
 // C[m][j] = alpha sum_k X[m][k] Y[j][k] for M <= 16 rows of X, J <= 128
 struct UFewArgs {
   const uint16_t* X;  int64_t ldx;

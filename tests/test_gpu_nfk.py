@@ -75,6 +75,8 @@ def test_nf_rejects_nonfinite(qb):
     (2, 256, 528, 1024, 260, 64),   # MFMA path with split-K
     (4, 32, 512, 4160, 16, 64),     # few tokens, K split over 2 workgroups
     (3, 256, 256, 2048, 1, 16),
+    (3, 64, 2064, 16448, 16, 16),   # streamed forward, unaligned group rows
+    (2, 128, 4160, 8192, 4, 16),    # streamed forward, 16-byte aligned group rows
 ])
 def test_layer_nf(qb, oracle, bits, block, d_out, d_in, M, r):
     from quantized_base_rank_amd.inputs import Workload, make_inputs

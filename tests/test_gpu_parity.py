@@ -122,17 +122,17 @@ def test_lut_decode_bit_exact(qb, oracle, fmt, dq):
 
 
 def _layer_case(qb, oracle, d_out, d_in, M, r, s=2.0, fmt="nf4", seed=0, pool=1, zero_w=False,
-                zero_b=False):
+                zero_b=False, dq=256):
     from quantized_base_rank_amd.inputs import Workload, make_inputs
     wl = Workload("case", d_out, d_in, M, r, s, fmt=fmt, block=64 if fmt == "nf4" else 32,
-                  dq_block=256 if fmt == "nf4" else 0, pool=pool)
+                  dq_block=dq if fmt == "nf4" else 0, pool=pool)
     inp = make_inputs(wl, seed=seed)
     W = np.zeros_like(inp.W) if zero_w else inp.W
     B = np.zeros_like(inp.B) if zero_b else inp.B
     if fmt == "nf4":
-        qw = qb.qlin_quantize_nf4(to_dev_f32(W), 64, 256)
-        codes, am, am2 = oracle.quantize_nf4(W, 64, 256)
-        Wd = oracle.bf16_bits_to_f64(oracle.dequant_nf4_bf16(codes, am, am2))
+        qw = qb.qlin_quantize_nf4(to_dev_f32(W), 64, dq)
+        codes, am, am2 = oracle.quantize_nf4(W, 64, dq)
+        Wd = oracle.bf16_bits_to_f64(oracle.dequant_nf4_bf16(codes, am, am2, 64, dq))
     else:
         qw = qb.qlin_quantize_int4_group(to_dev_f32(W), 32)
         codes, sc, zp = oracle.quantize_int4_group(W, 32)
@@ -404,14 +404,16 @@ def test_int4_scale_zero_grad(qb, oracle, d_out, d_in, M):
                  fmts={"dscale": "f32", "dzero": "f32"})
 
 
-@pytest.mark.parametrize("d_out,d_in,M,r,fmt,pool", [
-    (4112, 8192, 16, 16, "nf4", 1),    # streamed forward: ragged last row group
-    (4096, 8256, 5, 64, "nf4", 1),     # ragged last chunk (K % 256 == 64), u by the few-token product
-    (4096, 8256, 16, 64, "int4", 32),  # INT4, pooled adapter
-    (2064, 16448, 1, 16, "nf4", 1),    # one token, 17 row groups
+@pytest.mark.parametrize("d_out,d_in,M,r,fmt,pool,dq", [
+    (4112, 8192, 16, 16, "nf4", 1, 256),    # streamed forward: ragged last row group
+    (4096, 8256, 5, 64, "nf4", 1, 256),     # ragged last chunk (K % 256 == 64), u by the few-token product
+    (4096, 8256, 16, 64, "int4", 32, 0),    # INT4 with unaligned group rows, pooled adapter
+    (4160, 8192, 16, 32, "int4", 32, 0),    # INT4 with 16-byte aligned group rows
+    (4160, 8192, 7, 16, "nf4", 1, 0),       # NF4 with fp32 block constants (no double quantization)
+    (2064, 16448, 1, 16, "nf4", 1, 256),    # one token, 17 row groups
 ])
-def test_layer_streamed_few_token(qb, oracle, d_out, d_in, M, r, fmt, pool):
+def test_layer_streamed_few_token(qb, oracle, d_out, d_in, M, r, fmt, pool, dq):
     """Weights above 32 M elements at <= 16 tokens take the streamed forward
-    (K split over ~256 workgroups, ticketed fixed-order fix-up)."""
-    _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r, fmt=fmt, pool=pool)
+    (K split over the resident workgroups, ticketed fixed-order fix-up)."""
+    _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r, fmt=fmt, pool=pool, dq=dq)
     _check(oracle, got, ref)
