@@ -204,6 +204,8 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
                                  gemv_dx_partial_floats(N, K) + gemv_dx_dupart_floats(N, K, r),
                                  p.stream ? fwd_stream_partial_floats(N, K) : 0,
                                  p.dx_stream ? dx_stream_partial_floats(N, K, fmt_of(w)) : 0,
+                                 p.dx_stream ? adapter_few_partial_floats(N) : 0,
+                                 p.dx_stream && pool > 1 ? qa_dA_partial_floats(M, r, G) : 0,
                                  u_few_partial_floats(r > 0 ? r : 1, K)});
   } else {
     partial = std::max<int64_t>(partial, fwd_gemm_partial_floats(M, N, p.fwd_splits));
@@ -216,7 +218,7 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.off_Bt = off;       off = align256(off + static_cast<size_t>(N) * r * sizeof(uint16_t));
   p.off_At = off;       off = align256(off + static_cast<size_t>(G) * r * sizeof(uint16_t));
   p.off_P = off;        off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
-  p.off_z = off;        off = align256(off + (p.small && !p.dx_stream ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
+  p.off_z = off;        off = align256(off + (p.small ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
   p.off_partial = off;  off = align256(off + static_cast<size_t>(partial) * sizeof(float));
   p.off_tc = off;       off += transcode_bytes(w);
   p.total = off;
@@ -648,19 +650,30 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     a.counters = counters;
     return hip_status(hooked("k_gemv_dx", stream, [&] { return launch_gemv_dx(a, fmt, stream); }));
   }
-  // du = s dY B  (B^T staged so both operands are contiguous along n)
-  QLIN_TRY(hooked("k_transpose16", stream, [&] { return launch_transpose16(B, N, r, Bt, stream); }));
-  {
-    NtArgs a{};
-    a.X = dy; a.ldx = N; a.Y = Bt; a.ldy = N; a.C = du; a.ldc = r;
-    a.M = M; a.K = N; a.J = r; a.splits = p.nt_splits_du; a.alpha = s;
-    a.partial = partial; a.counters = counters;
-    QLIN_TRY(hooked("k_nt_skinny", stream, [&] { return launch_nt_skinny(a, stream); }));
-  }
-  // dB = s dY^T u  (u as bf16 hi/lo planes)
   const int64_t jp = tn2_jp(r);
   uint16_t* zp = ws_at<uint16_t>(workspace, p.off_z);
-  {
+  if (p.dx_stream) {
+    // few tokens: du = s dY B, then dB = s dY^T u and (unpooled) dA = du^T x
+    // in one launch
+    AdapterFewArgs f{};
+    f.dy = dy; f.M = M; f.N = N; f.B = B; f.r = r; f.s = s;
+    f.du = du; f.partial = partial; f.counters = counters;
+    QLIN_TRY(hooked("k_du_few", stream, [&] { return launch_du_few(f, stream); }));
+    DaDbFewArgs d{};
+    d.x = x; d.dy = dy; d.M = M; d.N = N; d.K = K; d.u = u; d.du = du; d.r = r; d.s = s;
+    d.dA = pool == 1 ? dA : nullptr; d.dB = dB;
+    QLIN_TRY(hooked("k_dadb_few", stream, [&] { return launch_dadb_few(d, stream); }));
+  } else {
+    // du = s dY B  (B^T staged so both operands are contiguous along n)
+    QLIN_TRY(hooked("k_transpose16", stream, [&] { return launch_transpose16(B, N, r, Bt, stream); }));
+    {
+      NtArgs a{};
+      a.X = dy; a.ldx = N; a.Y = Bt; a.ldy = N; a.C = du; a.ldc = r;
+      a.M = M; a.K = N; a.J = r; a.splits = p.nt_splits_du; a.alpha = s;
+      a.partial = partial; a.counters = counters;
+      QLIN_TRY(hooked("k_nt_skinny", stream, [&] { return launch_nt_skinny(a, stream); }));
+    }
+    // dB = s dY^T u  (u as bf16 hi/lo planes)
     QLIN_TRY(hooked("k_split_hl", stream, [&] { return launch_split_hl(u, M, r, r, zp, zp + M * jp, stream); }));
     Tn2Args a{};
     a.X = dy; a.ldx = N; a.Zh = zp; a.Zl = zp + M * jp; a.C = dB; a.ldc = r;
@@ -669,7 +682,9 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     QLIN_TRY(hooked("k_tn2", stream, [&] { return launch_tn2(a, stream); }));
   }
   // dA = du^T P
-  if (pool == 1) {
+  if (pool == 1 && p.dx_stream) {
+    // formed above
+  } else if (pool == 1) {
     QLIN_TRY(hooked("k_split_hl", stream, [&] { return launch_split_hl(du, M, r, r, zp + 2 * M * jp, zp + 3 * M * jp, stream); }));
     Tn2Args a{};
     a.X = x; a.ldx = K; a.Zh = zp + 2 * M * jp; a.Zl = zp + 3 * M * jp; a.C = dA; a.ldc = K;

@@ -474,11 +474,12 @@ hipError_t launch_gemv_fwd_stream(const FwdStreamArgs& a, int fmt, hipStream_t s
 
 int u_few_tiles(int J) { return (J + 15) / 16; }
 int u_few_splits(int J, int64_t K) {
+  (void)J;
+  // each wave's k-steps (one in four of a share's) in one round of eight
+  // loads, and the fix-up's shares (eight per wave) in one round as well
   const int64_t nst = K / 32;
-  int64_t s = (256 + u_few_tiles(J) - 1) / u_few_tiles(J);
-  // at least 16 k-steps (4 per wave) per workgroup
-  const int64_t cap = nst / 16 > 0 ? nst / 16 : 1;
-  if (s > cap) s = cap;
+  int64_t s = (nst + 31) / 32;
+  if (s > 32) s = 32;
   return static_cast<int>(s < 1 ? 1 : s);
 }
 int64_t u_few_partial_floats(int J, int64_t K) {
