@@ -22,6 +22,8 @@ Sources (web pages on the subject; cited by page title and section):
   code" (a numpy sketch, captioned as simplified).
 * [QA-LoRA] "QA-LoRA: Quantization-Aware Low-Rank Adaptation of Large
   Language Models" (codewithpapers.app record), abstract.
+* [LQ-LoRA] "LQ-LoRA: Low-rank Plus Quantized Matrix Decomposition for
+  Efficient Language Model Finetuning" (codewithpapers.app record), abstract.
 
 Readings taken where the pages are silent or garbled are tagged [R#] and
 listed in the repository's design notes.
@@ -59,6 +61,14 @@ Parity status per function
                              is "parity unpinned"
 * qa_merge_zero_f16 ....... pinned (exact rational RN16 of beta + s B A,
                              fp16 boundary ties, merged forward error)
+* lq_decompose ............ pinned (rank 0 is plain NF4; on a low-rank plus
+                             noise matrix the rank-r part equals numpy's
+                             truncated SVD and the error its Eckart-Young
+                             value; residual orthogonal to the basis; error
+                             below the rank-0 error and falling with r).  The
+                             iteration itself is a reading of a one-sentence
+                             abstract; agreement with LQ-LoRA's own code is
+                             "parity unpinned"
 * The absolute values of the NF4 levels beyond the stated construction are
   "parity unpinned": the pages print no table of levels.
 """
@@ -705,3 +715,61 @@ def constant_bits_per_param(block: int = 64, dq_block: int = 256) -> float:
     if not dq_block:
         return 32.0 / block
     return 8.0 / block + 32.0 / (block * dq_block)
+
+
+# ---------------------------------------------------------------------------
+# Low-rank plus quantized decomposition  [LQ-LoRA, abstract: each matrix is
+# split iteratively into a quantized part and a high-precision low-rank part]
+# ---------------------------------------------------------------------------
+
+
+def thin_qr_pos(X):
+    """Thin QR of a tall matrix X (rows >= columns, full column rank) with a
+    positive diagonal in R: the unique factorisation X = Q R with
+    Q^T Q = I.  [R27]"""
+    X = np.asarray(X, dtype=F64)
+    q, rr = np.linalg.qr(X, mode="reduced")
+    d = np.sign(np.diag(rr))
+    d[d == 0] = 1.0
+    return q * d, rr * d[:, None]
+
+
+def lowrank_part(R, omega_t, power: int):
+    """Rank-r part of R [N][K] by subspace iteration from the start
+    V0 = omega_t^T (omega_t: r x K, drawn by the caller):
+    U = orth(R V0); `power` times V = orth(R^T U), U = orth(R V); then the
+    projection L = U (U^T R).  Returns U [N][r] and C = U^T R [r][K].  [R27]"""
+    R = np.asarray(R, dtype=F64)
+    om = np.asarray(omega_t, dtype=F64)
+    U, _ = thin_qr_pos(R @ om.T)
+    for _ in range(power):
+        V, _ = thin_qr_pos(R.T @ U)
+        U, _ = thin_qr_pos(R @ V)
+    return U, U.T @ R
+
+
+def lq_decompose(W, r: int, iters: int, power: int, omega_t, block: int = 64,
+                 dq_block: int = 256):
+    """W ~ Q + L with Q an NF4 weight and L = U C of rank r.  [LQ-LoRA,
+    abstract; R26]
+
+    L starts at zero.  Each iteration quantizes W - L (rounded to fp32, the
+    quantizer's input format), takes the residual R = W - W_bf16(Q) against
+    the weight the layer computes with, and replaces L by the rank-r part of
+    R.  Returns (codes, absmax, absmax2, U, C, errs) where errs[t] is
+    ||W - W_bf16(Q_t) - L_t||_F / ||W||_F after iteration t."""
+    W = np.asarray(W, dtype=F64)
+    n, k = W.shape
+    U = np.zeros((n, r), dtype=F64)
+    C = np.zeros((r, k), dtype=F64)
+    wn = float(np.linalg.norm(W))
+    errs = []
+    for _ in range(iters):
+        D = (W - U @ C).astype(F32)
+        codes, am, am2 = quantize_nf4(D, block, dq_block)
+        Wq = bf16_bits_to_f64(dequant_nf4_bf16(codes, am, am2, block, dq_block))
+        R = W - Wq
+        if r > 0:
+            U, C = lowrank_part(R, omega_t, power)
+        errs.append(float(np.linalg.norm(R - U @ C)) / (wn if wn > 0 else 1.0))
+    return codes, am, am2, U, C, errs
