@@ -51,6 +51,11 @@ def parse():
     p.add_argument("--workload", default="down_proj70b")
     p.add_argument("--m", type=int, default=None, help="token count override")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--lq", action="store_true",
+                   help="time the low-rank plus quantized decomposition (qlin_lq_nf4) of the "
+                        "workload's weight instead of the layer step")
+    p.add_argument("--lq-iters", type=int, default=2)
+    p.add_argument("--lq-power", type=int, default=1)
     p.add_argument("--kernel-iters", type=int, default=200,
                    help="few-token workloads: graph-replayed launches for the kernel timing")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -143,6 +148,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(wl, seed=0)
+    if args.lq:
+        return lq_main(args, wl, inp, qb, torch, np, dev)
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -326,6 +333,58 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, hbm_bound, wbytes, flops)
+    print(json.dumps(out), flush=True)
+
+
+def lq_flops(N, K, r, iters, power):
+    """fp32 flops of the decomposition's products: per iteration the range
+    and coordinate products (2 N K r each, 2 + 2 power of them), the
+    orthonormalisations (two CholeskyQR passes of a Gram and an apply,
+    4 r^2 L each) and, after the first, W - U C (2 N K r)."""
+    per = (2 + 2 * power) * 2 * N * K * r + (1 + power) * 2 * 4 * r * r * N + power * 2 * 4 * r * r * K
+    return iters * per + (iters - 1) * 2 * N * K * r
+
+
+def lq_main(args, wl, inp, qb, torch, np, dev):
+    N, K, r = wl.d_out, wl.d_in, wl.r
+    W = torch.from_numpy(np.ascontiguousarray(inp.W, dtype=np.float32)).to(dev)
+    om_np = np.random.default_rng(1).standard_normal((r, K)).astype(np.float32)
+    om = torch.from_numpy(om_np).to(dev)
+    for _ in range(max(args.warmup, 1)):
+        qb.qlin_lq_nf4(W, r, args.lq_iters, args.lq_power, om)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        _, _, _, errs = qb.qlin_lq_nf4(W, r, args.lq_iters, args.lq_power, om)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = lq_flops(N, K, r, args.lq_iters, args.lq_power)
+    out = {"metric": "low-rank plus quantized decomposition (NF4 + rank r), fp32 TFLOP/s",
+           "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_decomposition": round(ms, 3),
+           "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": wl.name, "d_out": N, "d_in": K, "r": r, "iters": args.lq_iters,
+                      "power": args.lq_power, "format": "nf4", "block": 64, "dq_block": 256},
+           "flops_per_decomposition": flops, "errors": [round(float(e), 6) for e in errs.cpu().numpy()],
+           "peak_fp32_tflops": 157.3,
+           "frac_of_fp32_peak": round(flops / (ms * 1e-3) / 1e12 / 157.3, 4)}
+    if not args.no_cpu_baseline:
+        from oracle import qlin_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        rows = 512
+        t0 = time.time()
+        O.lq_decompose(inp.W[:rows].astype(np.float64), r, args.lq_iters, args.lq_power, om_np)
+        sec = time.time() - t0
+        out["cpu_baseline"] = {"value": round(lq_flops(rows, K, r, args.lq_iters, args.lq_power) / sec / 1e12, 6),
+                               "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                               "sample": f"the first {rows} rows of W ({rows}x{K}), same r, iterations, "
+                                         f"power steps and start; {sec:.2f} s"}
     print(json.dumps(out), flush=True)
 
 

@@ -213,6 +213,41 @@ int qlin_quantize_int4_group(const float *W, int64_t d_out, int64_t d_in, int32_
                              hipStream_t stream);
 
 /*
+ * Low-rank plus quantized decomposition W ~ Q + B A of an fp32 weight, with
+ * Q an NF4 weight (blocks of 64) and B A of rank r.  [LQ-LoRA record,
+ * abstract: each pretrained matrix is split iteratively into a quantized
+ * component and a high-precision low-rank component; only the latter is
+ * trained]
+ *
+ *   W        fp32[d_out][d_in] (device); shapes as for qlin_quantize_nf4
+ *   r        rank, 0 .. 128 (and <= d_out, d_in); 0 gives plain NF4
+ *   iters    alternations, >= 1;  power: subspace-iteration steps, >= 0
+ *   omega_t  fp32[r][d_in] (device): start of the subspace iteration, drawn
+ *            by the caller (NULL when r == 0)
+ *   dq_block 0 or 256;  codes, absmax, absmax2: outputs as for
+ *            qlin_quantize_nf4
+ *   B_out    bf16[d_out][r], A_out bf16[r][d_in] (device outputs; NULL when
+ *            r == 0): the layer's adapter with s = 1
+ *   err_out  fp32[iters] (device) or NULL: ||W - W_bf16(Q_t) - L_t|| / ||W||
+ *            (Frobenius) after each iteration
+ *   workspace, ws_bytes: device memory of qlin_lq_workspace_bytes bytes
+ *
+ * L_0 = 0.  Iteration t: Q_t = NF4(W - L_{t-1}) (the qlin_quantize_nf4
+ * rules on the fp32 difference); R = W - W_bf16(Q_t); U = the Q factor of
+ * the thin QR (positive diagonal) of R Omega, then `power` times
+ * V = QR(R^T U), U = QR(R V); L_t = U (U^T R).  B = U and A = U^T R of the
+ * last iteration, rounded to bf16.  All arithmetic is fp32 on the device
+ * (the small r x r Cholesky factorisations in fp64).  Synchronises `stream`
+ * (once per iteration and at the end); QLIN_E_NONFINITE as for
+ * qlin_quantize_nf4; QLIN_E_WORKSPACE if the workspace is too small.
+ */
+size_t qlin_lq_workspace_bytes(int64_t d_out, int64_t d_in, int32_t r);
+int qlin_lq_nf4(const float *W, int64_t d_out, int64_t d_in, int32_t r, int32_t iters, int32_t power,
+                const float *omega_t, int32_t dq_block, uint8_t *codes, void *absmax, float *absmax2,
+                uint16_t *B_out, uint16_t *A_out, float *err_out, void *workspace, size_t ws_bytes,
+                hipStream_t stream);
+
+/*
  * Bytes of device workspace qlin_fwd / qlin_bwd need for this weight, token
  * count M, adapter rank r and pool.  The first 64 KiB of every workspace hold
  * the ticket counters of the split reductions; the workspace must be

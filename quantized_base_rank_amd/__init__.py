@@ -100,6 +100,39 @@ def qlin_quantize_nf4(W, block: int = 64, dq_block: int = 256) -> QWeight:
     return QWeight(QLIN_FMT_NF4, block, dq_block, d_out, d_in, codes, absmax, absmax2)
 
 
+def qlin_lq_nf4(W, r: int, iters: int, power: int, omega_t, dq_block: int = 256):
+    """Low-rank plus quantized decomposition W ~ Q + B A (Q NF4 with blocks of
+    64; B [d_out][r] and A [r][d_in] bf16, for the layer with s = 1).
+    omega_t: fp32 [r][d_in] start of the subspace iteration (drawn by the
+    caller).  Returns (QWeight, B, A, errs) with errs[t] the relative
+    reconstruction error after iteration t."""
+    torch = _torch()
+    d_out, d_in = W.shape
+    _need(W, torch.float32, (d_out, d_in), "W")
+    dev = W.device
+    if r > 0:
+        _need(omega_t, torch.float32, (r, d_in), "omega_t")
+    nb = d_out * d_in // 64
+    codes = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
+    if dq_block:
+        absmax = torch.empty(nb, dtype=torch.int8, device=dev)
+        absmax2 = torch.empty(-(-nb // dq_block), dtype=torch.float32, device=dev)
+    else:
+        absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+        absmax2 = None
+    B = torch.empty((d_out, max(r, 1)), dtype=torch.bfloat16, device=dev)[:, :r]
+    A = torch.empty((max(r, 1), d_in), dtype=torch.bfloat16, device=dev)[:r]
+    errs = torch.empty(iters, dtype=torch.float32, device=dev)
+    nbytes = lib().qlin_lq_workspace_bytes(d_out, d_in, r)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    check(lib().qlin_lq_nf4(W.data_ptr(), d_out, d_in, r, iters, power,
+                            omega_t.data_ptr() if r > 0 else None, dq_block, codes.data_ptr(),
+                            absmax.data_ptr(), _ptr(absmax2), B.data_ptr() if r > 0 else None,
+                            A.data_ptr() if r > 0 else None, errs.data_ptr(), ws.data_ptr(), ws.numel(),
+                            _stream(dev)), "qlin_lq_nf4")
+    return QWeight(QLIN_FMT_NF4, 64, dq_block, d_out, d_in, codes, absmax, absmax2), B, A, errs
+
+
 def qlin_nf_codebook(bits: int) -> np.ndarray:
     out = (ctypes.c_float * 16)()
     check(lib().qlin_nf_codebook(bits, out), "qlin_nf_codebook")

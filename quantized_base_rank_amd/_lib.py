@@ -27,6 +27,8 @@ EXPORTS = (
     "qlin_dequant_bf16",
     "qlin_qa_merge",
     "qlin_int4_scale_zero_grad",
+    "qlin_lq_workspace_bytes",
+    "qlin_lq_nf4",
     "qlin_profile_next_launch",
     "qlin_status_string",
 )
@@ -79,6 +81,9 @@ def lib() -> ctypes.CDLL:
         "qlin_profile_next_launch": (ctypes.c_int, [ctypes.c_char_p, vp, vp]),
         "qlin_qa_merge": (ctypes.c_int, [qp, vp, vp, i32, f32, vp, vp]),
         "qlin_int4_scale_zero_grad": (ctypes.c_int, [qp, vp, i64, vp, vp, vp, vp]),
+        "qlin_lq_workspace_bytes": (sz, [i64, i64, i32]),
+        "qlin_lq_nf4": (ctypes.c_int, [vp, i64, i64, i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz,
+                                       vp]),
         "qlin_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():

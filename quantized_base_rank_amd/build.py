@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libqlin.so")
 
-SOURCES = ["api.hip", "quant.hip", "adapter.hip", "adapter_qa.hip", "adapter_tn.hip", "fwd_gemm.hip", "dx_gemm.hip", "gemv_fwd.hip", "gemv_dx.hip", "merge.hip", "nfk.hip", "loqa.hip", "gemv_stream.hip", "gemv_dx_stream.hip", "adapter_few.hip",
+SOURCES = ["api.hip", "quant.hip", "adapter.hip", "adapter_qa.hip", "adapter_tn.hip", "fwd_gemm.hip", "dx_gemm.hip", "gemv_fwd.hip", "gemv_dx.hip", "merge.hip", "nfk.hip", "loqa.hip", "gemv_stream.hip", "gemv_dx_stream.hip", "adapter_few.hip", "lq.hip",
            "codebook.cpp"]
 
 ARCH = "gfx950"

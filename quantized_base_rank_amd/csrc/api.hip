@@ -738,6 +738,111 @@ int qlin_qa_merge(const qlin_qweight* w, const uint16_t* A, const uint16_t* B, i
   return hip_status(launch_qa_merge(w->zero, A, B, w->d_out, G, r, s, zero_out, stream));
 }
 
+// ------------------------------------------ low-rank plus quantized (LQ)
+
+namespace {
+
+struct LqLayout {
+  size_t off_r = 0, off_ut = 0, off_ct = 0, off_t = 0, off_g = 0, off_uinv = 0, off_p = 0, off_parts = 0,
+         off_sums = 0, total = 0;
+};
+
+LqLayout lq_layout(int64_t N, int64_t K, int32_t r) {
+  LqLayout l;
+  size_t off = 0;
+  const size_t f = sizeof(float);
+  l.off_r = off;     off = align256(off + static_cast<size_t>(N) * K * f);
+  l.off_ut = off;    off = align256(off + static_cast<size_t>(r) * N * f);
+  l.off_ct = off;    off = align256(off + static_cast<size_t>(r) * K * f);
+  l.off_t = off;     off = align256(off + static_cast<size_t>(r) * std::max(N, K) * f);
+  l.off_g = off;     off = align256(off + static_cast<size_t>(r) * r * f);
+  l.off_uinv = off;  off = align256(off + static_cast<size_t>(r) * r * f);
+  l.off_p = off;     off = align256(off + lq_gemm_scratch_floats(N, K, r) * f);
+  l.off_parts = off; off = align256(off + static_cast<size_t>(lq_resid_parts(N * K)) * sizeof(double));
+  l.off_sums = off;  off = align256(off + 4 * sizeof(double));
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+size_t qlin_lq_workspace_bytes(int64_t d_out, int64_t d_in, int32_t r) {
+  if (d_out < 1 || d_in < 1 || r < 0 || r > kMaxRank) return 0;
+  return lq_layout(d_out, d_in, r).total;
+}
+
+int qlin_lq_nf4(const float* W, int64_t d_out, int64_t d_in, int32_t r, int32_t iters, int32_t power,
+                const float* omega_t, int32_t dq_block, uint8_t* codes, void* absmax, float* absmax2,
+                uint16_t* B_out, uint16_t* A_out, float* err_out, void* workspace, size_t ws_bytes,
+                hipStream_t stream) {
+  if (W == nullptr || codes == nullptr || absmax == nullptr) return QLIN_E_NULL;
+  if (dq_block != 0 && absmax2 == nullptr) return QLIN_E_NULL;
+  if (dq_block != 0 && dq_block != 256) return QLIN_E_UNSUPPORTED;
+  if (d_out < 1 || d_in < 1 || d_in % 64 != 0 || d_out % 16 != 0) return QLIN_E_SHAPE;
+  if (d_out > (int64_t{1} << 40) / d_in) return QLIN_E_SHAPE;
+  if (r < 0 || r > kMaxRank || r > d_out || r > d_in || iters < 1 || power < 0) return QLIN_E_SHAPE;
+  if (r > 0 && (omega_t == nullptr || B_out == nullptr || A_out == nullptr)) return QLIN_E_NULL;
+  if (!aligned16(W) || !aligned16(codes) || !aligned16(absmax) || (dq_block != 0 && !aligned16(absmax2)) ||
+      (omega_t != nullptr && !aligned16(omega_t)))
+    return QLIN_E_ALIGN;
+  const LqLayout l = lq_layout(d_out, d_in, r);
+  if (workspace == nullptr || ws_bytes < l.total) return QLIN_E_WORKSPACE;
+  if (!aligned16(workspace)) return QLIN_E_ALIGN;
+  const int64_t N = d_out, K = d_in;
+  float* R = ws_at<float>(workspace, l.off_r);
+  float* Ut = ws_at<float>(workspace, l.off_ut);
+  float* Ct = ws_at<float>(workspace, l.off_ct);
+  LqScratch sc{};
+  sc.G = ws_at<float>(workspace, l.off_g);
+  sc.Uinv = ws_at<float>(workspace, l.off_uinv);
+  sc.T = ws_at<float>(workspace, l.off_t);
+  sc.P = ws_at<float>(workspace, l.off_p);
+  sc.parts = ws_at<double>(workspace, l.off_parts);
+  sc.sums = ws_at<double>(workspace, l.off_sums);
+
+  qlin_qweight q{};
+  q.format = QLIN_FMT_NF4; q.d_out = N; q.d_in = K; q.block = 64; q.dq_block = dq_block;
+  q.codes = codes; q.absmax = absmax; q.absmax2 = dq_block != 0 ? absmax2 : nullptr;
+  const WeightView v = make_view(&q);
+  float cb[16];
+  nf4_levels(cb);
+  double mids[15];
+  for (int i = 0; i < 15; ++i) mids[i] = (static_cast<double>(cb[i]) + static_cast<double>(cb[i + 1])) / 2.0;
+  const int64_t n_blocks = N * K / 64;
+
+  QLIN_TRY(lq_sumsq(W, N * K, sc.sums + 2, sc, stream));
+  for (int t = 0; t < iters; ++t) {
+    // Q_t = NF4(W - L_{t-1}); L_0 = 0 quantizes W itself
+    const float* D = W;
+    if (t > 0 && r > 0) {
+      QLIN_TRY(lq_subtract(W, Ut, Ct, N, K, r, R, sc, stream));
+      D = R;
+    }
+    const int qs = run_flagged(stream, [&](uint32_t* flag) {
+      return launch_quant_nf4(D, n_blocks, dq_block != 0 ? 1 : 0, mids, codes, absmax, absmax2, flag, stream);
+    });
+    if (qs != QLIN_OK) return qs;
+    // R = W - W_bf16(Q_t), |R|^2
+    QLIN_TRY(lq_resid(W, v, R, sc, stream));
+    if (r > 0) {
+      // U = orth(R Omega); power steps V = orth(R^T U), U = orth(R V); C = U^T R
+      QLIN_TRY(lq_range(R, omega_t, N, K, r, Ut, sc, stream));
+      for (int i = 0; i < power; ++i) {
+        QLIN_TRY(lq_coords(R, Ut, N, K, r, Ct, sc, stream));
+        QLIN_TRY(lq_orth(Ct, K, r, sc, stream));
+        QLIN_TRY(lq_range(R, Ct, N, K, r, Ut, sc, stream));
+      }
+      QLIN_TRY(lq_coords(R, Ut, N, K, r, Ct, sc, stream));
+      QLIN_TRY(lq_sumsq(Ct, static_cast<int64_t>(r) * K, sc.sums + 1, sc, stream));
+    } else {
+      QLIN_TRY(lq_sumsq(Ct, 0, sc.sums + 1, sc, stream));
+    }
+    if (err_out != nullptr) QLIN_TRY(lq_err(sc, err_out + t, stream));
+  }
+  if (r > 0) QLIN_TRY(lq_outputs(Ut, Ct, N, K, r, B_out, A_out, stream));
+  return hip_status(hipStreamSynchronize(stream));
+}
+
 int qlin_int4_scale_zero_grad(const qlin_qweight* w, const uint16_t* x, int64_t M,
                               const uint16_t* dy, float* dscale, float* dzero,
                               hipStream_t stream) {

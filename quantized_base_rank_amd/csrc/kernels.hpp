@@ -239,6 +239,30 @@ struct DaDbFewArgs {
 };
 hipError_t launch_dadb_few(const DaDbFewArgs& a, hipStream_t stream);
 
+// Low-rank plus quantized decomposition (lq.hip): device scratch and steps
+struct LqScratch {
+  float* G;       // r x r Gram matrix
+  float* Uinv;    // r x r Cholesky factor of the Gram matrix
+  float* T;       // r x max(N, K)
+  float* P;       // split sums, lq_gemm_scratch_floats
+  double* parts;  // lq_resid_parts(N K) per-workgroup sums
+  double* sums;   // [0] |R|^2, [1] |C|^2, [2] |W|^2
+};
+size_t lq_gemm_scratch_floats(int64_t N, int64_t K, int r);
+int64_t lq_resid_parts(int64_t n_el);
+hipError_t lq_orth(float* X, int64_t L, int r, LqScratch s, hipStream_t st);
+hipError_t lq_range(const float* R, const float* Vt, int64_t N, int64_t K, int r, float* Ut, LqScratch s,
+                    hipStream_t st);
+hipError_t lq_coords(const float* R, const float* Ut, int64_t N, int64_t K, int r, float* Ct, LqScratch s,
+                     hipStream_t st);
+hipError_t lq_subtract(const float* W, const float* Ut, const float* Ct, int64_t N, int64_t K, int r, float* D,
+                       LqScratch s, hipStream_t st);
+hipError_t lq_resid(const float* W, const WeightView& w, float* R, LqScratch s, hipStream_t st);
+hipError_t lq_sumsq(const float* x, int64_t n, double* out, LqScratch s, hipStream_t st);
+hipError_t lq_err(LqScratch s, float* err, hipStream_t st);
+hipError_t lq_outputs(const float* Ut, const float* Ct, int64_t N, int64_t K, int r, uint16_t* B, uint16_t* A,
+                      hipStream_t st);
+
 // C[m][j] = alpha sum_k X[m][k] Y[j][k] for M <= 16 rows of X, J <= 128
 struct UFewArgs {
   const uint16_t* X;  int64_t ldx;

@@ -178,3 +178,16 @@ def test_binding_raises_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_lq_workspace_bytes_host_only():
+    """The decomposition's workspace query is host arithmetic: every rank,
+    including 0 (plain NF4), gets a size that holds the fp32 residual."""
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    f = L.qlin_lq_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+    for r in (0, 1, 8, 64, 128):
+        n = f(512, 1024, r)
+        assert n >= 512 * 1024 * 4 + r * (512 + 1024) * 4
+    assert f(512, 1024, 129) == 0 and f(0, 1024, 8) == 0
