@@ -397,6 +397,32 @@ __device__ __forceinline__ uint32_t publish_and_ticket(uint32_t* counter, uint32
   return *s_ticket;
 }
 
+// ------------------------------------------ tile order of the GEMM kernels
+// The MFMA kernels run one workgroup per compute unit, so 256 workgroups are
+// resident at a time, dealt to the 8 XCDs round-robin (workgroup b on XCD
+// b % 8).  xcd_round_order gives each group of 256 consecutive workgroups a
+// run of 256 consecutive work items, and within it each XCD a contiguous
+// run of 32 (fewer in a last, partial group).  grouped_tile then walks the
+// tile grid in blocks of 4 tile rows, column by column, so that the 32
+// items of one XCD form a 4 x 8 block of tiles: its workgroups share 4 row
+// operands and 8 column operands in that XCD's L2, instead of one row
+// operand and 32 column operands.
+__device__ __forceinline__ int xcd_round_order(int bid, int n) {
+  const int base = bid & ~255;
+  const int cnt = n - base < 256 ? n - base : 256;
+  const int q = cnt >> 3, rem = cnt & 7, b = bid & 255;
+  const int xcd = b & 7, idx = b >> 3;
+  return base + (xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx);
+}
+__device__ __forceinline__ void grouped_tile(int v, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kGroup = 4;
+  const int per = kGroup * tiles_n;
+  const int g = v / per, vin = v - g * per;
+  const int gm = tiles_m - kGroup * g < kGroup ? tiles_m - kGroup * g : kGroup;
+  tm = kGroup * g + vin % gm;
+  tn = vin / gm;
+}
+
 // ------------------------------------------------------------- misc helpers
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

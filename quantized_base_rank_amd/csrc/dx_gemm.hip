@@ -48,12 +48,6 @@ __device__ __forceinline__ int wpos(int c, int n) { return (c + 2 * n + (n >> 2)
 // so that 16 consecutive rows read one chunk from 16 distinct bank groups.
 __device__ __forceinline__ int dsw(int m) { return (m >> 1) & 7; }
 
-__device__ __forceinline__ int remap_xcd(int bid, int n) {
-  const int q = n >> 3, rem = n & 7;
-  const int xcd = bid & 7, idx = bid >> 3;
-  return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
-}
-
 // Raw decode constants of one lane's row segment (64 columns).
 template <int FMT>
 struct RowParams;
@@ -88,9 +82,12 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   const int64_t M = a.M, N = a.w.N, K = a.w.K;
   const int tiles_m = static_cast<int>((M + kTMx - 1) / kTMx);
   const int tiles_k = static_cast<int>((K + kTK - 1) / kTK);
-  const int t = remap_xcd(static_cast<int>(blockIdx.x), tiles_m * tiles_k);
-  const int tm = __builtin_amdgcn_readfirstlane(t / tiles_k);
-  const int tk = __builtin_amdgcn_readfirstlane(t % tiles_k);
+  // tiles in 4 x 8 blocks per XCD (4 token tiles sharing their dY rows, 8
+  // column tiles sharing their packed weight columns)
+  int tm, tk;
+  grouped_tile(xcd_round_order(static_cast<int>(blockIdx.x), tiles_m * tiles_k), tiles_m, tiles_k, tm, tk);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tk = __builtin_amdgcn_readfirstlane(tk);
   const int64_t m0 = static_cast<int64_t>(tm) * kTMx, k0 = static_cast<int64_t>(tk) * kTK;
   // whole pairs of steps (a step past the last one meets weight rows past N,
   // which decode to zero)

@@ -9,7 +9,9 @@
 // decoded exactly once per workgroup, straight from HBM into registers
 // (byte-permute lookup, no LDS), and reused by 8 MFMAs.  The 256x128 bf16
 // token tile of each K step is streamed into LDS with direct-to-LDS loads
-// (double buffered, XOR-swizzled 16-byte chunks: conflict-free reads).
+// in two halves, through a ring of four half-stages that keeps every load
+// about one and a half K steps ahead (XOR-swizzled 16-byte chunks:
+// conflict-free reads); the packed codes follow in two stages.
 // The adapter term is 2*ceil(r/16) extra MFMA k-steps on the same
 // accumulators, with s*u split into hi + lo bf16 halves.
 #include "device_common.hpp"
@@ -22,25 +24,7 @@ namespace {
 constexpr int kTM = 256;
 constexpr int kTN = 256;
 constexpr int kKS = 128;
-constexpr int kXTile = kTM * kKS * 2;  // bytes
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Token tile in LDS: 256 B per row (128 k), 16-byte chunks XOR-swizzled by
-// the row's low four bits so that 16 consecutive rows (the lanes of one
-// LDS cycle) read 16 distinct bank groups.
-__device__ __forceinline__ uint32_t xoff(int row, int chunk) {
-  return static_cast<uint32_t>(row * 256 + ((chunk ^ (row & 15)) << 4));
-}
-
-// Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
-// contiguous run of tiles (tile order: token tile major) so that the
-// workgroups resident on one XCD share their token rows in its L2.
-__device__ __forceinline__ int remap_xcd(int bid, int n) {
-  const int q = n >> 3, rem = n & 7;
-  const int xcd = bid & 7, idx = bid >> 3;
-  return xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
-}
 
 // Raw block constants of one K step for a lane's two rows (the scale is
 // formed when the table is built, so the loads are consumed a step later).
@@ -48,7 +32,8 @@ template <int FMT>
 struct StepParams;
 template <>
 struct StepParams<kFmtNF4> {
-  BlockParams bp[2];  // per row: a = the 8-bit code (DQ), b = fp32 bits of s2 or absmax
+  BlockParams bp[2];  // per row: a = the aligned word holding the 8-bit code (DQ), b = fp32 bits of s2 or absmax
+  uint32_t sh[2];     // per row: bit position of the code in a
 };
 template <>
 struct StepParams<kFmtINT4> {
@@ -111,36 +96,42 @@ __device__ __forceinline__ ParamSrc<kFmtNFG> param_src<kFmtNFG>(const WeightView
   return ps;
 }
 
-// Block constants of K step ks (blocks 2 ks + h).  Near the end of K a lane
-// of the upper half may read the next row's constants (or zeros past the
+// Block constants of K step ks (blocks 2 ks + h), one load per call: part q
+// of 4 is word q % 2 of the lane's row q / 2.  Near the end of K a lane of
+// the upper half may read the next row's constants (or zeros past the
 // array); such blocks are masked when the table is built.
 template <int FMT>
-__device__ __forceinline__ void load_params(const ParamSrc<FMT>& ps, int64_t ks, StepParams<FMT>& p);
+__device__ __forceinline__ void load_params(const ParamSrc<FMT>& ps, int64_t ks, StepParams<FMT>& p, int q);
 template <>
 __device__ __forceinline__ void load_params<kFmtNF4>(const ParamSrc<kFmtNF4>& ps, int64_t ks,
-                                                     StepParams<kFmtNF4>& p) {
-  const uint32_t b2 = static_cast<uint32_t>(2 * ks);
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    p.bp[r].a = __builtin_amdgcn_raw_buffer_load_b8(ps.r8, ps.lb[r], static_cast<int>(b2), 0);
-    p.bp[r].b = __builtin_amdgcn_raw_buffer_load_b32(ps.rw, ((ps.lb[r] + b2) >> ps.sh) << 2, 0, 0);
+                                                     StepParams<kFmtNF4>& p, int q) {
+  // The 8-bit code comes from the aligned word that holds it (the array
+  // length is a multiple of 16 bytes): a byte load whose value is
+  // sign-extended where it is used gets merged with that extension and moved
+  // down to the use, where the wave would then wait for every load in flight.
+  const int r = q >> 1;
+  const uint32_t o = ps.lb[r] + static_cast<uint32_t>(2 * ks);
+  if ((q & 1) == 0) {
+    p.bp[r].a = __builtin_amdgcn_raw_buffer_load_b32(ps.r8, o & ~3u, 0, 0);
+    p.sh[r] = (o & 3u) * 8u;
+  } else {
+    p.bp[r].b = __builtin_amdgcn_raw_buffer_load_b32(ps.rw, (o >> ps.sh) << 2, 0, 0);
   }
 }
 template <>
 __device__ __forceinline__ void load_params<kFmtINT4>(const ParamSrc<kFmtINT4>& ps, int64_t ks,
-                                                      StepParams<kFmtINT4>& p) {
+                                                      StepParams<kFmtINT4>& p, int q) {
   const int g8 = static_cast<int>(8 * ks);  // 4 groups of 2 bytes per step
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
+  const int r = q >> 1;
+  if ((q & 1) == 0)
     p.s[r] = __builtin_amdgcn_raw_buffer_load_b32(ps.rs, ps.lg[r], g8, 0);
+  else
     p.z[r] = __builtin_amdgcn_raw_buffer_load_b32(ps.rz, ps.lg[r], g8, 0);
-  }
 }
-
 template <>
 __device__ __forceinline__ void load_params<kFmtNFG>(const ParamSrc<kFmtNFG>& ps, int64_t ks,
-                                                     StepParams<kFmtNFG>& p) {
-  load_params<kFmtINT4>(ps, ks, p);
+                                                     StepParams<kFmtNFG>& p, int q) {
+  load_params<kFmtINT4>(ps, ks, p, q);
 }
 
 template <int FMT>
@@ -151,7 +142,8 @@ __device__ __forceinline__ Lut16 step_lut<kFmtNF4>(const WeightView& w,
                                                    const StepParams<kFmtNF4>& p, int r, int,
                                                    bool valid) {
   // an invalid block (past K) decodes to zeros through a zero scale
-  return lut_nf4(w.cb, nf4_params_scale_sel(w, p.bp[r], valid));
+  const BlockParams bp{(p.bp[r].a >> p.sh[r]) & 0xFFu, p.bp[r].b};
+  return lut_nf4(w.cb, nf4_params_scale_sel(w, bp, valid));
 }
 template <int FMT>
 __device__ __forceinline__ Lut16 step_lut_group32(const WeightView& w, const StepParams<kFmtINT4>& p,
@@ -173,13 +165,40 @@ __device__ __forceinline__ Lut16 step_lut<kFmtNFG>(const WeightView& w,
   return step_lut_group32<kFmtNFG>(w, p, r, q, valid);
 }
 
-constexpr int kCTile = kTN * kKS / 2;  // packed codes of one K step: 16 KB
+constexpr int kXHalf = kTM * (kKS / 2) * 2;  // token tile of half a K step: 32 KB
+constexpr int kCTile = kTN * kKS / 2;        // packed codes of one K step: 16 KB
+
+// Loads in flight per wave between the two barriers of a K step: the group
+// issued after the first barrier (token half 0: 8 instructions, codes: 4,
+// block constants: 4) and the one after the second (token half 1: 8).
+// Every step issues exactly these (past the range they are clamped or
+// masked, never skipped), so the waits can count them.
+constexpr int kG0Loads = 16;
+constexpr int kG1Loads = 8;
+
+// Waits until at most kG0Loads + kG1Loads of this wave's loads are in
+// flight and its LDS reads are done, then meets the other waves.  Written as
+// one asm block: a fence here would make the compiler wait for every
+// direct-to-LDS load in flight, including the ones that are meant to stay in
+// flight across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(kG0Loads + kG1Loads == 24, "the wait below counts 24 loads");
+  __asm__ volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
-  // two stages of [token tile 64 KB | packed codes 16 KB] = all 160 KB of LDS
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][kXTile + kCTile];
-  uint32_t* s_ticket = reinterpret_cast<uint32_t*>(&s_x[0][0]);  // used after the K loop
+  // Four token half-stages and two code stages, each an array of its own so
+  // that a read of one is never held for direct-to-LDS loads into another:
+  // all 160 KB of LDS.  After the K loop the same memory holds the adapter
+  // operands and the output tile.
+  __shared__ __attribute__((aligned(16))) uint8_t s_x0[kXHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x1[kXHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x2[kXHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_x3[kXHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_c0[kCTile];
+  __shared__ __attribute__((aligned(16))) uint8_t s_c1[kCTile];
+  uint32_t* s_ticket = reinterpret_cast<uint32_t*>(s_c0);  // used after the K loop
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,14 +207,15 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   const int tiles_m = static_cast<int>((M + kTM - 1) / kTM);
   const int tiles_n = static_cast<int>((N + kTN - 1) / kTN);
   const int n_work = tiles_m * tiles_n * a.splits;
-  const int t = remap_xcd(static_cast<int>(blockIdx.x), n_work);
-  const int sp = t % a.splits;
-  const int tmn = t / a.splits;
-  const int tm = tmn / tiles_n, tn = tmn % tiles_n;
+  const int v = xcd_round_order(static_cast<int>(blockIdx.x), n_work);
+  const int sp = v % a.splits;
+  const int tmn = v / a.splits;
+  int tm, tn;
+  grouped_tile(tmn, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = static_cast<int64_t>(tm) * kTM, n0 = static_cast<int64_t>(tn) * kTN;
   const int64_t ksteps = (K + kKS - 1) / kKS;
   const int64_t per = (ksteps + a.splits - 1) / a.splits;
-  const int64_t ks0 = sp * per;
+  const int64_t ks0 = sp * per < ksteps ? sp * per : ksteps;
   const int64_t ks1 = ks0 + per < ksteps ? ks0 + per : ksteps;
 
   int64_t nr[2];
@@ -210,63 +230,83 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms) acc[r][ms] = f32x16{};
 
-  // Token tile source: a buffer resource over this tile's rows of x, so a
-  // load is one instruction with a fixed per-lane offset and a scalar
-  // per-step offset.  Rows past M fall outside the resource (their output
-  // rows are never stored).  When the last K step holds only 64 columns
-  // (K % 128 == 64), its upper eight 16-byte pieces of a row would be the
-  // next token's first columns: their offsets are moved past the resource
-  // (bit 31), so they load zeros and a non-finite value in one token never
-  // reaches another token's output through the zero weights there.
+  // Token half-stage of part p of a K step: [256 m][8 pieces of 16 B], piece
+  // c holding the step's columns 64 (c / 4) + 32 p + 8 (c % 4) .. +7, so that
+  // sub-step 4 p + f reads piece f + 4 h in lane half h (each lane half
+  // walks its own 64-column block).  Pieces sit at c ^ ((m / 2) % 8): 16
+  // consecutive rows read one piece from 16 distinct bank groups.  Loaded by
+  // direct-to-LDS loads through a buffer resource over this tile's rows of
+  // x: instruction i of wave w fills rows 32 i + 8 w .. +7 (1 KB), the
+  // swizzle applied to the source piece.  Rows past M fall outside the
+  // resource (their output rows are never stored).  Pieces past K (the upper
+  // block of a last step that holds only 64 columns) and every piece of a
+  // step past this split's range load zeros (offset bit 31 set), so no
+  // value of another token or step reaches the accumulators.
   const int64_t rows_here = M - m0 < kTM ? M - m0 : kTM;
   const rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.x + m0 * K), 0, static_cast<int>(rows_here * K * 2), 0x00020000);
-  const int lrow = wave * 4 + (lane >> 4);  // row within each group of 16
-  const int xpiece = (lane & 15) ^ lrow;    // 16-byte piece of the step's 128 columns
-  const uint32_t xvoff = static_cast<uint32_t>(lrow * K * 2 + (xpiece << 4));
-  const uint32_t xtail_oob = xpiece >= 8 ? 0x80000000u : 0u;
+  const int xpc = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);  // source piece of this lane
+  const uint32_t xvoff = static_cast<uint32_t>((8 * wave + (lane >> 3)) * K * 2 + 128 * (xpc >> 2) +
+                                               16 * (xpc & 3));
+  const uint32_t xtail_oob = xpc >= 4 ? 0x80000000u : 0u;
   const int64_t ks_tail = (K % kKS) != 0 ? ksteps - 1 : -1;
-  auto load_x = [&](int64_t ks, int buf) {
-    const uint32_t kb2 = static_cast<uint32_t>(ks * kKS * 2);
-    const uint32_t voff = xvoff | (xtail_oob & (ks == ks_tail ? 0xFFFFFFFFu : 0u));
+  auto load_xhalf = [&](int64_t ks, int part, uint8_t* dst, int i0, int n) {
+    const int64_t kc = ks < ks1 ? ks : ks1 - 1;
+    const uint32_t kb2 = static_cast<uint32_t>(kc * kKS * 2 + 64 * part);
+    const uint32_t oob = (ks >= ks1 ? 0x80000000u : 0u) | (ks == ks_tail ? xtail_oob : 0u);
+    const uint32_t voff = xvoff | oob;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (lds_ptr_t)(&s_x[buf][(i * 4 + wave) * 1024]), 16, voff,
-          static_cast<int>(static_cast<uint32_t>(i * 16 * K * 2) + kb2), 0, 0);
+          xr, (lds_ptr_t)(dst + (i * 4 + wave) * 1024), 16, voff,
+          static_cast<int>(static_cast<uint32_t>(i * 32 * K * 2) + kb2), 0, 0);
   };
-  // Packed codes of a K step: 256 rows x 64 B into LDS next to the token
-  // tile.  A load instruction covers 16 rows (4 lanes x 16 B each); the four
-  // 16-byte pieces of a row are XOR-swizzled by (row / 4) % 4 so that the
-  // 16-byte reads of 16 consecutive rows hit distinct banks.  Rows past N
-  // fall outside the resource (their outputs are never stored).
+  // Packed codes of a K step: 256 rows x 64 B in a code stage.  A load
+  // instruction covers 16 rows (4 lanes x 16 B each); the four 16-byte
+  // pieces of a row are XOR-swizzled by (row / 4) % 4 so that the 16-byte
+  // reads of 16 consecutive rows hit distinct banks.  Rows past N fall
+  // outside the resource (their outputs are never stored); a step past the
+  // range re-reads the last one (its tables are zero).
   const int64_t nrows_here = N - n0 < kTN ? N - n0 : kTN;
   const rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(a.w.codes + n0 * (K >> 1)), 0, static_cast<int>(nrows_here * (K >> 1)),
       0x00020000);
   const int cpiece = (lane & 3) ^ ((lane >> 4) & 3);
   const uint32_t cvoff = static_cast<uint32_t>((wave * 16 + (lane >> 2)) * (K >> 1) + cpiece * 16);
-  auto load_codes = [&](int64_t ks, int buf) {
-    const uint32_t kb = static_cast<uint32_t>(ks * (kKS / 2));
+  auto load_codes = [&](int64_t ks, uint8_t* dst, int i0, int n) {
+    const int64_t kc = ks < ks1 ? ks : ks1 - 1;
+    const uint32_t kb = static_cast<uint32_t>(kc * (kKS / 2));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          cr, (lds_ptr_t)(&s_x[buf][kXTile + (i * 4 + wave) * 1024]), 16, cvoff,
+          cr, (lds_ptr_t)(dst + (i * 4 + wave) * 1024), 16, cvoff,
           static_cast<int>(static_cast<uint32_t>(i * 64 * (K >> 1)) + kb), 0, 0);
   };
   // this lane's 16 code words of a step: rows wave*64 + r*32 + l32, half h
-  auto read_codes = [&](int buf, u32x4 (&c)[2][2]) {
+  auto read_codes = [&](const uint8_t* src, u32x4 (&c)[2][2]) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int row = wave * 64 + r * 32 + l32;
       const int sw = (row >> 2) & 3;
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        c[r][q] = *reinterpret_cast<const u32x4*>(&s_x[buf][kXTile + row * 64 + (((2 * h + q) ^ sw) << 4)]);
+        c[r][q] = *reinterpret_cast<const u32x4*>(src + row * 64 + (((2 * h + q) ^ sw) << 4));
     }
   };
   const ParamSrc<FMT> psrc = param_src<FMT>(a.w, nr, h);
-  auto load_step_params = [&](int64_t ks, StepParams<FMT>& p) { load_params<FMT>(psrc, ks, p); };
+  auto load_step_params = [&](int64_t ks, StepParams<FMT>& p, int r) {
+    load_params<FMT>(psrc, ks < ks1 ? ks : ks1 - 1, p, r);
+  };
+  // the load groups of step ks (see kG0Loads), whole or in quarters: G0
+  // quarter q = 2 token pieces, 1 code piece and the constants of row q / 2
+  // (a word or the scale, q even; the other word, q odd); G1 quarter q = 2
+  // token pieces
+  auto issue_g0 = [&](int64_t ks, uint8_t* xdst, uint8_t* cdst, StepParams<FMT>& p, int q) {
+    load_xhalf(ks, 0, xdst, 2 * q, 2);
+    load_codes(ks, cdst, q, 1);
+    load_step_params(ks, p, q);
+  };
+  auto issue_g1 = [&](int64_t ks, uint8_t* xdst, int q) { load_xhalf(ks, 1, xdst, 2 * q, 2); };
 
   constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
   Lut16 lut[2][NL];
@@ -281,125 +321,145 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
     for (int r = 0; r < 2; ++r)
       wf[r] = lut_decode8(lut[r][NL == 1 ? 0 : (tt >> 2)], c[r][tt >> 2][tt & 3]);
   };
-  auto read_x = [&](const uint8_t* xb, int tt, u32x4 (&xf)[8]) {
+  // token fragments of sub-step f (0..7) from that part's half-stage: row
+  // 32 ms + l32, piece (f % 4) + 4 h; the row swizzle (l32 / 2) % 8 does not
+  // depend on ms
+  const int xsw = (l32 >> 1) & 7;
+  auto read_x = [&](const uint8_t* xb, int f, u32x4 (&xf)[8]) {
+    const uint32_t o = static_cast<uint32_t>(l32 * 128 + ((((f & 3) + 4 * h) ^ xsw) << 4));
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms)
-      xf[ms] = *reinterpret_cast<const u32x4*>(xb + xoff(ms * 32 + l32, 8 * h + tt));
+    for (int ms = 0; ms < 8; ++ms) xf[ms] = *reinterpret_cast<const u32x4*>(xb + o + ms * 4096);
   };
-  auto step_valid = [&](int64_t ks) { return ks * kKS + h * 64 < K; };
+  auto step_valid = [&](int64_t ks) { return ks < ks1 && ks * kKS + h * 64 < K; };
 
-  // Tiles and codes run one K step ahead, block constants two.  The stage
-  // barrier sits after sub-step 6: by then every wave has read its last
-  // token fragments of the step, and the next step's data has landed, so
-  // sub-step 7 overlaps its MFMAs with the next step's tables, code reads
-  // and first decode (no bubble at the top of a step).
-  StepParams<FMT> pc, pn, p2;
-  load_x(ks0, 0);
-  load_codes(ks0, 0);
-  load_step_params(ks0, pc);
-  if (ks0 + 1 < ks1) load_step_params(ks0 + 1, pn);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  build_luts(pc, step_valid(ks0));
+  // Pipeline.  The K steps run in pairs: step 2j + SI of the range uses
+  // token half-stages (s_x0, s_x1) or (s_x2, s_x3) and code stage s_c0 or
+  // s_c1 by SI, and block-constant register set P[SI] holds the constants of
+  // step ks + 2 from its load to its use.  Sub-step f reads its fragments
+  // (and decodes its weights) during sub-step f - 1.  Two barriers per step:
+  //   after sub-step 2: part 0 of this step is read by every wave (its
+  //     half-stage is free), and this step's part 1 has landed;
+  //   after sub-step 6: part 1 is read (free), and part 0, codes and
+  //     constants of the next step have landed.
+  // Each freed stage is refilled with step ks + 2, and the refills are spread
+  // evenly over the step, one load every four or eight MFMAs: the load path
+  // of a compute unit takes a 1 KB direct-to-LDS load only every few tens of
+  // cycles, and a wave that issues faster than that stalls, matrix cores
+  // included.  G0 of step ks + 2 goes out a quarter at a time in sub-steps
+  // 3-6 of step ks, G1 in sub-step 7 and sub-steps 0-2 of the next step, so
+  // every load has 8 to 11 sub-steps to land.
+  const int64_t nsteps = ks1 - ks0;
+  const int64_t npairs = (nsteps + 1) >> 1;
+  // The prologue issues the groups of the first two steps in this order, up
+  // to the first quarter of G1 of the second step (the loop issues the rest
+  // in its first three sub-steps), then waits for the first group.
+  // Scheduling barriers keep the constants' loads inside their groups, as
+  // the waits assume.
+  StepParams<FMT> P[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) issue_g0(ks0, s_x0, s_c0, P[0], q);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) issue_g1(ks0, s_x1, q);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) issue_g0(ks0 + 1, s_x2, s_c1, P[1], q);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_g1(ks0 + 1, s_x3, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  static_assert(kG1Loads + kG0Loads + kG1Loads / 4 == 26, "prologue wait");
+  __asm__ volatile("s_waitcnt vmcnt(26)\n\ts_barrier" ::: "memory");
+  build_luts(P[0], step_valid(ks0));
 
   // Two-stage register pipeline over the eight k16 sub-steps of a K step:
   // while the 16 MFMAs of sub-step tt run, the weight words of tt + 1 are
   // decoded and its token fragments read from LDS.
   u32x4 cw[2][2], wf[2][2], xf[2][8];
-  read_codes(0, cw);
-  read_x(s_x[0], 0, xf[0]);
+  read_codes(s_c0, cw);
+  read_x(s_x0, 0, xf[0]);
   decode_w(cw, 0, wf[0]);
-  // The loop body has no branches (a branch splits the scheduling region and
-  // the MFMA / decode interleave is lost), so it is instantiated once per
-  // wave with that wave's load slot fixed, and the loads of a missing next
-  // step are clamped to re-read the current one into the idle stage.
-  auto k_loop = [&](auto wave_c) __attribute__((always_inline)) {
-  constexpr int W = decltype(wave_c)::value;
-  for (int64_t ks = ks0; ks < ks1; ++ks) {
-    const int buf = static_cast<int>((ks - ks0) & 1);
-    const int64_t kn = ks + 1 < ks1 ? ks + 1 : ks;
-    const int64_t kp = ks + 2 < ks1 ? ks + 2 : ks1 - 1;
-    const uint8_t* xb = s_x[buf];
+  // The loop body has no branches: a branch splits the scheduling region,
+  // and the MFMA / decode / load interleave is lost.
+  auto step = [&](int64_t ks, auto si_c) __attribute__((always_inline)) {
+    constexpr int SI = decltype(si_c)::value;
+    uint8_t* const xa = SI == 0 ? s_x0 : s_x2;  // this step, part 0
+    uint8_t* const xb = SI == 0 ? s_x1 : s_x3;  // this step, part 1
+    uint8_t* const xn = SI == 0 ? s_x2 : s_x0;  // next step, part 0
+    uint8_t* const cc = SI == 0 ? s_c0 : s_c1;  // this step's codes (refilled with step ks + 2)
+    uint8_t* const cn = SI == 0 ? s_c1 : s_c0;  // next step's codes
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const int cur = tt & 1, nxt = cur ^ 1;
       if (tt < 7) {
         decode_w(cw, tt + 1, wf[nxt]);
-        read_x(xb, tt + 1, xf[nxt]);
+        read_x(tt + 1 < 4 ? xa : xb, tt + 1, xf[nxt]);
       } else {
         // the next step's tables, codes, first token fragments and first
-        // decode (on the last step: harmless reads of the idle stage)
-        build_luts(pn, step_valid(ks + 1));
-        read_codes(buf ^ 1, cw);
-        read_x(s_x[buf ^ 1], 0, xf[nxt]);
+        // decode (past the range: zero tables)
+        build_luts(P[SI ^ 1], step_valid(ks + 1));
+        read_codes(cn, cw);
+        read_x(xn, 0, xf[nxt]);
         decode_w(cw, 0, wf[nxt]);
       }
+      // refills: G1 of step ks + 1 (quarters 1-3, into the previous step's
+      // part-1 stage), G0 of step ks + 2, the first quarter of its G1
+      if (tt < 3) issue_g1(ks + 1, SI == 0 ? s_x3 : s_x1, tt + 1);
+      if (tt >= 3 && tt < 7) issue_g0(ks + 2, xa, cc, P[SI], tt - 3);
+      if (tt == 7) issue_g1(ks + 2, xb, 0);
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms) {
         acc[0][ms] = mfma32(wf[cur][0], xf[cur][ms], acc[0][ms]);
         acc[1][ms] = mfma32(wf[cur][1], xf[cur][ms], acc[1][ms]);
       }
-      if (tt < 7) {
-        // issue order: the 8 LDS reads of the next sub-step first, then
-        // {1 MFMA, 3 VALU of the next decode} x 16
+      // issue order: the LDS reads of the next sub-step first (8 token
+      // fragments; in sub-step 7 also the 4 code reads), then per MFMA 3 VALU
+      // of the next decode (7 in sub-step 7: the tables as well), and a
+      // refill load after every fourth (sub-steps 3-6) or eighth MFMA
+      constexpr int kVmemEvery[8] = {8, 8, 8, 4, 4, 4, 4, 8};
+      if (tt < 7)
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
-      } else {
-        // the next step's 4 code reads and 8 token-fragment reads first,
-        // then {1 MFMA, 7 VALU of its tables and first decode} x 16
+      else
         __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i % kVmemEvery[tt] == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (tt < 7)
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        else
           __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-        }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // Next step's loads, one wave at a time: a wave blocks while the load
-      // path takes its 1 KB load instructions, so the waves take turns
-      // (wave w after sub-step w) and the other three keep issuing MFMAs.
-      // The target stage was last read before the previous step's barrier.
-      if (tt == W) {
-        load_x(kn, buf ^ 1);
-        load_codes(kn, buf ^ 1);
-        load_step_params(kp, p2);
-      }
-      if (tt == 6) {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-      }
+      if (tt == 2 || tt == 6) stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-    pc = pn;
-    pn = p2;
-  }
   };
-  switch (wave) {
-    case 0: k_loop(std::integral_constant<int, 0>{}); break;
-    case 1: k_loop(std::integral_constant<int, 1>{}); break;
-    case 2: k_loop(std::integral_constant<int, 2>{}); break;
-    default: k_loop(std::integral_constant<int, 3>{}); break;
+  for (int64_t pi = 0; pi < npairs; ++pi) {
+    step(ks0 + 2 * pi, std::integral_constant<int, 0>{});
+    step(ks0 + 2 * pi + 1, std::integral_constant<int, 1>{});
   }
+  // the loads of the two steps past the range land, and every wave is past
+  // its last reads, before the memory is reused
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // adapter term: acc += B[n][j] * (s u[m][j]) over j, in k16 steps, with
   // s u split into hi + lo bf16 halves (two MFMAs per step).  s u of the
   // tile's 256 tokens (as the two halves) and B of its 256 features are
-  // staged in LDS 64 adapter columns at a time (rows padded by 16 B against
-  // bank conflicts), every load of a chunk in flight at once.  Indices are
-  // clamped and values masked (no divergent branches around loads).
+  // staged in LDS 48 adapter columns at a time (rows padded by 16 B against
+  // bank conflicts; each operand fills one 28 KB half-stage), every load of a
+  // chunk in flight at once.  Indices are clamped and values masked (no
+  // divergent branches around loads).
   if (sp == 0 && a.u != nullptr && a.r > 0) {
     const int rr = a.r;
-    constexpr int kJC = 64;          // adapter columns per staged chunk
+    constexpr int kJC = 48;          // adapter columns per staged chunk
     constexpr int rp = kJC + 8;      // staged row length (elements)
     constexpr int q4 = kJC / 4;      // 4-element pieces of a staged row
-    uint16_t* s_uh = reinterpret_cast<uint16_t*>(&s_x[0][0]);  // [256 m][rp]
-    uint16_t* s_ul = s_uh + kTM * rp;                           // [256 m][rp]
-    uint16_t* s_b = s_ul + kTM * rp;                            // [256 n][rp], 110.6 KB in all
-    constexpr int kUPer = kTM * q4 / 256;                       // 16 pieces of each kind per thread
+    static_assert(kTM * rp * 2 <= kXHalf, "a staged operand fits a half-stage");
+    uint16_t* s_uh = reinterpret_cast<uint16_t*>(s_x0);  // [256 m][rp]
+    uint16_t* s_ul = reinterpret_cast<uint16_t*>(s_x1);  // [256 m][rp]
+    uint16_t* s_b = reinterpret_cast<uint16_t*>(s_x2);   // [256 n][rp]
+    constexpr int kUPer = kTM * q4 / 256;                 // 12 pieces of each kind per thread
     for (int jc = 0; jc < rr; jc += kJC) {
       f32x4 uv[kUPer];
       u32x2 bv[kUPer];
@@ -507,33 +567,35 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
 
   // store: lane holds D[n = 8i + 4h + t][m = l32] of each 32x32 tile, i.e.
   // 8 bytes of 32 different output rows per instruction.  The bf16 tile goes
-  // through LDS instead ([256 m][512 B], 16-byte pieces at column piece XOR
-  // the row's low 5 bits), and leaves as whole 16-byte pieces of rows, 32
-  // consecutive threads per 512-byte row.
+  // through LDS instead ([256 m][512 B], rows 64 q .. 64 q + 63 in half-stage
+  // q, 16-byte pieces at column piece XOR the row's low 5 bits), and leaves
+  // as whole 16-byte pieces of rows, 32 consecutive threads per 512-byte row.
   __syncthreads();  // every wave is done with the LDS (adapter operands, ticket)
-  uint8_t* const s_y = &s_x[0][0];
+  uint8_t* const s_y[4] = {s_x0, s_x1, s_x2, s_x3};
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms) {
-      const int row = ms * 32 + l32;
+      const int row = (ms & 1) * 32 + l32;  // within half-stage ms / 2
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int p16 = wave * 8 + r * 4 + i;  // 16-byte piece of the row (columns 8 p16 ..)
         u32x2 o;
         o.x = pack_bf16x2(acc[r][ms][4 * i + 0], acc[r][ms][4 * i + 1]);
         o.y = pack_bf16x2(acc[r][ms][4 * i + 2], acc[r][ms][4 * i + 3]);
-        *reinterpret_cast<u32x2*>(s_y + row * 512 + ((p16 ^ (row & 31)) << 4) + h * 8) = o;
+        *reinterpret_cast<u32x2*>(s_y[ms >> 1] + row * 512 + ((p16 ^ (row & 31)) << 4) + h * 8) = o;
       }
     }
   __syncthreads();
-#pragma unroll 8
-  for (int q = 0; q < 32; ++q) {
-    const int piece = q * 256 + tid, row = piece >> 5, p16 = piece & 31;
-    const int64_t m = m0 + row, n = n0 + p16 * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(s_y + row * 512 + ((p16 ^ (row & 31)) << 4));
-    if (m < M && n < N) *reinterpret_cast<u32x4*>(a.y + m * N + n) = v;
-  }
+#pragma unroll
+  for (int hs = 0; hs < 4; ++hs)
+#pragma unroll 4
+    for (int q = 0; q < 8; ++q) {
+      const int piece = q * 256 + tid, row = piece >> 5, p16 = piece & 31;  // row within the half-stage
+      const int64_t m = m0 + hs * 64 + row, n = n0 + p16 * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(s_y[hs] + row * 512 + ((p16 ^ (row & 31)) << 4));
+      if (m < M && n < N) *reinterpret_cast<u32x4*>(a.y + m * N + n) = v;
+    }
 }
 
 }  // namespace
