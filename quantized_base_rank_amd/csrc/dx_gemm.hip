@@ -32,7 +32,7 @@ constexpr int kTMx = 256;                 // tokens per tile
 constexpr int kNS = 64;                   // reduction rows per step
 constexpr int kWReg = kNS * 64 * 2;       // one wave's decoded slab: 64 rows x 64 columns, 8 KB
 constexpr int kWStage = 4 * kWReg;        // 32 KB
-constexpr int kDyStage = kTMx * kNS * 2;  // 32 KB
+constexpr int kDyHalf = kTMx * (kNS / 2) * 2;  // dY of half a step: 16 KB
 constexpr int kCStage = kNS * kTK / 2;    // packed codes of a step: 8 KB
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -44,16 +44,32 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // the row bits, conflict-free for the reads, made every write wait 8 cycles.
 __device__ __forceinline__ int wpos(int c, int n) { return (c + 2 * n + (n >> 2)) & 7; }
 
-// dY tile [m][64 bf16]: rows of 128 B, 16-byte chunk c at c ^ ((m / 2) % 8),
-// so that 16 consecutive rows read one chunk from 16 distinct bank groups.
-__device__ __forceinline__ int dsw(int m) { return (m >> 1) & 7; }
+// dY half-stage [m][32 bf16] (the rows n of two sub-steps): rows of 64 B,
+// 16-byte piece c at c ^ ((m / 4) % 4), so that 16 consecutive rows read one
+// piece from 16 distinct bank groups.
+__device__ __forceinline__ int dsw(int m) { return (m >> 2) & 3; }
+
+// Loads in flight per wave between two barriers: one K step's loads (dY: 8
+// instructions, codes: 2, decode constants: 2).  Every step issues exactly
+// these (past the range they are clamped or masked, never skipped), so the
+// waits can count them.
+constexpr int kStepLoads = 12;
+
+// Waits until at most one step's loads of this wave are in flight and its
+// LDS accesses are done, then meets the other waves.  One asm block: a fence
+// here would make the compiler wait for every direct-to-LDS load in flight.
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(kStepLoads == 12, "the wait below counts 12 loads");
+  __asm__ volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Raw decode constants of one lane's row segment (64 columns).
 template <int FMT>
 struct RowParams;
 template <>
 struct RowParams<kFmtNF4> {
-  BlockParams bp;
+  BlockParams bp;  // a = the aligned word holding the 8-bit code (DQ)
+  uint32_t sh;     // bit position of the code in a
 };
 template <>
 struct RowParams<kFmtINT4> {
@@ -64,16 +80,19 @@ struct RowParams<kFmtNFG> : RowParams<kFmtINT4> {};  // the same group words
 
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
-  // decoded-weight and dY stages, 128 KB; after the loop the same memory
-  // holds the adapter operands
+  // decoded-weight stages (2 x 32 KB), dY half-stages (4 x 16 KB) and code
+  // stages (2 x 8 KB), each an array of its own so that a read of one is
+  // never held for direct-to-LDS loads into another; after the loop the same
+  // memory holds the adapter operands and the output tile
   __shared__ __attribute__((aligned(16))) uint8_t s_w0[kWStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_w1[kWStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_dy0[kDyStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_dy1[kDyStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dy0[kDyHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dy1[kDyHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dy2[kDyHalf];
+  __shared__ __attribute__((aligned(16))) uint8_t s_dy3[kDyHalf];
   __shared__ __attribute__((aligned(16))) uint8_t s_c0[kCStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_c1[kCStage];
   uint8_t* const s_w[2] = {s_w0, s_w1};
-  uint8_t* const s_dy[2] = {s_dy0, s_dy1};
   uint8_t* const s_c[2] = {s_c0, s_c1};
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -105,30 +124,32 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x16{};
 
-  // dY tile of a step by direct-to-LDS loads: instruction i of wave w
-  // covers rows 32 i + 8 w .. +7 (1 KB), the swizzle applied to the source
-  // chunk.  Rows past M fall outside the resource (their outputs are never
-  // stored).  In the last step of a d_out that is not a multiple of 64, the
-  // pieces past N would be the next token's first values: their offsets are
-  // moved past the resource (bit 31) so they load zeros, and a non-finite
-  // dY value never reaches another token's dX through the zero weights there.
+  // dY half-stage (part p of step st: the step's rows n 32 p .. 32 p + 31)
+  // by direct-to-LDS loads: instruction i of wave w fills tokens
+  // 64 i + 16 w .. +15 (1 KB), the swizzle applied to the source piece.
+  // Rows past M fall outside the resource (their outputs are never stored).
+  // Pieces past N in the last step (they would be the next token's first
+  // values) and every piece of a step past the last one load zeros (offset
+  // bit 31 set), so that a non-finite dY value never reaches another
+  // token's dX through the zero weights there.
   const int64_t dy_rows = M - m0 < kTMx ? M - m0 : kTMx;
   const rsrc_t dyr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.dy + m0 * N), 0, static_cast<int>(dy_rows * N * 2), 0x00020000);
-  const int dlrow = wave * 8 + (lane >> 3);
-  const int dpiece = (lane & 7) ^ dsw(dlrow);  // 16-byte piece of the step's 64 columns
-  const uint32_t dyvoff = static_cast<uint32_t>(dlrow * N * 2 + (dpiece << 4));
-  const int n_tail = static_cast<int>(N % kNS);  // valid columns of the last step (0: all)
-  const uint32_t dtail_oob = (n_tail != 0 && dpiece * 8 >= n_tail) ? 0x80000000u : 0u;
-  auto load_dy = [&](int64_t st, int stage) {
-    const int64_t stc = st < nsteps ? st : nsteps - 1;
-    const uint32_t nb = static_cast<uint32_t>(stc * kNS * 2);
-    const uint32_t voff = dyvoff | (dtail_oob & (stc == nsteps - 1 ? 0xFFFFFFFFu : 0u));
+  const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);  // source piece of this lane
+  const uint32_t dyvoff = static_cast<uint32_t>((wave * 16 + (lane >> 2)) * N * 2 + (dpiece << 4));
+  const int n_tail = static_cast<int>(N % kNS);  // valid rows of the last step (0: all)
+  uint32_t dtail_oob[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+  for (int p = 0; p < 2; ++p) dtail_oob[p] = (n_tail != 0 && 32 * p + 8 * dpiece >= n_tail) ? 0x80000000u : 0u;
+  auto load_dyh = [&](int64_t st, int part, uint8_t* dst, int i0, int n) {
+    const int64_t stc = st < nsteps ? st : nsteps - 1;
+    const uint32_t nb = static_cast<uint32_t>(stc * kNS * 2 + 64 * part);
+    const uint32_t oob = (st >= nsteps ? 0x80000000u : 0u) | (st == nsteps - 1 ? dtail_oob[part] : 0u);
+#pragma unroll
+    for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          dyr, (lds_ptr_t)(s_dy[stage] + (i * 4 + wave) * 1024), 16, voff,
-          static_cast<int>(static_cast<uint32_t>(i * 32 * N * 2) + nb), 0, 0);
+          dyr, (lds_ptr_t)(dst + (i * 4 + wave) * 1024), 16, dyvoff | oob,
+          static_cast<int>(static_cast<uint32_t>(i * 64 * N * 2) + nb), 0, 0);
   };
 
   // Packed codes of a step (64 rows x the tile's 128 bytes) by direct-to-LDS
@@ -143,10 +164,10 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     const int crow = wave * 16 + 8 * i + (lane >> 3);
     cvoff[i] = static_cast<uint32_t>(crow * (K >> 1) + (k0 >> 1) + (((lane & 7) ^ ((crow >> 1) & 7)) << 4));
   }
-  auto dma_codes = [&](int64_t st, int stage) {
+  auto dma_codes = [&](int64_t st, int stage, int i0, int n) {
     const int64_t stc = st < nsteps ? st : nsteps - 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           cr, (lds_ptr_t)(s_c[stage] + (2 * wave + i) * 1024), 16, cvoff[i],
           static_cast<int>(static_cast<uint32_t>(stc * kNS * (K >> 1))), 0, 0);
@@ -175,11 +196,15 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     plane = static_cast<uint32_t>((lane * (K >> 5) + (kwc >> 5)) * 2);
   }
   const uint32_t pshift = a.w.dq ? 8u : 0u;
+  // (the 8-bit code comes from the aligned word that holds it: a byte load
+  // sign-extended at its use gets merged with the extension and sunk to the
+  // use, where the wave would wait for every load in flight)
   auto load_params = [&](int64_t st, RowParams<FMT>& rc) {
     if constexpr (FMT == kFmtNF4) {
-      const uint32_t sb = static_cast<uint32_t>(st * kNS * (K >> 6));
-      rc.bp.a = __builtin_amdgcn_raw_buffer_load_b8(pr0, plane, static_cast<int>(sb), 0);
-      rc.bp.b = __builtin_amdgcn_raw_buffer_load_b32(pr1, ((plane + sb) >> pshift) << 2, 0, 0);
+      const uint32_t o = plane + static_cast<uint32_t>(st * kNS * (K >> 6));
+      rc.bp.a = __builtin_amdgcn_raw_buffer_load_b32(pr0, o & ~3u, 0, 0);
+      rc.sh = (o & 3u) * 8u;
+      rc.bp.b = __builtin_amdgcn_raw_buffer_load_b32(pr1, (o >> pshift) << 2, 0, 0);
     } else {
       const int so = static_cast<int>(st * kNS * (K >> 5) * 2);
       rc.s = __builtin_amdgcn_raw_buffer_load_b32(pr0, plane, so, 0);
@@ -196,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   auto build_lut_part = [&](int set, const RowParams<FMT>& rc, int64_t st, int part) {
     const bool valid = kvalid && st * kNS + lane < N;
     if constexpr (FMT == kFmtNF4) {
-      if (part == 0) lscale[set] = nf4_params_scale_sel(a.w, rc.bp, valid);
+      if (part == 0) lscale[set] = nf4_params_scale_sel(a.w, BlockParams{(rc.bp.a >> rc.sh) & 0xFFu, rc.bp.b}, valid);
       const float sc = lscale[set];
       uint32_t pr[4];
 #pragma unroll
@@ -238,30 +263,55 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         aofs[pn][i][x] =
             static_cast<uint32_t>(wave * kWReg + r * 128 + (wpos(col >> 3, r + 16 * pn) << 4) + ((col >> 2) & 1) * 8);
       }
-  uint32_t bofs[4];
+  // B operand rows: token 32 j + l32, the lane half's 8 rows n of sub-step
+  // 2 q + sub in half-stage q, at piece 2 sub + h
+  uint32_t bofs[2];
 #pragma unroll
-  for (int nn = 0; nn < 4; ++nn)
-    bofs[nn] = static_cast<uint32_t>(l32 * 128 + (((2 * nn + h) ^ dsw(l32)) << 4));
+  for (int sub = 0; sub < 2; ++sub)
+    bofs[sub] = static_cast<uint32_t>(l32 * 64 + (((2 * sub + h) ^ dsw(l32)) << 4));
   auto read_a = [&](int stage, int nn, int i) {
     const uint8_t* wa = s_w[stage] + nn * 16 * 128;
     const u32x2 lo = ds_read_tr16(wa + aofs[nn & 1][i][0]);
     const u32x2 hi = ds_read_tr16(wa + aofs[nn & 1][i][1]);
     return u32x4{lo.x, lo.y, hi.x, hi.y};
   };
-  auto read_b = [&](int stage, int nn, u32x4 (&bf)[8]) {
+  auto read_b = [&](const uint8_t* dyh, int sub, u32x4 (&bf)[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bf[j] = *reinterpret_cast<const u32x4*>(s_dy[stage] + j * 32 * 128 + bofs[nn]);
+    for (int j = 0; j < 8; ++j) bf[j] = *reinterpret_cast<const u32x4*>(dyh + j * 32 * 64 + bofs[sub]);
+  };
+  // dY half-stages of step parity ri: part 0 in s_dy0 / s_dy2, part 1 in
+  // s_dy1 / s_dy3
+  auto dyh_of = [&](int ri, int part) -> uint8_t* {
+    return ri == 0 ? (part == 0 ? s_dy0 : s_dy1) : (part == 0 ? s_dy2 : s_dy3);
   };
 
-  // Prologue: dY of steps 0 and 1 in LDS, codes of steps 1 and 2 in
-  // registers, step 0 decoded and the tables of step 1 built before the
-  // loop.
+  // Pipeline.  One step st (ri = st & 1: weight stage, dY half-stages, table
+  // and constant set of step st + 2) runs the products of st while step
+  // st + 1 is decoded from the code registers into the other weight stage
+  // (three, three and two words in sub-steps 0, 1, 2) and the tables of step
+  // st + 2 are built (sub-steps 2 and 3).  Sub-step nn reads the operands of
+  // nn + 1 (in sub-step 3: the first column tile and dY of st + 1, and this
+  // lane's codes of st + 2; the second column tile at the top of st + 1).
+  // Two barriers per step:
+  //   after sub-step 0: dY part 0 of st is read by every wave (free), and
+  //     part 1 of st has landed;
+  //   after sub-step 2: part 1 of st is read (free), and part 0 of st + 1
+  //     and the codes of st + 2 have landed; every wave has read its codes
+  //     of st + 1 (that code stage is free).
+  // Refills, spread over the step (a burst of direct-to-LDS loads stalls the
+  // issuing wave, matrix cores included): sub-step 0: the last half of dY
+  // part 1 of st + 1; 1 and 2: dY part 0 of st + 2 and the codes of st + 3;
+  // 3: the constants of st + 3 and the first half of dY part 1 of st + 2.
+  // Every load has 4-5 sub-steps to land.
+  //
+  // Prologue: dY of step 0, codes of steps 0 and 1 and the constants of
+  // steps 0 and 1 land; step 0 is decoded and the tables of step 1 built;
+  // then the loads that the loop expects in flight go out in its order.
   RowParams<FMT> rc[2];
-  load_dy(0, 0);
-  load_dy(1, 1);
-  dma_codes(0, 0);
-  dma_codes(1, 1);
+  load_dyh(0, 0, s_dy0, 0, 4);
+  load_dyh(0, 1, s_dy1, 0, 4);
+  dma_codes(0, 0, 0, 2);
+  dma_codes(1, 1, 0, 2);
   load_params(0, rc[0]);
   load_params(1, rc[1]);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -273,29 +323,24 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   for (int q = 0; q < 8; ++q) decode_word(0, q, 0);
   build_lut_part(1, rc[1], 1, 0);
   build_lut_part(1, rc[1], 1, 1);
-  load_params(2, rc[0]);
   read_codes(1);
   __syncthreads();  // every wave has read its step-0 codes
-  dma_codes(2, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_dyh(1, 0, s_dy2, 0, 2);
+  dma_codes(2, 0, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_dyh(1, 0, s_dy2, 2, 2);
+  dma_codes(2, 0, 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_params(2, rc[0]);
+  load_dyh(1, 1, s_dy3, 0, 2);
+  __builtin_amdgcn_sched_barrier(0);
 
   u32x4 af[2][2], bf[2][8];
   af[0][0] = read_a(0, 0, 0);
-  read_b(0, 0, bf[0]);
-  // One step st (ri = st & 1: dY and weight stage, table and constant set
-  // of step st + 2): the products of st while step st + 1 is decoded from
-  // the code registers into the other weight stage (three, three and two
-  // words in sub-steps 0, 1, 2), and the tables of step st + 2 are built in
-  // sub-steps 2 and 3.  After sub-step 2 the stage barrier (the dY of st + 1
-  // and the codes of st + 2 have landed; every wave has read its last dY
-  // fragments of st and its codes of st + 1).  Sub-step 3 reads the first
-  // column tile and the dY fragments of st + 1 and this lane's codes of
-  // st + 2; the second column tile is read at the top of st + 1, under the
-  // first tile's products.  Loads: waves 0, 1 take the dY of st + 2 and the
-  // codes of st + 3 right after the barrier, waves 2, 3 after sub-step 3 (so
-  // that two waves keep the matrix cores busy while the other two issue);
-  // the constants of st + 3 load after sub-step 3.
-  auto k_loop = [&](auto early_c) __attribute__((always_inline)) {
-  constexpr bool early = decltype(early_c)::value;
+  read_b(s_dy0, 0, bf[0]);
+  // The loop body has no branches: a branch splits the scheduling region,
+  // and the MFMA / decode / load interleave is lost.
   auto step = [&](int64_t st, auto ri_c) __attribute__((always_inline)) {
     constexpr int ri = decltype(ri_c)::value;
 #pragma unroll
@@ -305,10 +350,10 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
       if (nn < 3) {
         af[nxt][0] = read_a(ri, nn + 1, 0);
         af[nxt][1] = read_a(ri, nn + 1, 1);
-        read_b(ri, nn + 1, bf[nxt]);
+        read_b(dyh_of(ri, (nn + 1) >> 1), (nn + 1) & 1, bf[nxt]);
       } else {
         af[nxt][0] = read_a(ri ^ 1, 0, 0);
-        read_b(ri ^ 1, 0, bf[nxt]);
+        read_b(dyh_of(ri ^ 1, 0), 0, bf[nxt]);
       }
       // words 0-2, 3-5 and 6-7 of the next step's row in sub-steps 0, 1, 2
 #pragma unroll
@@ -319,53 +364,45 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         build_lut_part(ri, rc[ri], st + 2, 1);
         read_codes(ri);
       }
+      // refills (see above)
+      if (nn == 0) load_dyh(st + 1, 1, dyh_of(ri ^ 1, 1), 2, 2);
+      if (nn == 1 || nn == 2) {
+        load_dyh(st + 2, 0, dyh_of(ri, 0), 2 * (nn - 1), 2);
+        dma_codes(st + 3, ri ^ 1, nn - 1, 1);
+      }
+      if (nn == 3) {
+        // the constants first: their use waits for them and every older load
+        load_params(st + 3, rc[ri ^ 1]);
+        load_dyh(st + 2, 1, dyh_of(ri, 1), 0, 2);
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
-      // issue order: the operand reads of the next sub-step first (the
-      // LDS, not the matrix cores, is the tighter resource here), then
-      // {1 MFMA, 5 VALU of the decode} x 16
+      // issue order: the operand reads of the next sub-step first (the LDS,
+      // not the matrix cores, is the tighter resource here), then per MFMA
+      // 5 VALU of the decode, and a refill load after every fourth, sixth or
+      // eighth MFMA
+      constexpr int kVmemEvery[4] = {8, 6, 6, 4};
       if (nn == 0)
         __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
-      else if (nn < 3)
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
       else
         __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (g % kVmemEvery[nn] == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (nn == 2) {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (early) {
-          load_dy(st + 2, ri);
-          dma_codes(st + 3, ri ^ 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (nn == 3) {
-        if (!early) {
-          load_dy(st + 2, ri);
-          dma_codes(st + 3, ri ^ 1);
-        }
-        load_params(st + 3, rc[ri ^ 1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      if (nn == 0 || nn == 2) stage_barrier();
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int64_t sp = 0; sp < npairs; ++sp) {
     step(2 * sp, std::integral_constant<int, 0>{});
     step(2 * sp + 1, std::integral_constant<int, 1>{});
   }
-  };
-  if (wave < 2)
-    k_loop(std::true_type{});
-  else
-    k_loop(std::false_type{});
   // every load has landed and every wave is past its reads before the
   // memory is reused
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -373,7 +410,8 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 
   // adapter term du A: D[k][m] += sum_j A^T[k][j] du[m][j], in k16 steps,
   // du split into hi + lo bf16 halves.  du of the tile's 256 tokens (as the
-  // two halves) and A^T of its 256 columns are staged in LDS 48 adapter
+  // two halves, in the weight stages) and A^T of its 256 columns (rows
+  // 0-127 and 128-255 in two dY half-stages) are staged in LDS 48 adapter
   // columns at a time (rows padded by 16 B against bank conflicts), every
   // load of a chunk in flight at once.  Indices are clamped and values
   // masked (no divergent branches around loads).
@@ -384,7 +422,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     constexpr int q4 = kJC / 4;      // 4-element pieces of a staged row
     uint16_t* s_dh = reinterpret_cast<uint16_t*>(s_w0);   // [256 m][rp]
     uint16_t* s_dl = reinterpret_cast<uint16_t*>(s_w1);   // [256 m][rp]
-    uint16_t* s_at = reinterpret_cast<uint16_t*>(s_dy0);  // [256 k][rp]
+    static_assert(128 * rp * 2 <= kDyHalf, "half of A^T fits a dY half-stage");
+    // A^T row k of the tile: [128][rp] in s_dy0 (k < 128) or s_dy1
+    auto s_at = [&](int k) { return reinterpret_cast<uint16_t*>(k < 128 ? s_dy0 : s_dy1) + (k & 127) * rp; };
     constexpr int kUPer = kTMx * q4 / 256;                 // 12 pieces of each kind per thread
     for (int jc = 0; jc < rr; jc += kJC) {
       f32x4 dv[kUPer];
@@ -425,7 +465,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         *reinterpret_cast<u32x2*>(s_dl + row * rp + jl) = u32x2{pack_bf16x2(lv[0], lv[1]), pack_bf16x2(lv[2], lv[3])};
         const uint32_t k0m = (j < rr ? 0x0000FFFFu : 0u) | (j + 1 < rr ? 0xFFFF0000u : 0u);
         const uint32_t k1m = (j + 2 < rr ? 0x0000FFFFu : 0u) | (j + 3 < rr ? 0xFFFF0000u : 0u);
-        *reinterpret_cast<u32x2*>(s_at + row * rp + jl) = u32x2{av[q].x & k0m, av[q].y & k1m};
+        *reinterpret_cast<u32x2*>(s_at(row) + jl) = u32x2{av[q].x & k0m, av[q].y & k1m};
       }
       __syncthreads();
       const int jt_n = (rr - jc < kJC ? rr - jc + 15 : kJC) / 16;
@@ -434,7 +474,7 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         u32x4 at[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          at[i] = *reinterpret_cast<const u32x4*>(s_at + (wave * 64 + i * 32 + l32) * rp + j0);
+          at[i] = *reinterpret_cast<const u32x4*>(s_at(wave * 64 + i * 32 + l32) + j0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int ml = j * 32 + l32;
@@ -452,13 +492,17 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 
   // store: lane holds D[k = 8q + 4h + t][m = l32] of each 32x32 tile, i.e.
   // 8 bytes of 32 different output rows per instruction.  The bf16 tile goes
-  // through LDS instead (tokens 64 s .. 64 s + 63 in the stage array s, 512 B
-  // per token, 16-byte pieces at column piece XOR the token's low 5 bits) and
-  // leaves as whole 16-byte pieces of rows, 32 consecutive threads per row.
+  // through LDS instead (512 B per token: tokens 0-63 in s_w0, 64-127 in
+  // s_w1, then 32 each in the four dY half-stages; 16-byte pieces at column
+  // piece XOR the token's low 5 bits) and leaves as whole 16-byte pieces of
+  // rows, 32 consecutive threads per row.
   __syncthreads();  // every wave is done with the LDS (adapter operands)
-  // (a select, not an array of the four addresses: such an array would be
-  // emitted as a constant table of LDS addresses, which has no encoding)
-  auto s_out = [&](int i) -> uint8_t* { return i == 0 ? s_w0 : i == 1 ? s_w1 : i == 2 ? s_dy0 : s_dy1; };
+  // token row -> its staging row (the row is known at compile time in both
+  // loops below, so the selects fold away)
+  auto s_out = [&](int row) -> uint8_t* {
+    uint8_t* const b = row < 64 ? s_w0 : row < 128 ? s_w1 : row < 160 ? s_dy0 : row < 192 ? s_dy1 : row < 224 ? s_dy2 : s_dy3;
+    return b + (row < 128 ? (row & 63) : (row & 31)) * 512;
+  };
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -470,15 +514,18 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         u32x2 o;
         o.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
         o.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        *reinterpret_cast<u32x2*>(s_out(j >> 1) + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4) + h * 8) = o;
+        *reinterpret_cast<u32x2*>(s_out(j * 32) + (l32 & (j < 4 ? 63 : 31)) * 512 +
+                                  ((p16 ^ (row & 31)) << 4) + h * 8) = o;
       }
     }
   __syncthreads();
-#pragma unroll 8
+#pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int piece = q * 256 + tid, row = piece >> 5, p16 = piece & 31;
     const int64_t m = m0 + row, k = k0 + p16 * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(s_out(q >> 3) + (row & 63) * 512 + ((p16 ^ (row & 31)) << 4));
+    // rows 8 q .. 8 q + 7: one staging array per q
+    const u32x4 v = *reinterpret_cast<const u32x4*>(s_out(q * 8) + (row - q * 8) * 512 +
+                                                    ((p16 ^ (row & 31)) << 4));
     if (m < M && k < K) *reinterpret_cast<u32x4*>(a.dx + m * K + k) = v;
   }
 }
