@@ -118,11 +118,16 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   const bool kvalid = kw < K;
   const int64_t kwc = kvalid ? kw : k0;
 
-  f32x16 acc[2][8];
+  // products: wave w = 2 wk + wm owns dX columns [128 wk, 128 wk + 128) of
+  // the tile (4 column tiles of 32) for tokens [128 wm, 128 wm + 128) (4
+  // token tiles of 32); it decodes the weights of columns [64 w, 64 w + 64)
+  // (its slab), half of what it and its neighbour (w ^ 1) read.
+  const int wk = wave >> 1, wm = wave & 1;
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   // dY half-stage (part p of step st: the step's rows n 32 p .. 32 p + 31)
   // by direct-to-LDS loads: instruction i of wave w fills tokens
@@ -245,12 +250,15 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   };
 
   // MFMA operands of sub-step nn (rows 16 nn .. 16 nn + 15 of the step).
-  // A = W^T: for column tile i, lane p of each 16-lane group points at row
-  // 8 h + p / 4 (+ 4), columns 32 i + (l32 & 16) + 4 (p % 4) .. +3 of the
-  // slab; the transposing read hands lane t column 32 i + (l32 & 16) + t.
-  // B = dY^T: token 32 j + l32, reduction chunk 2 nn + h.  Row terms of nn
-  // and j are immediate offsets (the piece placement repeats every 32 rows,
-  // so the A offsets come in two sets, for even and odd nn).
+  // A = W^T: column tile i lies in slab 2 wk + i / 2; lane p of each 16-lane
+  // group points at row 8 h + p / 4 (+ 4), columns 32 (i % 2) + (l32 & 16)
+  // + 4 (p % 4) .. +3 of that slab; the transposing read hands lane t column
+  // 32 (i % 2) + (l32 & 16) + t.  B = dY^T: token 128 wm + 32 j + l32,
+  // reduction chunk 2 nn + h.  Row terms of nn, the slab and j are immediate
+  // offsets (the piece placement repeats every 32 rows, so the A offsets
+  // come in two sets, for even and odd nn).  Slabs are written by other
+  // waves: the stage barrier after sub-step 2 orders a step's decode (sub-
+  // steps 0-2 of the step before) before its first reads (sub-step 3).
   uint32_t aofs[2][2][2];
 #pragma unroll
   for (int pn = 0; pn < 2; ++pn)
@@ -261,23 +269,23 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         const int r = 8 * h + (l16 >> 2) + 4 * x;
         const int col = 32 * i + (l32 & 16) + 4 * (l16 & 3);
         aofs[pn][i][x] =
-            static_cast<uint32_t>(wave * kWReg + r * 128 + (wpos(col >> 3, r + 16 * pn) << 4) + ((col >> 2) & 1) * 8);
+            static_cast<uint32_t>(2 * wk * kWReg + r * 128 + (wpos(col >> 3, r + 16 * pn) << 4) + ((col >> 2) & 1) * 8);
       }
   // B operand rows: token 32 j + l32, the lane half's 8 rows n of sub-step
   // 2 q + sub in half-stage q, at piece 2 sub + h
   uint32_t bofs[2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
-    bofs[sub] = static_cast<uint32_t>(l32 * 64 + (((2 * sub + h) ^ dsw(l32)) << 4));
+    bofs[sub] = static_cast<uint32_t>((128 * wm + l32) * 64 + (((2 * sub + h) ^ dsw(l32)) << 4));
   auto read_a = [&](int stage, int nn, int i) {
-    const uint8_t* wa = s_w[stage] + nn * 16 * 128;
-    const u32x2 lo = ds_read_tr16(wa + aofs[nn & 1][i][0]);
-    const u32x2 hi = ds_read_tr16(wa + aofs[nn & 1][i][1]);
+    const uint8_t* wa = s_w[stage] + nn * 16 * 128 + (i >> 1) * kWReg;
+    const u32x2 lo = ds_read_tr16(wa + aofs[nn & 1][i & 1][0]);
+    const u32x2 hi = ds_read_tr16(wa + aofs[nn & 1][i & 1][1]);
     return u32x4{lo.x, lo.y, hi.x, hi.y};
   };
-  auto read_b = [&](const uint8_t* dyh, int sub, u32x4 (&bf)[8]) {
+  auto read_b = [&](const uint8_t* dyh, int sub, u32x4 (&bf)[4]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bf[j] = *reinterpret_cast<const u32x4*>(dyh + j * 32 * 64 + bofs[sub]);
+    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(dyh + j * 32 * 64 + bofs[sub]);
   };
   // dY half-stages of step parity ri: part 0 in s_dy0 / s_dy2, part 1 in
   // s_dy1 / s_dy3
@@ -336,8 +344,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   load_dyh(1, 1, s_dy3, 0, 2);
   __builtin_amdgcn_sched_barrier(0);
 
-  u32x4 af[2][2], bf[2][8];
+  u32x4 af[2][4], bf[2][4];
   af[0][0] = read_a(0, 0, 0);
+  af[0][1] = read_a(0, 0, 1);
   read_b(s_dy0, 0, bf[0]);
   // The loop body has no branches: a branch splits the scheduling region,
   // and the MFMA / decode / load interleave is lost.
@@ -346,13 +355,17 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
 #pragma unroll
     for (int nn = 0; nn < 4; ++nn) {
       const int cur = nn & 1, nxt = cur ^ 1;
-      if (nn == 0) af[cur][1] = read_a(ri, 0, 1);
+      if (nn == 0) {
+        af[cur][2] = read_a(ri, 0, 2);
+        af[cur][3] = read_a(ri, 0, 3);
+      }
       if (nn < 3) {
-        af[nxt][0] = read_a(ri, nn + 1, 0);
-        af[nxt][1] = read_a(ri, nn + 1, 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[nxt][i] = read_a(ri, nn + 1, i);
         read_b(dyh_of(ri, (nn + 1) >> 1), (nn + 1) & 1, bf[nxt]);
       } else {
         af[nxt][0] = read_a(ri ^ 1, 0, 0);
+        af[nxt][1] = read_a(ri ^ 1, 0, 1);
         read_b(dyh_of(ri ^ 1, 0), 0, bf[nxt]);
       }
       // words 0-2, 3-5 and 6-7 of the next step's row in sub-steps 0, 1, 2
@@ -376,18 +389,22 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
         load_dyh(st + 2, 1, dyh_of(ri, 1), 0, 2);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[cur][i], bf[cur][j], acc[i][j]);
       // issue order: the operand reads of the next sub-step first (the LDS,
       // not the matrix cores, is the tighter resource here), then per MFMA
       // 5 VALU of the decode, and a refill load after every fourth, sixth or
       // eighth MFMA
       constexpr int kVmemEvery[4] = {8, 6, 6, 4};
+      // (LDS reads: 8 transposing A reads + 4 B reads; sub-step 0 also
+      // reads its own last two column tiles, sub-step 3 only two tiles)
       if (nn == 0)
-        __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
-      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      else if (nn < 3)
         __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -471,17 +488,17 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
       const int jt_n = (rr - jc < kJC ? rr - jc + 15 : kJC) / 16;
       for (int jt = 0; jt < jt_n; ++jt) {
         const int j0 = jt * 16 + h * 8;
-        u32x4 at[2];
+        u32x4 at[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          at[i] = *reinterpret_cast<const u32x4*>(s_at(wave * 64 + i * 32 + l32) + j0);
+        for (int i = 0; i < 4; ++i)
+          at[i] = *reinterpret_cast<const u32x4*>(s_at(128 * wk + i * 32 + l32) + j0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int ml = j * 32 + l32;
+        for (int j = 0; j < 4; ++j) {
+          const int ml = 128 * wm + j * 32 + l32;
           const u32x4 uh = *reinterpret_cast<const u32x4*>(s_dh + ml * rp + j0);
           const u32x4 ul = *reinterpret_cast<const u32x4*>(s_dl + ml * rp + j0);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
+          for (int i = 0; i < 4; ++i) {
             acc[i][j] = mfma32(at[i], uh, acc[i][j]);
             acc[i][j] = mfma32(at[i], ul, acc[i][j]);
           }
@@ -497,27 +514,28 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   // piece XOR the token's low 5 bits) and leaves as whole 16-byte pieces of
   // rows, 32 consecutive threads per row.
   __syncthreads();  // every wave is done with the LDS (adapter operands)
-  // token row -> its staging row (the row is known at compile time in both
-  // loops below, so the selects fold away)
+  // staging row of the first token of a 32-token group (a multiple of 32;
+  // wave-uniform in the first loop below, known at compile time in the
+  // second)
   auto s_out = [&](int row) -> uint8_t* {
     uint8_t* const b = row < 64 ? s_w0 : row < 128 ? s_w1 : row < 160 ? s_dy0 : row < 192 ? s_dy1 : row < 224 ? s_dy2 : s_dy3;
     return b + (row < 128 ? (row & 63) : (row & 31)) * 512;
   };
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int row0 = 128 * wm + 32 * j;  // tokens row0 .. row0 + 31, lane l32 holds row0 + l32
+    uint8_t* const so = s_out(row0) + l32 * 512;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = j * 32 + l32;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int p16 = wave * 8 + i * 4 + q;  // 16-byte piece of the row (columns 8 p16 ..)
+        const int p16 = 16 * wk + 4 * i + q;  // 16-byte piece of the row (columns 8 p16 ..)
         u32x2 o;
         o.x = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
         o.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        *reinterpret_cast<u32x2*>(s_out(j * 32) + (l32 & (j < 4 ? 63 : 31)) * 512 +
-                                  ((p16 ^ (row & 31)) << 4) + h * 8) = o;
+        *reinterpret_cast<u32x2*>(so + ((p16 ^ l32) << 4) + h * 8) = o;
       }
-    }
+  }
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
