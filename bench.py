@@ -85,12 +85,14 @@ def source_digest(kernel):
     return h.hexdigest()
 
 
-def recorded_traffic(kernel, workload):
+def recorded_traffic(kernel, workload, m=None):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE +
     WRITE_SIZE, scaled by a plain copy of known size), taken from the record
-    under profiles/; None when there is no record or the kernel's source has
+    under profiles/ (named for the token count too when it is not the
+    workload's own); None when there is no record or the kernel's source has
     changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    suffix = f"_M{m}" if m is not None else ""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}{suffix}.txt")
     try:
         with open(path) as f:
             text = f.read()
@@ -304,14 +306,14 @@ def main():
         achieved = work / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(dominant, args.workload),
+                "traffic": recorded_traffic(dominant, args.workload, wl.M if wl.M != WORKLOADS[args.workload].M else None),
                 "kernel": dominant, "bytes_per_launch": work}
         value, unit = weight_gbs, "GB/s"
     else:
         achieved = work / (k_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": recorded_traffic(dominant, args.workload),
+                "traffic": recorded_traffic(dominant, args.workload, wl.M if wl.M != WORKLOADS[args.workload].M else None),
                 "kernel": dominant, "flops_per_launch": work}
         value, unit = tflops, "TFLOP/s"
     roof["avg_launch_us"] = round(k_ms * 1e3, 3)
