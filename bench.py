@@ -332,10 +332,28 @@ def main():
         "frac_of_bf16_peak_step": round(tflops / BF16_PEAK_TFLOPS, 4),
         "packed_weight_bytes": wbytes, "flops_per_step": flops,
         "roofline": roof, "setup_s": round(setup_s, 2),
+        "footprint": footprint(wl, wbytes),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, hbm_bound, wbytes, flops)
     print(json.dumps(out), flush=True)
+
+
+def footprint(wl, wbytes):
+    """The pages' memory-footprint claims as context, from this format's own
+    bytes: bits per parameter of the packed weight (codes + block constants),
+    and what that makes the frozen weights of the models the pages name (the
+    QLoRA explainer fine-tunes a 65B model on one 48 GB GPU; the LQ-LoRA
+    abstract puts a 2.75-bit LLaMA-2-70B in 27 GB).  NormalFloat-3 with
+    double quantization (3.127 bits) is the format of this library nearest
+    to that 2.75-bit average, which the pages reach by mixing bit widths."""
+    bpp = 8 * wbytes / (wl.d_out * wl.d_in)
+    nf3 = 3 + 8 / 64 + 32 / (64 * 256)
+    return {"bits_per_param": round(bpp, 4),
+            "weights_65b_gb": round(65e9 * bpp / 8 / 1e9, 1),
+            "weights_70b_gb": round(70e9 * bpp / 8 / 1e9, 1),
+            "weights_70b_nf3_dq_gb": round(70e9 * nf3 / 8 / 1e9, 1),
+            "pages": "65B model fine-tuned on one 48 GB GPU (QLoRA); 2.75-bit LLaMA-2-70B in 27 GB (LQ-LoRA)"}
 
 
 def lq_flops(N, K, r, iters, power):
