@@ -171,6 +171,7 @@ def _check(oracle, got, ref, keys=("y", "u", "dX", "dA", "dB")):
     (512, 1024, 17, 8),       # just above the weight-streaming threshold
     (1040, 768, 513, 48),
     (512, 4096, 260, 16),     # few tiles, long K: split-K with ticketed fix-up
+    (256, 1280, 100, 16),     # split-K with an odd number of K steps per split (a masked pad step)
 ])
 def test_layer_nf4(qb, oracle, d_out, d_in, M, r):
     _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r)
@@ -183,6 +184,7 @@ def test_layer_nf4(qb, oracle, d_out, d_in, M, r):
     (256, 1024, 16, 16, 32),    # QA-LoRA pooled adapter, weight-streaming
     (528, 1088, 300, 64, 32),   # QA-LoRA pooled adapter, MFMA path (34 groups)
     (272, 2048, 260, 16, 32),   # pooled, MFMA path, group count a multiple of 8
+    (256, 1280, 100, 16, 32),   # pooled, split-K with an odd number of K steps per split
 ])
 def test_layer_int4(qb, oracle, d_out, d_in, M, r, pool):
     _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r, fmt="int4", pool=pool)
