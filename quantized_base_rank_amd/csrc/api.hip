@@ -756,7 +756,7 @@ LqLayout lq_layout(int64_t N, int64_t K, int32_t r) {
   l.off_ct = off;    off = align256(off + static_cast<size_t>(r) * K * f);
   l.off_t = off;     off = align256(off + static_cast<size_t>(r) * std::max(N, K) * f);
   l.off_g = off;     off = align256(off + static_cast<size_t>(r) * r * f);
-  l.off_uinv = off;  off = align256(off + static_cast<size_t>(r) * r * f);
+  l.off_uinv = off;  off = align256(off + static_cast<size_t>(r) * ((r + 3) & ~3) * f);
   l.off_p = off;     off = align256(off + lq_gemm_scratch_floats(N, K, r) * f);
   l.off_parts = off; off = align256(off + static_cast<size_t>(lq_resid_parts(N * K)) * sizeof(double));
   l.off_sums = off;  off = align256(off + 4 * sizeof(double));

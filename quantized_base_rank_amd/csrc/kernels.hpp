@@ -242,8 +242,8 @@ hipError_t launch_dadb_few(const DaDbFewArgs& a, hipStream_t stream);
 // Low-rank plus quantized decomposition (lq.hip): device scratch and steps
 struct LqScratch {
   float* G;       // r x r Gram matrix
-  float* Uinv;    // r x r Cholesky factor of the Gram matrix
-  float* T;       // r x max(N, K)
+  float* Uinv;    // r x roundup(r, 4): inverse of the Gram matrix's Cholesky factor
+  float* T;       // r x max(N, K): the first CholeskyQR pass's output
   float* P;       // split sums, lq_gemm_scratch_floats
   double* parts;  // lq_resid_parts(N K) per-workgroup sums
   double* sums;   // [0] |R|^2, [1] |C|^2, [2] |W|^2

@@ -9,9 +9,9 @@
 // iteration from a caller-drawn start, orthonormalised by CholeskyQR2 (the
 // thin QR with a positive diagonal, which is unique), then C = U^T R.
 //
-// Everything runs in fp32 on the device: one tiled GEMM kernel with strided
-// operands (split over the reduction with a fixed-order second pass) serves
-// every product; a one-workgroup kernel factors the r x r Gram matrix in
+// Everything runs in fp32 on the device: one GEMM kernel on the fp32 matrix
+// cores, with strided operands (split over the reduction with a fixed-order
+// second pass), serves every product; a one-workgroup kernel factors the r x r Gram matrix in
 // fp64, and the orthonormal factor follows by triangular solves (a column of
 // the tall matrix per thread).  U is kept transposed (r x N) and C as
 // r x K, so that both tall factors are r rows of contiguous data.
@@ -27,10 +27,20 @@ namespace {
 
 // ------------------------------------------------------------------ GEMM
 // C[m][n] = alpha sum_k A(m, k) B(n, k) + beta Cin[m][n], A(m, k) at
-// A[m * sam + k * sak], B(n, k) at B[n * sbn + k * sbk].  64 x 64 tiles,
-// 16 k per step, 256 threads of 4 x 4 outputs.  With splits > 1, split z
-// writes its sum over its share of k to P[z][m][n] and k_lq_reduce finishes.
-constexpr int kGt = 64, kGk = 16;
+// A[m * sam + k * sak], B(n, k) at B[n * sbn + k * sbk]; each operand has a
+// contiguous index (k, or m / n: stride 1), every other stride and the
+// contiguous extent are multiples of 4 floats, and the bases are 16-byte
+// aligned (the host checks).  On the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32: fp32 products and sums): 64 x 256 output tiles,
+// four waves of 64 x 64, 32 k per chunk.  A chunk of each operand is
+// staged in LDS in its memory order ([x][k] when k is contiguous, [k][x]
+// otherwise; rows padded against bank conflicts) from registers loaded one
+// chunk ahead.  MFMA s of a chunk sums k = s (lanes 0-31) and k = 16 + s
+// (lanes 32-63), so that a lane reads 16 consecutive k of a [x][k] row.
+// Rows, columns and k past the ranges are zero.  With splits > 1, split z
+// writes its sum over its share of k to P[z][m][n] and k_lq_reduce
+// finishes.
+constexpr int kMt = 64, kNt = 128, kKc = 32;
 
 struct GemmArgs {
   const float* A; int64_t sam, sak;
@@ -43,70 +53,177 @@ struct GemmArgs {
   float* P;                         // [splits][M][N] when splits > 1
 };
 
-__global__ __launch_bounds__(256) void k_lq_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) float As[kGk][kGt + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[kGk][kGt + 4];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kGt, n0 = static_cast<int64_t>(blockIdx.x) * kGt;
-  const int z = blockIdx.z;
-  const int64_t kper = (a.K + a.splits - 1) / a.splits;
-  const int64_t k0 = z * kper, k1 = k0 + kper < a.K ? k0 + kper : a.K;
-  float acc[4][4] = {};
-  // tile loads: 1024 elements of each operand, four per thread, along
-  // whichever index is contiguous in memory
-  auto load_tile = [&](const float* X, int64_t sx, int64_t sk, int64_t x0, int64_t xn, int64_t kb,
-                       float (&T)[kGk][kGt + 4]) {
-    float v[4];
-    if (sk == 1) {
-      const int xi = tid >> 2, kk = (tid & 3) * 4;
+// LDS row strides (floats): [x][k] rows of 32 k, [k][x] rows of TX x
+constexpr int kXkStride = kKc + 4;
+template <int TX>
+constexpr int kx_stride() { return TX + 2; }
+template <bool KC, int TX>
+constexpr int stage_floats() { return KC ? TX * kXkStride : kKc * kx_stride<TX>(); }
+constexpr int kOutStride = kNt + 8;  // output staging rows: the two lane halves hit disjoint banks
+
+// One operand's chunk: TX rows x (m or n) from x0, 32 k from kb, limited
+// to x < xn and k < k1.  Thread t holds pieces t + 256 i (4 floats each).
+template <bool KC, int TX>
+struct Chunk {
+  static constexpr int kPieces = TX * kKc / 4 / 256;
+  f32x4 v[kPieces];
+  __device__ __forceinline__ void load(const float* X, int64_t sx, int64_t sk, int64_t x0, int64_t xn, int64_t kb,
+                                       int64_t k1, int tid) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t x = x0 + xi, k = kb + kk + e;
-        v[e] = (x < xn && k < k1) ? X[x * sx + k] : 0.0f;
+    for (int i = 0; i < kPieces; ++i) {
+      const int p = tid + 256 * i;
+      if constexpr (KC) {  // row x = p / 8, k = 4 (p % 8) .. +3
+        const int64_t x = x0 + p / 8, k = kb + 4 * (p % 8);
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        if (x < xn && k < k1) t = *reinterpret_cast<const f32x4*>(X + x * sx + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = k + e < k1 ? t[e] : 0.0f;
+        v[i] = t;
+      } else {  // k row p / (TX / 4), x = 4 (p % (TX / 4)) .. +3
+        const int64_t k = kb + p / (TX / 4), x = x0 + 4 * (p % (TX / 4));
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        if (k < k1 && x < xn) t = *reinterpret_cast<const f32x4*>(X + k * sk + x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = x + e < xn ? t[e] : 0.0f;
+        v[i] = t;
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) T[kk + e][xi] = v[e];
-    } else {
-      const int kk = tid >> 4, xi = (tid & 15) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t x = x0 + xi + e, k = kb + kk;
-        v[e] = (x < xn && k < k1) ? X[x * sx + k * sk] : 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) T[kk][xi + e] = v[e];
     }
-  };
-  for (int64_t kb = k0; kb < k1; kb += kGk) {
-    load_tile(a.A, a.sam, a.sak, m0, a.M, kb, As);
-    load_tile(a.B, a.sbn, a.sbk, n0, a.N, kb, Bs);
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kGk; ++kk) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk][tx * 4]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
-    }
-    __syncthreads();
   }
+  __device__ __forceinline__ void store(float* T, int tid) const {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + ty * 4 + i;
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + tx * 4 + j;
-      if (n >= a.N) continue;
-      if (a.splits > 1) {
-        a.P[(z * a.M + m) * a.N + n] = acc[i][j];
-      } else {
-        float v = a.alpha * acc[i][j];
-        if (a.Cin != nullptr) v = __builtin_fmaf(a.beta, a.Cin[m * a.ldci + n], v);
-        a.C[m * a.ldc + n] = v;
+    for (int i = 0; i < kPieces; ++i) {
+      const int p = tid + 256 * i;
+      float* d = KC ? T + (p / 8) * kXkStride + 4 * (p % 8) : T + (p / (TX / 4)) * kx_stride<TX>() + 4 * (p % (TX / 4));
+      if constexpr (KC) {
+        *reinterpret_cast<f32x4*>(d) = v[i];
+      } else {  // rows of TX + 2 floats: 8-byte aligned pieces
+        *reinterpret_cast<f32x2*>(d) = f32x2{v[i][0], v[i][1]};
+        *reinterpret_cast<f32x2*>(d + 2) = f32x2{v[i][2], v[i][3]};
       }
+    }
+  }
+};
+
+// The 16 values of a lane for one 32-row fragment (rows xb .. xb + 31 of
+// the stage; lane half h covers k = 16 h .. 16 h + 15)
+template <bool KC, int TX>
+__device__ __forceinline__ void read_frag(const float* T, int xb, int l32, int h, float (&f)[16]) {
+  if constexpr (KC) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(T + (xb + l32) * kXkStride + 16 * h + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[4 * q + e] = t[e];
+    }
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) f[s2] = T[(16 * h + s2) * kx_stride<TX>() + xb + l32];
+  }
+}
+
+// Two workgroups per compute unit (two waves per SIMD): while one waits
+// for its loads or at its barrier, the other's products run.  Operands are
+// loaded into registers two chunks ahead (two register sets, the chunk loop
+// unrolled by two).
+template <bool AKC, bool BKC>
+__global__ __launch_bounds__(256, 2) void k_lq_mm(GemmArgs a) {
+  constexpr int kAS = stage_floats<AKC, kMt>();
+  // (the B stages also hold the output tile after the loop)
+  constexpr int kBS = stage_floats<BKC, kNt>() > kMt * kOutStride / 2 ? stage_floats<BKC, kNt>() : kMt * kOutStride / 2;
+  __shared__ __attribute__((aligned(16))) float s_a[2][kAS];
+  __shared__ __attribute__((aligned(16))) float s_b[2][kBS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kMt, n0 = static_cast<int64_t>(blockIdx.x) * kNt;
+  const int z = blockIdx.z;
+  // whole chunks per split, so that every k-contiguous load is 16-byte aligned
+  const int64_t kper = ((a.K + a.splits - 1) / a.splits + kKc - 1) / kKc * kKc;
+  const int64_t k0 = z * kper < a.K ? z * kper : a.K;
+  const int64_t k1 = k0 + kper < a.K ? k0 + kper : a.K;
+  const int64_t nch = (k1 - k0 + kKc - 1) / kKc;
+
+  f32x16 acc[2] = {f32x16{}, f32x16{}};  // rows 32 i .. +31, columns 32 wave .. +31
+  Chunk<AKC, kMt> ca[2];
+  Chunk<BKC, kNt> cb[2];
+  auto load = [&](int64_t c, int set) {
+    const int64_t kb = k0 + c * kKc;
+    ca[set].load(a.A, AKC ? a.sam : 1, AKC ? 1 : a.sak, m0, a.M, kb, k1, tid);
+    cb[set].load(a.B, BKC ? a.sbn : 1, BKC ? 1 : a.sbk, n0, a.N, kb, k1, tid);
+  };
+  // chunk c: LDS stage c & 1; before that, register set c & 1
+  if (nch > 0) load(0, 0);
+  if (nch > 1) load(1, 1);
+  if (nch > 0) {
+    ca[0].store(s_a[0], tid);
+    cb[0].store(s_b[0], tid);
+  }
+  __syncthreads();
+  auto chunk = [&](int64_t c, auto set_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_c)::value;  // c & 1
+    if (c + 2 < nch) load(c + 2, S);           // set S held chunk c, already in LDS
+    float fa[2][16], fb[16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) read_frag<AKC, kMt>(s_a[S], 32 * i, l32, h, fa[i]);
+    read_frag<BKC, kNt>(s_b[S], 32 * wave, l32, h, fb);
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s2], fb[s2], acc[i], 0, 0, 0);
+    if (c + 1 < nch) {
+      ca[S ^ 1].store(s_a[S ^ 1], tid);
+      cb[S ^ 1].store(s_b[S ^ 1], tid);
+    }
+    __syncthreads();
+  };
+  for (int64_t c = 0; c < nch; c += 2) {
+    chunk(c, std::integral_constant<int, 0>{});
+    if (c + 1 < nch) chunk(c + 1, std::integral_constant<int, 1>{});
+  }
+
+  // output: the tile goes through LDS ([64 m][kOutStride], in the B stages)
+  // and leaves as 16-byte pieces of rows (32 threads per 128-float row)
+  float* const s_o = &s_b[0][0];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      s_o[(32 * i + 8 * (v >> 2) + 4 * h + (v & 3)) * kOutStride + 32 * wave + l32] = acc[i][v];
+  __syncthreads();
+  const int c4 = 4 * (tid & 31);
+  const int64_t n = n0 + c4;
+  float* const out = a.splits > 1 ? a.P + static_cast<int64_t>(z) * a.M * a.N : a.C;
+  const int64_t ldo = a.splits > 1 ? a.N : a.ldc;
+  const bool vec = (ldo & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0 &&
+                   (a.splits > 1 || a.Cin == nullptr || ((a.ldci & 3) == 0 && (reinterpret_cast<uintptr_t>(a.Cin) & 15) == 0));
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = q * 8 + (tid >> 5);
+    const int64_t m = m0 + row;
+    if (m >= a.M || n >= a.N) continue;
+    f32x4 y = *reinterpret_cast<const f32x4*>(&s_o[row * kOutStride + c4]);
+    if (a.splits == 1) {
+      y *= a.alpha;
+      if (a.Cin != nullptr) {
+        const float* ci = a.Cin + m * a.ldci + n;
+        if (vec && n + 3 < a.N) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(ci);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf(a.beta, t[e], y[e]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < a.N) y[e] = __builtin_fmaf(a.beta, ci[e], y[e]);
+        }
+      }
+    }
+    float* o = out + m * ldo + n;
+    if (vec && n + 3 < a.N) {
+      *reinterpret_cast<f32x4*>(o) = y;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < a.N) o[e] = y[e];
     }
   }
 }
@@ -215,7 +332,17 @@ __global__ void k_lq_err(const double* rr, const double* cc, const double* ww, f
 // row, which keeps the result finite.
 constexpr int kLqMaxR = 128;
 
-__global__ __launch_bounds__(256) void k_lq_chol(const float* __restrict__ G, int r, float* __restrict__ U) {
+// Cholesky factor U (upper triangular, U^T U = G) of the r x r Gram matrix,
+// right-looking in fp64 in LDS (the trailing update spread over the
+// workgroup), and its inverse: thread c solves U x = e_c by back
+// substitution (x in the free lower triangle of row c, x_c in a register,
+// the sums in four parts).  The output is Uinv[j][i] = (U^{-1})[j][i] in
+// fp32, row stride ldu (zero below the diagonal and in the padding), the
+// left operand of X <- U^{-T} X.  A pivot that is not positive and finite
+// (a zero or rank-deficient Gram matrix) gives a zero row of U with a unit
+// diagonal, so the matching row of X passes through unchanged.
+__global__ __launch_bounds__(256) void k_lq_cholinv(const float* __restrict__ G, int r, float* __restrict__ Uinv,
+                                                    int ldu) {
   __shared__ double s_a[kLqMaxR * (kLqMaxR + 1)];  // r x r, row stride r + 1
   __shared__ double s_piv;
   const int tid = threadIdx.x;
@@ -239,32 +366,32 @@ __global__ __launch_bounds__(256) void k_lq_chol(const float* __restrict__ G, in
     }
     __syncthreads();
   }
-  for (int i = tid; i < r * r; i += 256) {
-    const int row = i / r, col = i % r;
-    U[i] = row <= col ? static_cast<float>(s_a[row * ld + col]) : 0.0f;
+  // column c of U^{-1}: x_c = 1 / u_cc, x_i = -(sum_{k = i+1..c} u_ik x_k) / u_ii
+  const int c = tid;
+  double xc = 0.0;
+  if (c < r) {
+    xc = 1.0 / s_a[c * ld + c];
+    for (int i = c - 1; i >= 0; --i) {
+      double p0 = s_a[i * ld + c] * xc, p1 = 0.0, p2 = 0.0, p3 = 0.0;
+      int k = i + 1;
+      for (; k + 3 < c; k += 4) {
+        p0 += s_a[i * ld + k] * s_a[c * ld + k];
+        p1 += s_a[i * ld + k + 1] * s_a[c * ld + k + 1];
+        p2 += s_a[i * ld + k + 2] * s_a[c * ld + k + 2];
+        p3 += s_a[i * ld + k + 3] * s_a[c * ld + k + 3];
+      }
+      for (; k < c; ++k) p0 += s_a[i * ld + k] * s_a[c * ld + k];
+      s_a[c * ld + i] = -((p0 + p1) + (p2 + p3)) / s_a[i * ld + i];
+    }
   }
-}
-
-// X (r x L) <- its thin-QR Q factor given U: column l of X is solved from
-// U^T q = x by forward substitution, one column per thread, in an LDS tile.
-constexpr int kTrCols = 64;
-
-__global__ __launch_bounds__(kTrCols) void k_lq_trsm(const float* __restrict__ U, int r, int64_t L,
-                                                      float* __restrict__ X) {
-  __shared__ float s_u[kLqMaxR * kLqMaxR];
-  __shared__ float s_x[kLqMaxR][kTrCols];
-  const int tid = threadIdx.x;
-  const int64_t l = static_cast<int64_t>(blockIdx.x) * kTrCols + tid;
-  for (int i = tid; i < r * r; i += kTrCols) s_u[i] = U[i];
-  for (int i = 0; i < r; ++i) s_x[i][tid] = l < L ? X[i * L + l] : 0.0f;
   __syncthreads();
-  for (int i = 0; i < r; ++i) {
-    float v = s_x[i][tid];
-    for (int k = 0; k < i; ++k) v = __builtin_fmaf(-s_u[k * r + i], s_x[k][tid], v);
-    s_x[i][tid] = v / s_u[i * r + i];
+  // Uinv[j][i] = x_i[j] for j <= i < r: x_i[j] is at a[i][j] (j < i) or x_i (j = i)
+  if (c < r) Uinv[c * ldu + c] = static_cast<float>(xc);
+  for (int e = tid; e < r * ldu; e += 256) {
+    const int j = e / ldu, i = e % ldu;
+    if (i == j && i < r) continue;
+    Uinv[e] = (i < r && j < i) ? static_cast<float>(s_a[i * ld + j]) : 0.0f;
   }
-  if (l < L)
-    for (int i = 0; i < r; ++i) X[i * L + l] = s_x[i][tid];
 }
 
 // bf16 outputs: B[n][j] = Ut[j][n]; A[j][k] = C[j][k].
@@ -286,7 +413,7 @@ __global__ __launch_bounds__(256) void k_lq_outputs(const float* __restrict__ Ut
 namespace {
 
 int64_t lq_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + kGt - 1) / kGt) * ((N + kGt - 1) / kGt);
+  const int64_t tiles = ((M + kMt - 1) / kMt) * ((N + kNt - 1) / kNt);
   if (tiles < 1) return 1;  // an empty product (rank 0) is never launched
   int64_t s = (512 + tiles - 1) / tiles;
   const int64_t cap = (K + 255) / 256;  // at least 256 of the reduction per split
@@ -297,9 +424,25 @@ int64_t lq_splits(int64_t M, int64_t N, int64_t K) {
 hipError_t gemm(GemmArgs a, float* scratch, hipStream_t st) {
   a.splits = static_cast<int32_t>(lq_splits(a.M, a.N, a.K));
   a.P = scratch;
-  const dim3 grid(static_cast<uint32_t>((a.N + kGt - 1) / kGt), static_cast<uint32_t>((a.M + kGt - 1) / kGt),
+  const bool akc = a.sak == 1, bkc = a.sbk == 1;
+  // each operand needs a contiguous index, 4-float strides, rows whose
+  // contiguous extent rounded up to 4 fits their stride (4-float pieces
+  // never leave a row's storage) and 16-byte bases
+  const int64_t ao = akc ? a.sam : a.sak, bo = bkc ? a.sbn : a.sbk;
+  if ((!akc && a.sam != 1) || (!bkc && a.sbn != 1) || (ao & 3) != 0 || (bo & 3) != 0 ||
+      ((akc ? a.K : a.M) + 3) / 4 * 4 > ao || ((bkc ? a.K : a.N) + 3) / 4 * 4 > bo ||
+      (reinterpret_cast<uintptr_t>(a.A) & 15) != 0 || (reinterpret_cast<uintptr_t>(a.B) & 15) != 0)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>((a.N + kNt - 1) / kNt), static_cast<uint32_t>((a.M + kMt - 1) / kMt),
                   static_cast<uint32_t>(a.splits));
-  hipLaunchKernelGGL(k_lq_gemm, grid, dim3(256), 0, st, a);
+  if (akc && bkc)
+    hipLaunchKernelGGL((k_lq_mm<true, true>), grid, dim3(256), 0, st, a);
+  else if (akc)
+    hipLaunchKernelGGL((k_lq_mm<true, false>), grid, dim3(256), 0, st, a);
+  else if (bkc)
+    hipLaunchKernelGGL((k_lq_mm<false, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_lq_mm<false, false>), grid, dim3(256), 0, st, a);
   if (a.splits > 1) {
     const int64_t n = a.M * a.N;
     hipLaunchKernelGGL(k_lq_reduce, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st, a);
@@ -321,20 +464,26 @@ size_t lq_gemm_scratch_floats(int64_t N, int64_t K, int r) {
 }
 
 // X (r x L, fp32) <- the Q factor of its transpose's thin QR (CholeskyQR2:
-// twice the Gram matrix, its Cholesky factor U, and X <- X U^{-1} as
-// triangular solves).
+// twice the Gram matrix, its Cholesky factor U and X <- U^{-T} X, the last
+// as a product with the inverted factor; the first pass writes the scratch
+// s.T, the second writes X back).
 hipError_t lq_orth(float* X, int64_t L, int r, LqScratch s, hipStream_t st) {
+  const int ldu = (r + 3) & ~3;
+  float* src = X;
+  float* dst = s.T;
   for (int pass = 0; pass < 2; ++pass) {
     GemmArgs g{};
-    g.A = X; g.sam = L; g.sak = 1; g.B = X; g.sbn = L; g.sbk = 1;
+    g.A = src; g.sam = L; g.sak = 1; g.B = src; g.sbn = L; g.sbk = 1;
     g.C = s.G; g.ldc = r; g.alpha = 1.0f; g.M = r; g.N = r; g.K = L;
     hipError_t e = gemm(g, s.P, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lq_chol, dim3(1), dim3(256), 0, st, s.G, r, s.Uinv);
+    hipLaunchKernelGGL(k_lq_cholinv, dim3(1), dim3(256), 0, st, s.G, r, s.Uinv, ldu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lq_trsm, dim3(static_cast<uint32_t>((L + kTrCols - 1) / kTrCols)), dim3(kTrCols), 0, st,
-                       s.Uinv, r, L, X);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    GemmArgs t{};
+    t.A = s.Uinv; t.sam = 1; t.sak = ldu; t.B = src; t.sbn = 1; t.sbk = L;
+    t.C = dst; t.ldc = L; t.alpha = 1.0f; t.M = r; t.N = L; t.K = r;
+    if ((e = gemm(t, s.P, st)) != hipSuccess) return e;
+    std::swap(src, dst);
   }
   return hipSuccess;
 }
