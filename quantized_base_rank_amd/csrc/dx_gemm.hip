@@ -5,19 +5,20 @@
 //
 // The reduction runs over the output features n, i.e. across rows of the
 // packed weight.  Tile: 256 columns of dX x 256 tokens per workgroup of 4
-// waves, one per SIMD; wave w owns columns [64 w, 64 w + 64) (one NF4 block,
-// two INT4 groups) for all 256 tokens.  In each 64-row step every lane
-// decodes one weight row of its wave's columns (one table per lane) and
-// writes it row-major into the wave's own LDS slab; the transposing LDS read
-// then turns 8 consecutive rows of one column into an MFMA operand.  A wave
-// only ever reads the weights it decoded itself, so only the shared dY tile
-// needs the workgroup barrier.  The next step's weights are decoded while
-// the current step's MFMAs run (a two-stage register pipeline over the four
-// 16-row sub-steps).  The dY tile of a step arrives by direct-to-LDS loads
-// two steps ahead, the packed codes (whole rows, shared by the four waves)
-// three steps ahead.  Each LDS stage is an array of its own, so that the
-// compiler can tell that reads of one stage do not depend on loads still
-// landing in another.
+// waves, one per SIMD.  In each 64-row step wave w decodes the weights of
+// columns [64 w, 64 w + 64) (one NF4 block, two INT4 groups): every lane
+// one weight row (one table per lane), written row-major into the wave's
+// LDS slab.  The products are arranged 2 x 2: wave 2 wk + wm computes
+// columns [128 wk, 128 wk + 128) for tokens [128 wm, 128 wm + 128) from its
+// own slab and its neighbour's, the transposing LDS read turning 8
+// consecutive rows of one column into an MFMA operand.  The next step's
+// weights are decoded while the current step's MFMAs run (a two-stage
+// register pipeline over the four 16-row sub-steps).  dY streams through a
+// ring of four half-step stages and the packed codes (whole rows, shared by
+// the four waves) through two stages, by direct-to-LDS loads spread over
+// the step; two barriers per step wait with counted vmcnt.  Each LDS stage
+// is an array of its own, so that the compiler can tell that reads of one
+// stage do not depend on loads still landing in another.
 // The adapter term du A is 2*ceil(r/16) extra MFMA k-steps (du split hi +
 // lo), read from A^T [K][r].
 #include "device_common.hpp"

@@ -6,8 +6,8 @@
 //
 // Tile: 256 tokens x 256 output features per workgroup of 4 waves; wave w
 // owns features [64w, 64w+64) for all 256 tokens, so every 4-bit weight is
-// decoded exactly once per workgroup, straight from HBM into registers
-// (byte-permute lookup, no LDS), and reused by 8 MFMAs.  The 256x128 bf16
+// decoded exactly once per workgroup, from its codes in LDS into registers
+// (byte-permute lookup), and reused by 8 MFMAs.  The 256x128 bf16
 // token tile of each K step is streamed into LDS with direct-to-LDS loads
 // in two halves, through a ring of four half-stages that keeps every load
 // about one and a half K steps ahead (XOR-swizzled 16-byte chunks:
