@@ -60,6 +60,7 @@ def test_rank_zero_is_the_quantizer(qb, oracle):
     (256, 1024, 8, 3, 2, 256),
     (528, 768, 16, 2, 1, 0),      # fp32 block constants; ragged 64-tiles
     (1040, 2112, 64, 2, 1, 256),  # the widest adapter the layer kernels are tuned for
+    (256, 512, 5, 2, 1, 256),     # a rank that is not a multiple of 4 (padded inverse, ragged tiles)
 ])
 def test_decomposition(qb, oracle, n, k, r, iters, power, dq):
     W = _weight(n, k, 8, 1 + r)
