@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--lq-power", type=int, default=1)
     p.add_argument("--kernel-iters", type=int, default=200,
                    help="few-token workloads: graph-replayed launches for the kernel timing")
+    p.add_argument("--reference-gemm", action="store_true",
+                   help="time hipBLASLt's bf16 GEMMs (torch.matmul on a materialised bf16 W, which the layer "
+                        "never makes) at the workload's forward and input-gradient shapes, as a reference "
+                        "point for the MFMA roofline; prints its own JSON line")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="before timing, copy a buffer of this many MiB once: a plain copy "
                         "kernel of known size that scales the HBM byte counters")
@@ -152,6 +156,8 @@ def main():
     inp = make_inputs(wl, seed=0)
     if args.lq:
         return lq_main(args, wl, inp, qb, torch, np, dev)
+    if args.reference_gemm:
+        return reference_gemm_main(args, wl, inp, torch, np, dev)
 
     def dev_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -363,6 +369,35 @@ def lq_flops(N, K, r, iters, power):
     4 r^2 L each) and, after the first, W - U C (2 N K r)."""
     per = (2 + 2 * power) * 2 * N * K * r + (1 + power) * 2 * 4 * r * r * N + power * 2 * 4 * r * r * K
     return iters * per + (iters - 1) * 2 * N * K * r
+
+
+def reference_gemm_main(args, wl, inp, torch, np, dev):
+    """The library's two large products as plain bf16 GEMMs through
+    torch.matmul (hipBLASLt) on a materialised bf16 copy of W: y = x W^T
+    (W used transposed, as the forward reads it) and dX = dY W.  Not part of
+    the layer (which never materialises W): a measured reference point for
+    what a dense bf16 GEMM of these shapes reaches on this GPU."""
+    M, N, K = wl.M, wl.d_out, wl.d_in
+    Wb = torch.from_numpy(np.ascontiguousarray(inp.W, dtype=np.float32)).to(dev).to(torch.bfloat16)
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).view(torch.bfloat16).to(dev)
+    dy = torch.from_numpy(np.ascontiguousarray(inp.dy).view(np.int16)).view(torch.bfloat16).to(dev)
+    res = {}
+    for name, f in (("x_Wt", lambda: torch.matmul(x, Wb.t())), ("dY_W", lambda: torch.matmul(dy, Wb))):
+        for _ in range(max(args.warmup, 1)):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        tf = 2 * M * N * K / (us * 1e-6) / 1e12
+        res[name] = {"us": round(us, 1), "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    print(json.dumps({"reference": "hipBLASLt bf16 GEMM via torch.matmul (materialised bf16 W)",
+                      "config": {"workload": wl.name, "M": M, "N": N, "K": K}, "steps": args.steps,
+                      "warmup": args.warmup, **res}), flush=True)
 
 
 def lq_main(args, wl, inp, qb, torch, np, dev):
