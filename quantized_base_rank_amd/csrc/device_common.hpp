@@ -116,11 +116,19 @@ __device__ __forceinline__ uint32_t lut_plane4(const uint32_t (&plane)[4], uint3
 // element b in its low nibble and element b + 4 in its high nibble, so the
 // low nibbles are elements 0..3 and the high nibbles elements 4..7, and one
 // byte interleave per output pair puts them in natural order.
+// The two byte constants of the selectors are held in vector registers:
+// a three-operand instruction on this target takes no literal and at most
+// one scalar operand, so with both constants in registers the mask-and-offset
+// of each selector is one v_and_or_b32 instead of an and plus an or.  (The
+// moves carry no side effects, so the compiler hoists them out of loops.)
 __device__ __forceinline__ u32x4 lut_decode8(const Lut16& t, uint32_t w) {
-  const uint32_t sl = w & 0x07070707u;                           // e0..e3, low 3 bits
-  const uint32_t sh = (w >> 4) & 0x07070707u;                    // e4..e7
-  const uint32_t pl = ((w >> 1) & 0x04040404u) | 0x03020100u;    // bit 3 -> +4
-  const uint32_t ph = ((w >> 5) & 0x04040404u) | 0x03020100u;
+  uint32_t m4, c3210;
+  asm("v_mov_b32 %0, 0x04040404" : "=v"(m4));
+  asm("v_mov_b32 %0, 0x03020100" : "=v"(c3210));
+  const uint32_t sl = w & 0x07070707u;         // e0..e3, low 3 bits
+  const uint32_t sh = (w >> 4) & 0x07070707u;  // e4..e7
+  const uint32_t pl = ((w >> 1) & m4) | c3210;  // bit 3 -> +4
+  const uint32_t ph = ((w >> 5) & m4) | c3210;
   const uint32_t ll = lut_plane4(t.lo, sl, pl), hl = lut_plane4(t.hi, sl, pl);
   const uint32_t lh = lut_plane4(t.lo, sh, ph), hh = lut_plane4(t.hi, sh, ph);
   u32x4 r;
