@@ -264,12 +264,15 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
     for (int c = 0; c < 4; ++c) acc[c] += *reinterpret_cast<const f32x4*>(&s_red[((blk * 64 + lane) * 4 + c) * 4]);
   }
 
+  // lane (l16, g) holds tokens 4 g .. 4 g + 3: lanes whose tokens all lie
+  // past M hold no output and move no partial sums
+  const bool live = 4 * g < M;
   if (S > 1) {
     const rsrc_t pr = make_rsrc(a.partial);
     auto slot_off = [&](int share, int c) {
       return static_cast<uint32_t>((((static_cast<int64_t>(share) * n_pan + pan) * 256 + tid) * 4 + c) * 16);
     };
-    if (half == 0) {
+    if (half == 0 && live) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) st_sys16(pr, slot_off(sh, c), acc[c]);
     }
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
     if (__builtin_amdgcn_readfirstlane(publish_and_ticket(a.counters + pan, s_ticket)) !=
         static_cast<uint32_t>(S - 1))
       return;
-    if (half == 0) {
+    if (half == 0 && live) {
       // shares in order, two at a time
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -292,15 +292,18 @@ __global__ __launch_bounds__(kFsThreads, 2 * QLIN_FS_WGS_PER_CU) void k_gemv_fwd
     }
   }
 
-  // lane (l16, g) holds y[m = l16][n = n0 + 16 wave + 4 g + v]
+  // lane (l16, g) holds y[m = l16][n = n0 + 16 wave + 4 g + v]; lanes of
+  // tokens past M hold no output and move no partial sums
   f32x4 sum = acc;
+  const bool live = l16 < M;
   if (S > 1) {
     const rsrc_t pr_ = make_rsrc(a.partial);
     const uint32_t mine = static_cast<uint32_t>(((static_cast<int64_t>(ks) * n_rg + rg) * kFsThreads + tid) * 16);
-    st_sys16(pr_, mine, acc);
+    if (live) st_sys16(pr_, mine, acc);
     if (__builtin_amdgcn_readfirstlane(publish_and_ticket(a.counters + rg, &s_ticket)) !=
         static_cast<uint32_t>(S - 1))
       return;
+    if (live) {
     f32x4 part[8];
 #pragma unroll
     for (int sp = 0; sp < 8; ++sp) {
@@ -320,6 +323,7 @@ __global__ __launch_bounds__(kFsThreads, 2 * QLIN_FS_WGS_PER_CU) void k_gemv_fwd
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         if (sp0 + q < S) sum += part[q];
+    }
     }
     if (tid == 0) a.counters[rg] = 0u;
   }
