@@ -152,6 +152,20 @@ __global__ __launch_bounds__(kAfThreads) void k_dadb_few(DaDbFewArgs a) {
   const int64_t nda_blocks = (nda + 3) / 4;                             // dB units start after them
   const bool da = static_cast<int64_t>(blockIdx.x) < nda_blocks;
   const float* src = da ? a.du : a.u;
+  // unit = (64-wide slice, column group); the block holds four units.  The
+  // thread's sixteen token values (x[m][k] for dA, dY[m][n] for dB) load
+  // before the staging barrier, so that they are in flight with the staging
+  // loads.
+  const int64_t unit = (static_cast<int64_t>(blockIdx.x) - (da ? 0 : nda_blocks)) * 4 + (tid >> 6);
+  const int sub = tid & 63;
+  const int jg = static_cast<int>(unit % ngrp);
+  const int64_t col = unit / ngrp * 64 + sub;  // k (dA) or n (dB)
+  const int64_t ncol = da ? a.K : a.N;
+  const bool ok = unit < (ncol + 63) / 64 * ngrp && col < ncol;
+  const uint16_t* tok = da ? a.x : a.dy;
+  float tv[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) tv[m] = (ok && m < M) ? bf16_to_f32(tok[m * ncol + col]) : 0.0f;
   {
     // all of a thread's loads in flight before its LDS stores
     constexpr int kPer = 16 * kAfMaxR / kAfThreads;
@@ -168,29 +182,20 @@ __global__ __launch_bounds__(kAfThreads) void k_dadb_few(DaDbFewArgs a) {
     }
   }
   __syncthreads();
-  // unit = (64-wide slice, column group); the block holds four units
-  const int64_t unit = (static_cast<int64_t>(blockIdx.x) - (da ? 0 : nda_blocks)) * 4 + (tid >> 6);
-  const int sub = tid & 63;
+  if (!ok) return;
   f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   if (da) {
     // dA[j][k] = sum_m du[m][j] x[m][k]
-    if (unit >= nda) return;
-    const int64_t K = a.K;
-    const int jg = static_cast<int>(unit % ngrp);
-    const int64_t k = unit / ngrp * 64 + sub;
-    if (k >= K) return;
-    float xv[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) xv[m] = m < M ? bf16_to_f32(a.x[m * K + k]) : 0.0f;
+    const int64_t K = a.K, k = col;
 #pragma unroll 2
     for (int m = 0; m < 16; ++m) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4 d = *reinterpret_cast<const f32x4*>(&s_t[m][16 * jg + 4 * q]);
-        acc[q][0] = __builtin_fmaf(d[0], xv[m], acc[q][0]);
-        acc[q][1] = __builtin_fmaf(d[1], xv[m], acc[q][1]);
-        acc[q][2] = __builtin_fmaf(d[2], xv[m], acc[q][2]);
-        acc[q][3] = __builtin_fmaf(d[3], xv[m], acc[q][3]);
+        acc[q][0] = __builtin_fmaf(d[0], tv[m], acc[q][0]);
+        acc[q][1] = __builtin_fmaf(d[1], tv[m], acc[q][1]);
+        acc[q][2] = __builtin_fmaf(d[2], tv[m], acc[q][2]);
+        acc[q][3] = __builtin_fmaf(d[3], tv[m], acc[q][3]);
       }
     }
 #pragma unroll
@@ -203,23 +208,16 @@ __global__ __launch_bounds__(kAfThreads) void k_dadb_few(DaDbFewArgs a) {
     return;
   }
   // dB[n][j] = s sum_m dY[m][n] u[m][j]
-  const int64_t N = a.N;
-  if (unit >= (N + 63) / 64 * ngrp) return;
-  const int jg = static_cast<int>(unit % ngrp);
-  const int64_t n = unit / ngrp * 64 + sub;
-  if (n >= N) return;
-  float dy[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) dy[m] = m < M ? bf16_to_f32(a.dy[m * N + n]) : 0.0f;
+  const int64_t n = col;
 #pragma unroll 2
   for (int m = 0; m < 16; ++m) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const f32x4 uu = *reinterpret_cast<const f32x4*>(&s_t[m][16 * jg + 4 * q]);
-      acc[q][0] = __builtin_fmaf(dy[m], uu[0], acc[q][0]);
-      acc[q][1] = __builtin_fmaf(dy[m], uu[1], acc[q][1]);
-      acc[q][2] = __builtin_fmaf(dy[m], uu[2], acc[q][2]);
-      acc[q][3] = __builtin_fmaf(dy[m], uu[3], acc[q][3]);
+      acc[q][0] = __builtin_fmaf(tv[m], uu[0], acc[q][0]);
+      acc[q][1] = __builtin_fmaf(tv[m], uu[1], acc[q][1]);
+      acc[q][2] = __builtin_fmaf(tv[m], uu[2], acc[q][2]);
+      acc[q][3] = __builtin_fmaf(tv[m], uu[3], acc[q][3]);
     }
   }
   uint16_t* dbrow = a.dB + n * r + 16 * jg;
