@@ -332,65 +332,175 @@ __global__ void k_lq_err(const double* rr, const double* cc, const double* ww, f
 // row, which keeps the result finite.
 constexpr int kLqMaxR = 128;
 
-// Cholesky factor U (upper triangular, U^T U = G) of the r x r Gram matrix,
-// right-looking in fp64 in LDS (the trailing update spread over the
-// workgroup), and its inverse: thread c solves U x = e_c by back
-// substitution (x in the free lower triangle of row c, x_c in a register,
-// the sums in four parts).  The output is Uinv[j][i] = (U^{-1})[j][i] in
-// fp32, row stride ldu (zero below the diagonal and in the padding), the
-// left operand of X <- U^{-T} X.  A pivot that is not positive and finite
-// (a zero or rank-deficient Gram matrix) gives a zero row of U with a unit
-// diagonal, so the matching row of X passes through unchanged.
+// Cholesky factor U (upper triangular, U^T U = G) of the r x r Gram matrix
+// and its inverse, in fp64.  Thread (ti, tc) of a 16 x 16 grid keeps the
+// elements (ti + 16 p, tc + 16 q) in registers, so each elimination step
+// reads only the published pivot row from LDS (double buffered, one barrier
+// per step): right-looking on unscaled rows, a[i][c] -= a[j][i] a[j][c] / d_j,
+// then row j of U is a[j][.] / sqrt(d_j).  The inverse X = U^{-1} solves
+// U X = I from the last row up, the same way: row i of X is the updated
+// row i of B (B = I at the start) over u_ii, published, and every row k < i
+// of B loses U[k][i] times it (U read from LDS).  The output is
+// Uinv[j][i] = (U^{-1})[j][i] in fp32, row stride ldu (zero below the
+// diagonal and in the padding), the left operand of X <- U^{-T} X.  A pivot
+// that is not positive and finite (a zero or rank-deficient Gram matrix)
+// gives a zero row of U with a unit diagonal, so the matching row of X
+// passes through unchanged.
+// S: register slots per thread along each dimension (r <= 16 S).
+// 1 / d for d > 0: the hardware reciprocal refined by two Newton steps
+// (within an ulp or two of the quotient; the divide sequence would sit on the
+// serial chain of every elimination step).
+__device__ __forceinline__ double recip64(double d) {
+  double y = __builtin_amdgcn_rcp(d);
+  double e = __builtin_fma(-d, y, 1.0);
+  y = __builtin_fma(y, e, y);
+  e = __builtin_fma(-d, y, 1.0);
+  return __builtin_fma(y, e, y);
+}
+
+template <int S>
 __global__ __launch_bounds__(256) void k_lq_cholinv(const float* __restrict__ G, int r, float* __restrict__ Uinv,
                                                     int ldu) {
-  __shared__ double s_a[kLqMaxR * (kLqMaxR + 1)];  // r x r, row stride r + 1
-  __shared__ double s_piv;
+  constexpr int kChS = S;
+  __shared__ double s_u[kLqMaxR * (kLqMaxR + 1)];  // U, row stride r + 1 (read-only during the inverse)
+  __shared__ double s_row[2][kLqMaxR];              // published pivot row / row of X
+  __shared__ double s_piv[kLqMaxR];                 // sqrt of each pivot (0: not positive)
+  __shared__ double s_rd[kLqMaxR];                  // 1 / u_ii
   const int tid = threadIdx.x;
+  const int ti = tid >> 4, tc = tid & 15;
   const int ld = r + 1;
-  for (int i = tid; i < r * r; i += 256) s_a[(i / r) * ld + i % r] = static_cast<double>(G[i]);
+  double a[kChS][kChS];
+#pragma unroll
+  for (int p = 0; p < kChS; ++p)
+#pragma unroll
+    for (int q = 0; q < kChS; ++q) {
+      const int i = ti + 16 * p, c = tc + 16 * q;
+      a[p][q] = (i < r && c < r && c >= i) ? static_cast<double>(G[i * r + c]) : 0.0;
+    }
+  // publish row 0 (its owners: ti == 0, slot p == 0)
+  if (ti == 0) {
+#pragma unroll
+    for (int q = 0; q < kChS; ++q)
+      if (tc + 16 * q < r) s_row[0][tc + 16 * q] = a[0][q];
+  }
   __syncthreads();
   for (int j = 0; j < r; ++j) {
-    if (tid == 0) {
-      const double d = s_a[j * ld + j];
-      s_piv = (d > 0.0 && std::isfinite(d)) ? std::sqrt(d) : 0.0;
-      s_a[j * ld + j] = s_piv > 0.0 ? s_piv : 1.0;
-    }
-    __syncthreads();
-    const double piv = s_piv;
-    for (int c = j + 1 + tid; c < r; c += 256) s_a[j * ld + c] = piv > 0.0 ? s_a[j * ld + c] / piv : 0.0;
-    __syncthreads();
-    // trailing update of the upper triangle: a[i][c] -= u[j][i] u[j][c]
-    for (int i = j + 1 + (tid >> 5); i < r; i += 8) {
-      const double uji = s_a[j * ld + i];
-      for (int c = i + (tid & 31); c < r; c += 32) s_a[i * ld + c] -= uji * s_a[j * ld + c];
-    }
-    __syncthreads();
-  }
-  // column c of U^{-1}: x_c = 1 / u_cc, x_i = -(sum_{k = i+1..c} u_ik x_k) / u_ii
-  const int c = tid;
-  double xc = 0.0;
-  if (c < r) {
-    xc = 1.0 / s_a[c * ld + c];
-    for (int i = c - 1; i >= 0; --i) {
-      double p0 = s_a[i * ld + c] * xc, p1 = 0.0, p2 = 0.0, p3 = 0.0;
-      int k = i + 1;
-      for (; k + 3 < c; k += 4) {
-        p0 += s_a[i * ld + k] * s_a[c * ld + k];
-        p1 += s_a[i * ld + k + 1] * s_a[c * ld + k + 1];
-        p2 += s_a[i * ld + k + 2] * s_a[c * ld + k + 2];
-        p3 += s_a[i * ld + k + 3] * s_a[c * ld + k + 3];
+    const double* prow = s_row[j & 1];
+    const double d = prow[j];
+    const double inv = (d > 0.0 && std::isfinite(d)) ? recip64(d) : 0.0;
+    // all of the step's LDS reads first, then a branch-free update (a
+    // branch around each slot would wait for its own read in turn)
+    double rowc[kChS], rowi[kChS];
+#pragma unroll
+    for (int q = 0; q < kChS; ++q) rowc[q] = prow[tc + 16 * q];
+#pragma unroll
+    for (int p = 0; p < kChS; ++p) rowi[p] = prow[ti + 16 * p];
+#pragma unroll
+    for (int p = 0; p < kChS; ++p) {
+      const int i = ti + 16 * p;
+      const double t = rowi[p] * inv;
+#pragma unroll
+      for (int q = 0; q < kChS; ++q) {
+        const int c = tc + 16 * q;
+        const double v = __builtin_fma(-t, rowc[q], a[p][q]);
+        a[p][q] = (i > j && c >= i && c < r) ? v : a[p][q];
       }
-      for (; k < c; ++k) p0 += s_a[i * ld + k] * s_a[c * ld + k];
-      s_a[c * ld + i] = -((p0 + p1) + (p2 + p3)) / s_a[i * ld + i];
     }
+    // publish row j + 1, now final (rows are updated only by earlier pivots)
+    const int jn = j + 1;
+    if (jn < r && ti == (jn & 15)) {
+#pragma unroll
+      for (int p = 0; p < kChS; ++p)
+        if (p == (jn >> 4)) {
+#pragma unroll
+          for (int q = 0; q < kChS; ++q) {
+            const int c = tc + 16 * q;
+            if (c >= jn && c < r) s_row[jn & 1][c] = a[p][q];
+          }
+        }
+    }
+    __syncthreads();
   }
+  // pivots, then U = rows over sqrt(pivot) into LDS (zero below the diagonal)
+#pragma unroll
+  for (int p = 0; p < kChS; ++p)
+#pragma unroll
+    for (int q = 0; q < kChS; ++q) {
+      const int i = ti + 16 * p, c = tc + 16 * q;
+      if (i == c && i < r) {
+        const double d = a[p][q];
+        const double pv = (d > 0.0 && std::isfinite(d)) ? std::sqrt(d) : 0.0;
+        s_piv[i] = pv;
+        s_rd[i] = pv > 0.0 ? 1.0 / pv : 1.0;
+      }
+    }
   __syncthreads();
-  // Uinv[j][i] = x_i[j] for j <= i < r: x_i[j] is at a[i][j] (j < i) or x_i (j = i)
-  if (c < r) Uinv[c * ldu + c] = static_cast<float>(xc);
-  for (int e = tid; e < r * ldu; e += 256) {
-    const int j = e / ldu, i = e % ldu;
-    if (i == j && i < r) continue;
-    Uinv[e] = (i < r && j < i) ? static_cast<float>(s_a[i * ld + j]) : 0.0f;
+#pragma unroll
+  for (int p = 0; p < kChS; ++p)
+#pragma unroll
+    for (int q = 0; q < kChS; ++q) {
+      const int i = ti + 16 * p, c = tc + 16 * q;
+      if (i < r && c < r) {
+        const double pv = s_piv[i];
+        s_u[i * ld + c] = c < i ? 0.0 : c == i ? (pv > 0.0 ? pv : 1.0) : (pv > 0.0 ? a[p][q] / pv : 0.0);
+      }
+    }
+  __syncthreads();
+  // inverse: B = I in the registers, rows solved from the last one up
+#pragma unroll
+  for (int p = 0; p < kChS; ++p)
+#pragma unroll
+    for (int q = 0; q < kChS; ++q) a[p][q] = (ti + 16 * p == tc + 16 * q) ? 1.0 : 0.0;
+  auto solve_row = [&](int i) {  // row i of X from row i of B, by its owners; published
+    if (ti == (i & 15)) {
+      const double rd = s_rd[i];
+#pragma unroll
+      for (int p = 0; p < kChS; ++p)
+        if (p == (i >> 4)) {
+#pragma unroll
+          for (int q = 0; q < kChS; ++q) {
+            const int c = tc + 16 * q;
+            if (c < r) {
+              a[p][q] = c >= i ? a[p][q] * rd : 0.0;
+              s_row[i & 1][c] = a[p][q];
+            }
+          }
+        }
+    }
+  };
+  solve_row(r - 1);
+  __syncthreads();
+  for (int i = r - 1; i > 0; --i) {
+    const double* xrow = s_row[i & 1];
+    double xc[kChS], uki[kChS];
+#pragma unroll
+    for (int q = 0; q < kChS; ++q) xc[q] = xrow[tc + 16 * q];
+#pragma unroll
+    for (int p = 0; p < kChS; ++p) uki[p] = s_u[(ti + 16 * p) * ld + i];
+#pragma unroll
+    for (int p = 0; p < kChS; ++p) {
+      const int k = ti + 16 * p;
+#pragma unroll
+      for (int q = 0; q < kChS; ++q) {
+        const int c = tc + 16 * q;
+        const double v = __builtin_fma(-uki[p], xc[q], a[p][q]);
+        a[p][q] = (k < i && c >= i && c < r) ? v : a[p][q];
+      }
+    }
+    solve_row(i - 1);
+    __syncthreads();
+  }
+  // Uinv[i][c] = X[i][c] for c >= i (zero below the diagonal); padding zero
+#pragma unroll
+  for (int p = 0; p < kChS; ++p)
+#pragma unroll
+    for (int q = 0; q < kChS; ++q) {
+      const int i = ti + 16 * p, c = tc + 16 * q;
+      if (i < r && c < r) Uinv[i * ldu + c] = c >= i ? static_cast<float>(a[p][q]) : 0.0f;
+    }
+  for (int e = tid; e < r * (ldu - r); e += 256) {
+    const int i = e / (ldu - r), c = r + e % (ldu - r);
+    Uinv[i * ldu + c] = 0.0f;
   }
 }
 
@@ -477,7 +587,10 @@ hipError_t lq_orth(float* X, int64_t L, int r, LqScratch s, hipStream_t st) {
     g.C = s.G; g.ldc = r; g.alpha = 1.0f; g.M = r; g.N = r; g.K = L;
     hipError_t e = gemm(g, s.P, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lq_cholinv, dim3(1), dim3(256), 0, st, s.G, r, s.Uinv, ldu);
+    if (r <= 64)
+      hipLaunchKernelGGL(k_lq_cholinv<4>, dim3(1), dim3(256), 0, st, s.G, r, s.Uinv, ldu);
+    else
+      hipLaunchKernelGGL(k_lq_cholinv<8>, dim3(1), dim3(256), 0, st, s.G, r, s.Uinv, ldu);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GemmArgs t{};
     t.A = s.Uinv; t.sam = 1; t.sak = ldu; t.B = src; t.sbn = 1; t.sbk = L;
