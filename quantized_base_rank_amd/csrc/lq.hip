@@ -327,7 +327,7 @@ __global__ void k_lq_err(const double* rr, const double* cc, const double* ww, f
 
 // ------------------------------------------------------ small factorisation
 // G (r x r, fp32, symmetric) = U^T U with U upper triangular and a positive
-// diagonal: right-looking fp64 Cholesky in LDS, U written out as fp32.  A
+// diagonal: right-looking fp64 Cholesky, then U^{-1} written out as fp32.  A
 // pivot that is not positive (a rank-deficient start) becomes 1 with a zero
 // row, which keeps the result finite.
 constexpr int kLqMaxR = 128;
