@@ -123,8 +123,9 @@ def kernel_work(wl, kernel):
         return (wbytes + 2 * M * N + 4 * M * K + 4 * r * Ka + 4 * N * r + 4 * M * r), "byte"
     if kernel == "k_gemv_fwd_stream":  # W, x, B, u, y
         return wbytes + 2 * M * K + 2 * N * r + 4 * M * r + 2 * M * N, "byte"
-    if kernel == "k_gemv_dx_stream":  # W, dY, A, du, dX
-        return wbytes + 2 * M * N + 2 * r * Ka + 4 * M * r + 2 * M * K, "byte"
+    if kernel == "k_gemv_dx_stream":  # W, dY, A, du, dX; unpooled also x and dA
+        extra = 2 * M * K + 2 * r * K if wl.pool == 1 else 0
+        return wbytes + 2 * M * N + 2 * r * Ka + 4 * M * r + 2 * M * K + extra, "byte"
     raise KeyError(kernel)
 
 

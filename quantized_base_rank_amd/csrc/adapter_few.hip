@@ -2,15 +2,17 @@
 // ["Background: how LoRA works": y = x W^T + s (x A^T) B^T, so with
 // u = x A^T the gradients are du = s dY B, dB = s dY^T u, dA = du^T x]
 //
-// k_du_few:  du = s dY B.  The reduction runs over the N rows of dY^T and B,
-//   split into up to 32 shares of 256-row chunks; a workgroup stages a chunk
-//   of B in LDS and forms its share with MFMAs on the bf16 inputs (exact
-//   products, fp32 sums).  Shares publish fp32 partial sums (write-through
-//   stores) and the last workgroup (atomic ticket) adds them in share order,
-//   every thread one element with sixteen shares' loads in flight.
-// k_dadb_few:  dB = s dY^T u and, unpooled, dA = du^T x in fp32 FMAs, as two
-//   ranges of one grid: a thread forms sixteen adapter columns of one row of
-//   dB or of one column of dA.
+// k_du_few:  du = s dY B and dB = s dY^T u, as two ranges of one grid.
+//   du: the reduction runs over the N rows of dY^T and B, split into up to
+//   32 shares of 256-row chunks; a workgroup stages a chunk of B in LDS and
+//   forms its share with MFMAs on the bf16 inputs (exact products, fp32
+//   sums).  Shares publish fp32 partial sums (write-through stores) and the
+//   last share's workgroup (atomic ticket) adds them in share order, every
+//   thread one element with sixteen shares' loads in flight.
+//   dB: a thread forms sixteen adapter columns of one row of dB in fp32
+//   FMAs over the tokens in order.
+// (dA = du^T x needs the finished du: the streamed input-gradient kernel
+// forms it per column panel after its own reduction.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -29,6 +31,72 @@ int du_shares(int64_t N) {
   return static_cast<int>(chunks < kAfMaxShares ? chunks : kAfMaxShares);
 }
 
+// dB rows for blocks past the du shares: thread (t % 64 -> row n, t / 64 ->
+// 16-column group of the adapter) forms sixteen independent fp32 sums over
+// the tokens, in token order.  The thread's sixteen dY values load before
+// the staging barrier, so that they are in flight with the staging loads.
+__device__ __forceinline__ void db_block(const AdapterFewArgs& a, int block, float (*s_t)[kAfMaxR]) {
+  const int tid = threadIdx.x;
+  const int64_t M = a.M, N = a.N;
+  const int r = a.r;
+  const int ngrp = (r + 15) / 16;
+  const int64_t unit = static_cast<int64_t>(block) * 4 + (tid >> 6);
+  const int sub = tid & 63;
+  const int jg = static_cast<int>(unit % ngrp);
+  const int64_t n = unit / ngrp * 64 + sub;
+  const bool ok = unit < (N + 63) / 64 * ngrp && n < N;
+  float tv[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) tv[m] = (ok && m < M) ? bf16_to_f32(a.dy[m * N + n]) : 0.0f;
+  {
+    constexpr int kPer = 16 * kAfMaxR / kAfThreads;
+    float v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = tid + e * kAfThreads, m = i / kAfMaxR, j = i % kAfMaxR;
+      v[e] = (m < M && j < r) ? a.u[m * r + j] : 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = tid + e * kAfThreads;
+      s_t[i / kAfMaxR][i % kAfMaxR] = v[e];
+    }
+  }
+  __syncthreads();
+  if (!ok) return;
+  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 2
+  for (int m = 0; m < 16; ++m) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 uu = *reinterpret_cast<const f32x4*>(&s_t[m][16 * jg + 4 * q]);
+      acc[q][0] = __builtin_fmaf(tv[m], uu[0], acc[q][0]);
+      acc[q][1] = __builtin_fmaf(tv[m], uu[1], acc[q][1]);
+      acc[q][2] = __builtin_fmaf(tv[m], uu[2], acc[q][2]);
+      acc[q][3] = __builtin_fmaf(tv[m], uu[3], acc[q][3]);
+    }
+  }
+  uint16_t* dbrow = a.dB + n * r + 16 * jg;
+  if (r % 16 == 0) {
+    // sixteen columns = 32 bytes of the row, 16-byte aligned
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 8 * h + 2 * e;
+        w[e] = static_cast<uint32_t>(f32_to_bf16(a.s * acc[c / 4][c % 4])) |
+               (static_cast<uint32_t>(f32_to_bf16(a.s * acc[(c + 1) / 4][(c + 1) % 4])) << 16);
+      }
+      *reinterpret_cast<u32x4*>(dbrow + 8 * h) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      if (16 * jg + c < r) dbrow[c] = f32_to_bf16(a.s * acc[c / 4][c % 4]);
+  }
+}
+
 __global__ __launch_bounds__(kAfThreads) void k_du_few(AdapterFewArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_b[kAfChunk * kAfBStride];  // B rows (bf16)
   __shared__ uint32_t s_ticket;
@@ -38,7 +106,11 @@ __global__ __launch_bounds__(kAfThreads) void k_du_few(AdapterFewArgs a) {
   const int r = a.r;
   const int rp = (r + 15) & ~15;  // adapter columns in whole 16-column tiles
   const int ntile = rp / 16;
-  const int S = static_cast<int>(gridDim.x);
+  const int S = a.shares;
+  if (static_cast<int>(blockIdx.x) >= S) {
+    db_block(a, static_cast<int>(blockIdx.x) - S, reinterpret_cast<float (*)[kAfMaxR]>(s_b));
+    return;
+  }
   const int64_t nchunk = (N + kAfChunk - 1) / kAfChunk;
   const int64_t per = (nchunk + S - 1) / S;
   const int64_t c0 = blockIdx.x * per, c1 = c0 + per < nchunk ? c0 + per : nchunk;
@@ -140,107 +212,6 @@ __global__ __launch_bounds__(kAfThreads) void k_du_few(AdapterFewArgs a) {
   }
 }
 
-// Thread (t % 64 -> row or column, t / 64 -> 16-column group of the
-// adapter): sixteen independent fp32 sums over the tokens, in token order.
-__global__ __launch_bounds__(kAfThreads) void k_dadb_few(DaDbFewArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_t[16][kAfMaxR];  // u or du: token, adapter column
-  const int tid = threadIdx.x;
-  const int64_t M = a.M;
-  const int r = a.r;
-  const int ngrp = (r + 15) / 16;
-  const int64_t nda = a.dA != nullptr ? (a.K + 63) / 64 * ngrp : 0;  // dA units (64 threads each)
-  const int64_t nda_blocks = (nda + 3) / 4;                             // dB units start after them
-  const bool da = static_cast<int64_t>(blockIdx.x) < nda_blocks;
-  const float* src = da ? a.du : a.u;
-  // unit = (64-wide slice, column group); the block holds four units.  The
-  // thread's sixteen token values (x[m][k] for dA, dY[m][n] for dB) load
-  // before the staging barrier, so that they are in flight with the staging
-  // loads.
-  const int64_t unit = (static_cast<int64_t>(blockIdx.x) - (da ? 0 : nda_blocks)) * 4 + (tid >> 6);
-  const int sub = tid & 63;
-  const int jg = static_cast<int>(unit % ngrp);
-  const int64_t col = unit / ngrp * 64 + sub;  // k (dA) or n (dB)
-  const int64_t ncol = da ? a.K : a.N;
-  const bool ok = unit < (ncol + 63) / 64 * ngrp && col < ncol;
-  const uint16_t* tok = da ? a.x : a.dy;
-  float tv[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) tv[m] = (ok && m < M) ? bf16_to_f32(tok[m * ncol + col]) : 0.0f;
-  {
-    // all of a thread's loads in flight before its LDS stores
-    constexpr int kPer = 16 * kAfMaxR / kAfThreads;
-    float v[kPer];
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int i = tid + e * kAfThreads, m = i / kAfMaxR, j = i % kAfMaxR;
-      v[e] = (m < M && j < r) ? src[m * r + j] : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int i = tid + e * kAfThreads;
-      s_t[i / kAfMaxR][i % kAfMaxR] = v[e];
-    }
-  }
-  __syncthreads();
-  if (!ok) return;
-  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  if (da) {
-    // dA[j][k] = sum_m du[m][j] x[m][k]
-    const int64_t K = a.K, k = col;
-#pragma unroll 2
-    for (int m = 0; m < 16; ++m) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 d = *reinterpret_cast<const f32x4*>(&s_t[m][16 * jg + 4 * q]);
-        acc[q][0] = __builtin_fmaf(d[0], tv[m], acc[q][0]);
-        acc[q][1] = __builtin_fmaf(d[1], tv[m], acc[q][1]);
-        acc[q][2] = __builtin_fmaf(d[2], tv[m], acc[q][2]);
-        acc[q][3] = __builtin_fmaf(d[3], tv[m], acc[q][3]);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 16 * jg + 4 * q + e;
-        if (j < r) a.dA[j * K + k] = f32_to_bf16(acc[q][e]);
-      }
-    return;
-  }
-  // dB[n][j] = s sum_m dY[m][n] u[m][j]
-  const int64_t n = col;
-#pragma unroll 2
-  for (int m = 0; m < 16; ++m) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 uu = *reinterpret_cast<const f32x4*>(&s_t[m][16 * jg + 4 * q]);
-      acc[q][0] = __builtin_fmaf(tv[m], uu[0], acc[q][0]);
-      acc[q][1] = __builtin_fmaf(tv[m], uu[1], acc[q][1]);
-      acc[q][2] = __builtin_fmaf(tv[m], uu[2], acc[q][2]);
-      acc[q][3] = __builtin_fmaf(tv[m], uu[3], acc[q][3]);
-    }
-  }
-  uint16_t* dbrow = a.dB + n * r + 16 * jg;
-  if (r % 16 == 0) {
-    // sixteen columns = 32 bytes of the row, 16-byte aligned
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = 8 * h + 2 * e;
-        w[e] = static_cast<uint32_t>(f32_to_bf16(a.s * acc[c / 4][c % 4])) |
-               (static_cast<uint32_t>(f32_to_bf16(a.s * acc[(c + 1) / 4][(c + 1) % 4])) << 16);
-      }
-      *reinterpret_cast<u32x4*>(dbrow + 8 * h) = u32x4{w[0], w[1], w[2], w[3]};
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 16; ++c)
-      if (16 * jg + c < r) dbrow[c] = f32_to_bf16(a.s * acc[c / 4][c % 4]);
-  }
-}
-
 }  // namespace
 
 int adapter_few_shares(int64_t N) { return du_shares(N); }
@@ -249,18 +220,12 @@ int64_t adapter_few_partial_floats(int64_t N) {
   return S > 1 ? static_cast<int64_t>(S) * 8 * 64 * 4 : 0;
 }
 
-hipError_t launch_du_few(const AdapterFewArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_du_few, dim3(static_cast<uint32_t>(du_shares(a.N))), dim3(kAfThreads), 0, stream, a);
-  return hipGetLastError();
-}
+static int db_few_blocks(int64_t N, int r) { return static_cast<int>(((N + 63) / 64 * ((r + 15) / 16) + 3) / 4); }
 
-hipError_t launch_dadb_few(const DaDbFewArgs& a, hipStream_t stream) {
-  const int64_t ngrp = (a.r + 15) / 16;
-  const int64_t nda = a.dA != nullptr ? (a.K + 63) / 64 * ngrp : 0;  // units of 64 threads
-  const int64_t ndb = (a.N + 63) / 64 * ngrp;
-  // dA units fill whole blocks first, so no block mixes the two
-  const int64_t blocks = (nda + 3) / 4 + (ndb + 3) / 4;
-  hipLaunchKernelGGL(k_dadb_few, dim3(static_cast<uint32_t>(blocks)), dim3(kAfThreads), 0, stream, a);
+hipError_t launch_du_few(const AdapterFewArgs& a, hipStream_t stream) {
+  // a.shares workgroups of du, then the dB rows
+  hipLaunchKernelGGL(k_du_few, dim3(static_cast<uint32_t>(a.shares + db_few_blocks(a.N, a.r))), dim3(kAfThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -218,7 +218,9 @@ Plan make_plan(const qlin_qweight* w, int64_t M, int32_t r, int32_t pool) {
   p.off_Bt = off;       off = align256(off + static_cast<size_t>(N) * r * sizeof(uint16_t));
   p.off_At = off;       off = align256(off + static_cast<size_t>(G) * r * sizeof(uint16_t));
   p.off_P = off;        off = align256(off + (pool > 1 ? static_cast<size_t>(M) * G * sizeof(float) : 0));
-  p.off_z = off;        off = align256(off + (p.small ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
+  // (hi/lo planes of u and du for the transposed products; the few-token
+  // streamed path uses them only for dA when dX is not wanted)
+  p.off_z = off;        off = align256(off + (p.small && !p.dx_stream ? 0 : 4 * static_cast<size_t>(M) * tn2_jp(r) * sizeof(uint16_t)));
   p.off_partial = off;  off = align256(off + static_cast<size_t>(partial) * sizeof(float));
   p.off_tc = off;       off += transcode_bytes(w);
   p.total = off;
@@ -653,16 +655,13 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
   const int64_t jp = tn2_jp(r);
   uint16_t* zp = ws_at<uint16_t>(workspace, p.off_z);
   if (p.dx_stream) {
-    // few tokens: du = s dY B, then dB = s dY^T u and (unpooled) dA = du^T x
-    // in one launch
+    // few tokens: du = s dY B and dB = s dY^T u in one launch (dA, which
+    // needs the finished du, is formed by the streamed input gradient)
     AdapterFewArgs f{};
-    f.dy = dy; f.M = M; f.N = N; f.B = B; f.r = r; f.s = s;
-    f.du = du; f.partial = partial; f.counters = counters;
+    f.dy = dy; f.M = M; f.N = N; f.B = B; f.u = u; f.r = r; f.s = s;
+    f.du = du; f.dB = dB; f.shares = adapter_few_shares(N);
+    f.partial = partial; f.counters = counters;
     QLIN_TRY(hooked("k_du_few", stream, [&] { return launch_du_few(f, stream); }));
-    DaDbFewArgs d{};
-    d.x = x; d.dy = dy; d.M = M; d.N = N; d.K = K; d.u = u; d.du = du; d.r = r; d.s = s;
-    d.dA = pool == 1 ? dA : nullptr; d.dB = dB;
-    QLIN_TRY(hooked("k_dadb_few", stream, [&] { return launch_dadb_few(d, stream); }));
   } else {
     // du = s dY B  (B^T staged so both operands are contiguous along n)
     QLIN_TRY(hooked("k_transpose16", stream, [&] { return launch_transpose16(B, N, r, Bt, stream); }));
@@ -682,8 +681,8 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     QLIN_TRY(hooked("k_tn2", stream, [&] { return launch_tn2(a, stream); }));
   }
   // dA = du^T P
-  if (pool == 1 && p.dx_stream) {
-    // formed above
+  if (pool == 1 && p.dx_stream && dx != nullptr) {
+    // formed per column panel by the streamed input gradient below
   } else if (pool == 1) {
     QLIN_TRY(hooked("k_split_hl", stream, [&] { return launch_split_hl(du, M, r, r, zp + 2 * M * jp, zp + 3 * M * jp, stream); }));
     Tn2Args a{};
@@ -709,6 +708,8 @@ int qlin_bwd(const qlin_qweight* w, const uint16_t* x, int64_t M, const uint16_t
     a.pool_shift = __builtin_ctz(static_cast<unsigned>(pool));
     a.adapter = (r > 0 && s != 0.0f) ? 1 : 0;
     a.dx = dx;
+    a.x = x;
+    a.dA = (r > 0 && pool == 1) ? dA : nullptr;
     a.splits = p.ds_splits;
     a.partial = partial;
     a.counters = counters;

@@ -18,7 +18,8 @@
 //   add their sums in fixed order; row shares publish fp32 partial sums
 //   (write-through stores) and the last workgroup of a panel (atomic ticket)
 //   adds them in fixed share order, adds du A with MFMAs (du split into bf16
-//   hi + lo halves) and stores dX.
+//   hi + lo halves) and stores dX; with an unpooled adapter it then forms
+//   dA = du^T x for the panel's columns.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -362,6 +363,44 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
         if (m < M && k < K) a.dx[m * K + k] = f32_to_bf16(acc[c][v]);
+      }
+    }
+  }
+
+  // dA over the panel's columns (unpooled adapter; du is final before this
+  // launch): dA[j][k] = sum_m du[m][j] x[m][k], fp32 fma over the tokens in
+  // order.  du is staged in LDS; a thread takes one column k and every other
+  // run of 32 adapter columns.
+  if (a.dA != nullptr) {
+    __syncthreads();  // the staged adapter panel is no longer read
+    float* s_du = reinterpret_cast<float*>(s_tiles);
+    const int rp4 = (r + 3) & ~3;
+    for (int i = tid; i < 16 * rp4; i += kDsThreads) {
+      const int m = i / rp4, j = i % rp4;
+      s_du[i] = (m < M && j < r) ? a.du[m * r + j] : 0.0f;
+    }
+    __syncthreads();
+    const int64_t k = static_cast<int64_t>(pan) * kDsCols + (tid & (kDsCols - 1));
+    if (k < K) {
+      for (int j0 = (tid / kDsCols) * 32; j0 < r; j0 += 64) {
+        float sa[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) sa[e] = 0.0f;
+        // one token at a time (not unrolled: the registers of the main loop's
+        // occupancy budget stay free)
+#pragma unroll 1
+        for (int m = 0; m < M; ++m) {
+          const float xm = bf16_to_f32(a.x[m * K + k]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const f32x4 d = *reinterpret_cast<const f32x4*>(&s_du[m * rp4 + j0 + 4 * q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sa[4 * q + e] = __builtin_fmaf(d[e], xm, sa[4 * q + e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+          if (j0 + e < r) a.dA[(j0 + e) * K + k] = f32_to_bf16(sa[e]);
       }
     }
   }

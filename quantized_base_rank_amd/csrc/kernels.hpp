@@ -201,6 +201,8 @@ struct DxStreamArgs {
   int32_t r, pool_shift;
   int32_t adapter;
   uint16_t* dx;         // [M][K]
+  const uint16_t* x;    // [M][K] (dA)
+  uint16_t* dA;         // [r][K], or nullptr: dA = du^T x formed per panel (unpooled adapter)
   int32_t splits;       // dx_stream_splits(N, K, fmt)
   float* partial;       // dx_stream_partial_floats(N, K, fmt)
   uint32_t* counters;   // dx_stream_panels(K)
@@ -211,33 +213,24 @@ int dx_stream_splits(int64_t N, int64_t K, int fmt);
 int64_t dx_stream_partial_floats(int64_t N, int64_t K, int fmt);
 bool dx_stream_fits(int64_t N, int64_t K, int fmt);
 
-// du = s dY B for M <= 16 tokens (MFMA on bf16 inputs, fp32 sums, fixed order)
+// du = s dY B (MFMA on bf16 inputs, fp32 sums, fixed order) and
+// dB = s dY^T u (fp32) for M <= 16 tokens
 struct AdapterFewArgs {
   const uint16_t* dy;   // [M][N]
   int64_t M, N;
   const uint16_t* B;    // [N][r]
+  const float* u;       // [M][r]
   int32_t r;
   float s;
   float* du;            // [M][r]
+  uint16_t* dB;         // [N][r]
+  int32_t shares;       // adapter_few_shares(N)
   float* partial;       // adapter_few_partial_floats(N)
   uint32_t* counters;   // 1
 };
 hipError_t launch_du_few(const AdapterFewArgs& a, hipStream_t stream);
 int adapter_few_shares(int64_t N);
 int64_t adapter_few_partial_floats(int64_t N);
-// dB = s dY^T u and (dA != nullptr) dA = du^T x for M <= 16 tokens, fp32
-struct DaDbFewArgs {
-  const uint16_t* x;    // [M][K]
-  const uint16_t* dy;   // [M][N]
-  int64_t M, N, K;
-  const float* u;       // [M][r]
-  const float* du;      // [M][r]
-  int32_t r;
-  float s;
-  uint16_t* dA;         // [r][K] or nullptr (pooled adapter: formed elsewhere)
-  uint16_t* dB;         // [N][r]
-};
-hipError_t launch_dadb_few(const DaDbFewArgs& a, hipStream_t stream);
 
 // Low-rank plus quantized decomposition (lq.hip): device scratch and steps
 struct LqScratch {

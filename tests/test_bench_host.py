@@ -41,7 +41,9 @@ def test_kernel_work_is_the_closed_form_count():
     assert wl.packed_weight_bytes() == packed == 121_167_872
     m = 16
     w16 = wl.with_m(m)
-    assert bench.kernel_work(w16, "k_gemv_dx_stream") == (packed + 2 * m * N + 2 * r * K + 4 * m * r + 2 * m * K, "byte")
+    # dX pass: W, dY, A, du, dX, and (unpooled adapter) x and dA formed per panel
+    assert bench.kernel_work(w16, "k_gemv_dx_stream") == (
+        packed + 2 * m * N + 2 * r * K + 4 * m * r + 2 * m * K + 2 * m * K + 2 * r * K, "byte")
     assert bench.kernel_work(w16, "k_gemv_fwd_stream") == (packed + 2 * m * K + 2 * N * r + 4 * m * r + 2 * m * N, "byte")
     assert bench.streamed(w16) and not bench.streamed(wl)
 

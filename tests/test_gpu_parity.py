@@ -419,3 +419,20 @@ def test_layer_streamed_few_token(qb, oracle, d_out, d_in, M, r, fmt, pool, dq):
     (K split over the resident workgroups, ticketed fixed-order fix-up)."""
     _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r, fmt=fmt, pool=pool, dq=dq)
     _check(oracle, got, ref)
+
+
+@pytest.mark.parametrize("d_out,d_in,M,r,fmt,pool", [
+    (4096, 8256, 5, 64, "nf4", 1),      # streamed backward: dA formed without the dX pass
+    (4096, 8256, 16, 64, "int4", 32),   # streamed, pooled adapter
+    (336, 1088, 7, 16, "nf4", 1),       # one-shot few-token kernel
+    (256, 1280, 100, 16, "nf4", 1),     # large-M path
+])
+def test_backward_without_input_gradient(qb, oracle, d_out, d_in, M, r, fmt, pool):
+    """dX is optional (the first layer of a network needs none); dA and dB
+    must come out the same way without it."""
+    qw, (x, A, Bd, dy), got, ref = _layer_case(qb, oracle, d_out, d_in, M, r, fmt=fmt, pool=pool)
+    _, u = qb.qlin_fwd(qw, x, A, Bd, r, 2.0, pool)
+    dx, dA, dB = qb.qlin_bwd(qw, x, A, Bd, r, 2.0, dy, pool, u_saved=u, need_dx=False)
+    assert dx is None
+    got2 = {"dA": oracle.bf16_bits_to_f64(bf16_host_bits(dA)), "dB": oracle.bf16_bits_to_f64(bf16_host_bits(dB))}
+    _check(oracle, got2, ref, keys=("dA", "dB"))
