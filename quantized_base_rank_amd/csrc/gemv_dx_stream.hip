@@ -18,8 +18,9 @@
 //   add their sums in fixed order; row shares publish fp32 partial sums
 //   (write-through stores) and the last workgroup of a panel (atomic ticket)
 //   adds them in fixed share order, adds du A with MFMAs (du split into bf16
-//   hi + lo halves) and stores dX; with an unpooled adapter it then forms
-//   dA = du^T x for the panel's columns.
+//   hi + lo halves) and stores dX.  With an unpooled adapter every workgroup
+//   also forms its share of dA = du^T x over the panel's columns (a slice of
+//   the adapter rows; du is complete before the launch).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -265,6 +266,36 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
     for (int c = 0; c < 4; ++c) acc[c] += *reinterpret_cast<const f32x4*>(&s_red[((blk * 64 + lane) * 4 + c) * 4]);
   }
 
+  // dA over the panel's columns (unpooled adapter; du is final before this
+  // launch): dA[j][k] = sum_m du[m][j] x[m][k], fp32 fma over the tokens in
+  // order.  The row shares of a panel split the adapter rows between them;
+  // du is staged in LDS beside the reduction buffer.
+  const int r = a.r;
+  if (a.dA != nullptr) {
+    float* s_du = reinterpret_cast<float*>(s_tiles + 32768);
+    const int rp4 = (r + 3) & ~3;
+    for (int i = tid; i < 16 * rp4; i += kDsThreads) {
+      const int m = i / rp4, j = i % rp4;
+      s_du[i] = (m < M && j < r) ? a.du[m * r + j] : 0.0f;
+    }
+    __syncthreads();
+    const int jper = (r + S - 1) / S, jlo = sh * jper, jhi = jlo + jper < r ? jlo + jper : r;
+    const int64_t k = static_cast<int64_t>(pan) * kDsCols + (tid & (kDsCols - 1));
+    if (k < K) {
+      float xv[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) xv[m] = m < M ? bf16_to_f32(a.x[m * K + k]) : 0.0f;
+#pragma unroll 1
+      for (int j = jlo + tid / kDsCols; j < jhi; j += kDsThreads / kDsCols) {
+        float sa = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          if (m < M) sa = __builtin_fmaf(s_du[m * rp4 + j], xv[m], sa);
+        a.dA[j * K + k] = f32_to_bf16(sa);
+      }
+    }
+  }
+
   // lane (l16, g) holds tokens 4 g .. 4 g + 3: lanes whose tokens all lie
   // past M hold no output and move no partial sums
   const bool live = 4 * g < M;
@@ -307,7 +338,6 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
   // adapter term du A over the panel: A staged in LDS as rows of the panel's
   // 256 columns (pooled A expanded: column k reads A[.][k >> pool_shift]),
   // zero past r (to the next multiple of 32) and past K
-  const int r = a.r;
   if (a.adapter) {
     __syncthreads();  // the reduction buffer is free again
     const int rp = (r + 31) & ~31;
@@ -367,43 +397,6 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
     }
   }
 
-  // dA over the panel's columns (unpooled adapter; du is final before this
-  // launch): dA[j][k] = sum_m du[m][j] x[m][k], fp32 fma over the tokens in
-  // order.  du is staged in LDS; a thread takes one column k and every other
-  // run of 32 adapter columns.
-  if (a.dA != nullptr) {
-    __syncthreads();  // the staged adapter panel is no longer read
-    float* s_du = reinterpret_cast<float*>(s_tiles);
-    const int rp4 = (r + 3) & ~3;
-    for (int i = tid; i < 16 * rp4; i += kDsThreads) {
-      const int m = i / rp4, j = i % rp4;
-      s_du[i] = (m < M && j < r) ? a.du[m * r + j] : 0.0f;
-    }
-    __syncthreads();
-    const int64_t k = static_cast<int64_t>(pan) * kDsCols + (tid & (kDsCols - 1));
-    if (k < K) {
-      for (int j0 = (tid / kDsCols) * 32; j0 < r; j0 += 64) {
-        float sa[32];
-#pragma unroll
-        for (int e = 0; e < 32; ++e) sa[e] = 0.0f;
-        // one token at a time (not unrolled: the registers of the main loop's
-        // occupancy budget stay free)
-#pragma unroll 1
-        for (int m = 0; m < M; ++m) {
-          const float xm = bf16_to_f32(a.x[m * K + k]);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const f32x4 d = *reinterpret_cast<const f32x4*>(&s_du[m * rp4 + j0 + 4 * q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sa[4 * q + e] = __builtin_fmaf(d[e], xm, sa[4 * q + e]);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 32; ++e)
-          if (j0 + e < r) a.dA[(j0 + e) * K + k] = f32_to_bf16(sa[e]);
-      }
-    }
-  }
 }
 
 }  // namespace
