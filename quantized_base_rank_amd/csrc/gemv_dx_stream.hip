@@ -204,12 +204,39 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
   f32x4 acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // dA over the panel's columns (unpooled adapter; du is complete before
+  // this launch): dA[j][k] = sum_m du[m][j] x[m][k], fp32 fma over the tokens
+  // in order.  The row shares of a panel split the adapter rows between
+  // them; a wave's rows are uniform, so du is read through scalar loads.
+  // The token loads go out ahead of the pipeline's first loads and the sums
+  // run while those are in flight.
+  const int r = a.r;
+  const bool do_da = a.dA != nullptr;
+  const int64_t kda = static_cast<int64_t>(pan) * kDsCols + (tid & (kDsCols - 1));
+  const int64_t kdc = kda < K ? kda : K - 1;
+  // (branch-free: a branch join here would wait for these loads before the
+  // pipeline's go out; without dA they re-read the first dY element)
+  const uint16_t* const xsrc = do_da ? a.x : a.dy;
+  uint16_t xraw[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) xraw[m] = xsrc[do_da ? (m < M ? m : M - 1) * K + kdc : 0];
   DsSlot ring[2];
   {
     Raw raw;
     load_raw(i0, raw);
     load_slot(i0, ring[0]);
     load_slot(i0 + 1, ring[1]);
+    if (do_da) {
+      const int jper = (r + S - 1) / S, jlo = sh * jper, jhi = jlo + jper < r ? jlo + jper : r;
+#pragma unroll 1
+      for (int j = jlo + __builtin_amdgcn_readfirstlane(tid / kDsCols); j < jhi; j += kDsThreads / kDsCols) {
+        float sa = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          if (m < M) sa = __builtin_fmaf(a.du[m * r + j], bf16_to_f32(xraw[m]), sa);
+        if (kda < K) a.dA[j * K + kda] = f32_to_bf16(sa);
+      }
+    }
     write_tab(i0, raw, 0);
   }
   __syncthreads();
@@ -264,36 +291,6 @@ __global__ __launch_bounds__(kDsThreads, FMT == kFmtNF4 ? 4 : 2) void k_gemv_dx_
   if (half == 0) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] += *reinterpret_cast<const f32x4*>(&s_red[((blk * 64 + lane) * 4 + c) * 4]);
-  }
-
-  // dA over the panel's columns (unpooled adapter; du is final before this
-  // launch): dA[j][k] = sum_m du[m][j] x[m][k], fp32 fma over the tokens in
-  // order.  The row shares of a panel split the adapter rows between them;
-  // du is staged in LDS beside the reduction buffer.
-  const int r = a.r;
-  if (a.dA != nullptr) {
-    float* s_du = reinterpret_cast<float*>(s_tiles + 32768);
-    const int rp4 = (r + 3) & ~3;
-    for (int i = tid; i < 16 * rp4; i += kDsThreads) {
-      const int m = i / rp4, j = i % rp4;
-      s_du[i] = (m < M && j < r) ? a.du[m * r + j] : 0.0f;
-    }
-    __syncthreads();
-    const int jper = (r + S - 1) / S, jlo = sh * jper, jhi = jlo + jper < r ? jlo + jper : r;
-    const int64_t k = static_cast<int64_t>(pan) * kDsCols + (tid & (kDsCols - 1));
-    if (k < K) {
-      float xv[16];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) xv[m] = m < M ? bf16_to_f32(a.x[m * K + k]) : 0.0f;
-#pragma unroll 1
-      for (int j = jlo + tid / kDsCols; j < jhi; j += kDsThreads / kDsCols) {
-        float sa = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-          if (m < M) sa = __builtin_fmaf(s_du[m * rp4 + j], xv[m], sa);
-        a.dA[j * K + k] = f32_to_bf16(sa);
-      }
-    }
   }
 
   // lane (l16, g) holds tokens 4 g .. 4 g + 3: lanes whose tokens all lie
