@@ -144,17 +144,26 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   const int dpiece = (lane & 3) ^ ((lane >> 4) & 3);  // source piece of this lane
   const uint32_t dyvoff = static_cast<uint32_t>((wave * 16 + (lane >> 2)) * N * 2 + (dpiece << 4));
   const int n_tail = static_cast<int>(N % kNS);  // valid rows of the last step (0: all)
-  uint32_t dtail_oob[2];
+  // lane offsets of the last step's two parts (pieces past N out of range)
+  uint32_t dyvoff_tail[2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) dtail_oob[p] = (n_tail != 0 && 32 * p + 8 * dpiece >= n_tail) ? 0x80000000u : 0u;
-  auto load_dyh = [&](int64_t st, int part, uint8_t* dst, int i0, int n) {
-    const int64_t stc = st < nsteps ? st : nsteps - 1;
+  for (int p = 0; p < 2; ++p)
+    dyvoff_tail[p] = dyvoff | ((n_tail != 0 && 32 * p + 8 * dpiece >= n_tail) ? 0x80000000u : 0u);
+  // a step past the last one loads through an empty resource
+  const rsrc_t dyr_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.dy), 0, 0, 0x00020000);
+  // (step indices are wave-uniform: read into scalar registers, so that the
+  // range tests below are scalar and pick between prepared offsets)
+  const int nsteps_s = __builtin_amdgcn_readfirstlane(static_cast<int>(nsteps));
+  auto load_dyh = [&](int64_t st64, int part, uint8_t* dst, int i0, int n) {
+    const int st = __builtin_amdgcn_readfirstlane(static_cast<int>(st64));
+    const int stc = st < nsteps_s ? st : nsteps_s - 1;
     const uint32_t nb = static_cast<uint32_t>(stc * kNS * 2 + 64 * part);
-    const uint32_t oob = (st >= nsteps ? 0x80000000u : 0u) | (st == nsteps - 1 ? dtail_oob[part] : 0u);
+    const rsrc_t rr = st < nsteps_s ? dyr : dyr_none;
+    const uint32_t voff = st == nsteps_s - 1 ? dyvoff_tail[part] : dyvoff;
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          dyr, (lds_ptr_t)(dst + (i * 4 + wave) * 1024), 16, dyvoff | oob,
+          rr, (lds_ptr_t)(dst + (i * 4 + wave) * 1024), 16, voff,
           static_cast<int>(static_cast<uint32_t>(i * 64 * N * 2) + nb), 0, 0);
   };
 
@@ -170,8 +179,9 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
     const int crow = wave * 16 + 8 * i + (lane >> 3);
     cvoff[i] = static_cast<uint32_t>(crow * (K >> 1) + (k0 >> 1) + (((lane & 7) ^ ((crow >> 1) & 7)) << 4));
   }
-  auto dma_codes = [&](int64_t st, int stage, int i0, int n) {
-    const int64_t stc = st < nsteps ? st : nsteps - 1;
+  auto dma_codes = [&](int64_t st64, int stage, int i0, int n) {
+    const int st = __builtin_amdgcn_readfirstlane(static_cast<int>(st64));
+    const int64_t stc = st < nsteps_s ? st : nsteps_s - 1;
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -224,8 +234,12 @@ __global__ __launch_bounds__(256, 1) void k_dx_gemm(DxArgs a) {
   constexpr int NL = FMT == kFmtNF4 ? 1 : 2;
   Lut16 lut[2][NL];
   float lscale[2];
+  // Columns past K need no mask: a weight column feeds only its own dX
+  // column, and those past K are never stored.  NF4 rows past N read zero
+  // constants (their offsets lie past the constant arrays) and so get
+  // all-zero tables; INT4 tables of such rows are masked.
   auto build_lut_part = [&](int set, const RowParams<FMT>& rc, int64_t st, int part) {
-    const bool valid = kvalid && st * kNS + lane < N;
+    const bool valid = FMT == kFmtNF4 || st * kNS + lane < N;
     if constexpr (FMT == kFmtNF4) {
       if (part == 0) lscale[set] = nf4_params_scale_sel(a.w, BlockParams{(rc.bp.a >> rc.sh) & 0xFFu, rc.bp.b}, valid);
       const float sc = lscale[set];
