@@ -186,6 +186,13 @@ __device__ __forceinline__ void stage_barrier() {
   __asm__ volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// A wave-uniform value the compiler may not hoist or fold: each use forms
+// what depends on it where it is used.
+__device__ __forceinline__ int opaque_sgpr(int v) {
+  __asm__ volatile("" : "+s"(v));
+  return v;
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   // Four token half-stages and two code stages, each an array of its own so
@@ -248,17 +255,28 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
   const int xpc = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);  // source piece of this lane
   const uint32_t xvoff = static_cast<uint32_t>((8 * wave + (lane >> 3)) * K * 2 + 128 * (xpc >> 2) +
                                                16 * (xpc & 3));
-  const uint32_t xtail_oob = xpc >= 4 ? 0x80000000u : 0u;
-  const int64_t ks_tail = (K % kKS) != 0 ? ksteps - 1 : -1;
-  auto load_xhalf = [&](int64_t ks, int part, uint8_t* dst, int i0, int n) {
-    const int64_t kc = ks < ks1 ? ks : ks1 - 1;
+  const uint32_t xvoff_tail = xvoff | (xpc >= 4 ? 0x80000000u : 0u);  // the last step's lane offset
+  // a step past the range loads through an empty resource
+  const rsrc_t xr_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, 0, 0x00020000);
+  // (step indices are wave-uniform: taken into scalar registers, so that the
+  // range tests are scalar and pick between prepared offsets)
+  const int ks1_s = __builtin_amdgcn_readfirstlane(static_cast<int>(ks1));
+  const int ks_tail_s = __builtin_amdgcn_readfirstlane(static_cast<int>((K % kKS) != 0 ? ksteps - 1 : -1));
+  // LDS offset of this wave's slot in a stage.  Made opaque at each use, so
+  // that the destination of every load is formed where the load is issued
+  // (scalar adds) instead of being computed once per destination and held
+  // for the whole loop, which runs the scalar registers out.
+  const int wslot = wave * 1024;
+  auto load_xhalf = [&](int64_t ks64, int part, uint8_t* dst, int i0, int n) {
+    const int ks = __builtin_amdgcn_readfirstlane(static_cast<int>(ks64));
+    const int kc = ks < ks1_s ? ks : ks1_s - 1;
     const uint32_t kb2 = static_cast<uint32_t>(kc * kKS * 2 + 64 * part);
-    const uint32_t oob = (ks >= ks1 ? 0x80000000u : 0u) | (ks == ks_tail ? xtail_oob : 0u);
-    const uint32_t voff = xvoff | oob;
+    const rsrc_t rr = ks < ks1_s ? xr : xr_none;
+    const uint32_t voff = ks == ks_tail_s ? xvoff_tail : xvoff;
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (lds_ptr_t)(dst + (i * 4 + wave) * 1024), 16, voff,
+          rr, (lds_ptr_t)(dst + i * 4096 + opaque_sgpr(wslot)), 16, voff,
           static_cast<int>(static_cast<uint32_t>(i * 32 * K * 2) + kb2), 0, 0);
   };
   // Packed codes of a K step: 256 rows x 64 B in a code stage.  A load
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          cr, (lds_ptr_t)(dst + (i * 4 + wave) * 1024), 16, cvoff,
+          cr, (lds_ptr_t)(dst + i * 4096 + opaque_sgpr(wslot)), 16, cvoff,
           static_cast<int>(static_cast<uint32_t>(i * 64 * (K >> 1)) + kb), 0, 0);
   };
   // this lane's 16 code words of a step: rows wave*64 + r*32 + l32, half h
@@ -330,7 +348,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_gemm(FwdArgs a) {
 #pragma unroll
     for (int ms = 0; ms < 8; ++ms) xf[ms] = *reinterpret_cast<const u32x4*>(xb + o + ms * 4096);
   };
-  auto step_valid = [&](int64_t ks) { return ks < ks1 && ks * kKS + h * 64 < K; };
+  auto step_valid = [&](int64_t ks64) {
+    const int ks = __builtin_amdgcn_readfirstlane(static_cast<int>(ks64));
+    return ks < ks1_s && ks * kKS + h * 64 < static_cast<int>(K);
+  };
 
   // Pipeline.  The K steps run in pairs: step 2j + SI of the range uses
   // token half-stages (s_x0, s_x1) or (s_x2, s_x3) and code stage s_c0 or
