@@ -125,17 +125,28 @@ __global__ __launch_bounds__(kFsThreads, 2 * QLIN_FS_WGS_PER_CU) void k_gemv_fwd
   // steps past the share reload its last step (no extra HBM traffic)
   const int clast = c1 > c0 ? c1 - 1 : nchk - 1;
   auto clampc = [&](int c) { return c < clast ? c : clast; };
+  // Token offsets: a lane part fixed for the kernel and a chunk part in the
+  // scalar operand; the last chunk clamps its columns into the row through
+  // a lane part of its own.
+  const int64_t klast = static_cast<int64_t>(nchk - 1) * kFsChunk;
+  uint32_t xoff[kFsXPer], xoff_last[kFsXPer];
+#pragma unroll
+  for (int i = 0; i < kFsXPer; ++i) {
+    const int64_t rel = (xp0 + i) * 8;
+    const int64_t rel_last = klast + rel < K ? rel : K - 8 - klast;
+    xoff[i] = static_cast<uint32_t>((xrc * K + rel) * 2);
+    xoff_last[i] = static_cast<uint32_t>((xrc * K + rel_last) * 2);
+  }
   auto load_slot = [&](int c, FsSlot& sl) {
-    const uint32_t off = voff_c + static_cast<uint32_t>(clampc(c) * (kFsChunk / 2));
+    const int cc = __builtin_amdgcn_readfirstlane(clampc(c));
+    const int cso = static_cast<int>(static_cast<uint32_t>(cc) * static_cast<uint32_t>(kFsChunk / 2));
 #pragma unroll
     for (int j = 0; j < 2 * kFsBlk; ++j)
-      sl.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, off + 16 * j, 0, 0);
+      sl.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, voff_c + 16 * j, cso, 0);
+    const int xso = static_cast<int>(static_cast<uint32_t>(cc) * static_cast<uint32_t>(kFsChunk * 2));
 #pragma unroll
-    for (int i = 0; i < kFsXPer; ++i) {
-      int64_t k = static_cast<int64_t>(clampc(c)) * kFsChunk + (xp0 + i) * 8;
-      k = k < K ? k : K - 8;
-      sl.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<uint32_t>((xrc * K + k) * 2), 0, 0);
-    }
+    for (int i = 0; i < kFsXPer; ++i)
+      sl.x[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, cc == nchk - 1 ? xoff_last[i] : xoff[i], xso, 0);
   };
   auto store_x = [&](int buf, const FsSlot& sl) {
 #pragma unroll
