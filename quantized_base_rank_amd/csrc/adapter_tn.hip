@@ -7,9 +7,11 @@
 //     dA = du^T x     (X = x,  P = d_in,  Z = du, C = dA [r][d_in], transposed)
 //
 // The work is one pass over X (dY or x), which is large; u / du are narrow.
-// A workgroup owns 128 columns of X and a share of the tokens.  Each 64-token
+// A workgroup owns 128 columns of X and a share of the tokens.  Each 32-token
 // stage of X and of Z is copied to LDS in its natural layout with whole-line
-// direct-to-LDS loads, and the transposing LDS read (ds_read_b64_tr_b16)
+// direct-to-LDS loads into a ring of stages (four for r <= 64, three above),
+// issued that many stages less one ahead, so that two workgroups per compute
+// unit keep about 48 KB of X in flight; the transposing LDS read (ds_read_b64_tr_b16)
 // turns 8 consecutive tokens of one column into an MFMA operand, so neither
 // operand is transposed in memory.  Z enters the bf16 MFMA as two planes,
 // hi = bf16(z) and lo = bf16(z - hi), keeping its fp32 precision.  Token
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256) void k_split_hl(const float* __restrict__ Z, i
 }
 
 constexpr int kTp = 128;  // columns of X per workgroup
-constexpr int kTm = 64;   // tokens per stage
+constexpr int kTm = 32;   // tokens per stage
 
 // 16-byte chunk swizzle of a staged row: 16 lanes of a transposing read take
 // 4 consecutive rows x 2 adjacent chunks; XOR-ing the chunk index with
@@ -83,13 +85,20 @@ __global__ __launch_bounds__(256) void k_tn2(Tn2Args a) {
   constexpr int JG = JP / 16;              // 16-wide groups of j
   constexpr int kXC = kTp * 2 / 16;        // 16 chunks per X row
   constexpr int kZC = JP * 2 / 16;         // 8 or 16 chunks per Z row
-  constexpr int kXB = kTm * kTp * 2;       // 16 KB
-  constexpr int kZB = kTm * JP * 2;        // 8 or 16 KB per plane
+  constexpr int kXB = kTm * kTp * 2;       // 8 KB
+  constexpr int kZB = kTm * JP * 2;        // 4 or 8 KB per plane
   constexpr int kStage = kXB + 2 * kZB;
-  __shared__ __attribute__((aligned(16))) uint8_t s[2][kStage];
+  constexpr int kRing = JP == 64 ? 4 : 3;  // 64 or 72 KB: two workgroups per compute unit
+  // one array per ring slot: a read of one slot then does not wait for the
+  // direct-to-LDS loads still landing in the others
+  __shared__ __attribute__((aligned(16))) uint8_t s0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s2[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s3[kRing == 4 ? kStage : 16];
   __shared__ uint32_t s_ticket;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int tiles = static_cast<int>((a.P + kTp - 1) / kTp);
   const int lin = tn_xcd_order(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
@@ -112,18 +121,19 @@ __global__ __launch_bounds__(256) void k_tn2(Tn2Args a) {
   const rsrc_t zlr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.Zl + mb0 * JP), 0, static_cast<int>(rows * JP * 2), 0x00020000);
 
-  // stage loads: X 16 instructions of 4 rows x 256 B; each Z plane
+  // stage loads: X 8 instructions of 4 rows x 256 B; each Z plane
   // kZB / 1 KB instructions of (1024 / (kZC * 16)) rows; instruction i is
-  // issued by wave i % 4
-  auto load_stage = [&](int st, int buf) {
-    const uint32_t m_rel = static_cast<uint32_t>(st * kTm);
+  // issued by wave i % 4, so every wave issues kStageLoads per stage.  A stage
+  // past the share starts at its end and reads zeros (outside the resources).
+  auto load_stage = [&](int st, uint8_t* sb) {
+    const uint32_t m_rel = static_cast<uint32_t>((st < nstages ? st : nstages) * kTm);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int ii = 0; ii < kXB / 4096; ++ii) {
       const int i = ii * 4 + wave;
       const int row = 4 * i + (lane >> 4);
       const int c = (lane & 15) ^ tn_swz<kXC>(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (lds_ptr_t)(&s[buf][i * 1024]), 16,
+          xr, (lds_ptr_t)(sb + i * 1024), 16,
           static_cast<uint32_t>(((lane >> 4) * a.ldx) * 2 + c * 16),
           static_cast<int>((m_rel + 4 * i) * a.ldx * 2), 0, 0);
     }
@@ -136,9 +146,9 @@ __global__ __launch_bounds__(256) void k_tn2(Tn2Args a) {
       const int c = (lane % kZC) ^ tn_swz<kZC>(row);
       const uint32_t voff = static_cast<uint32_t>((lane / kZC) * JP * 2 + c * 16);
       const int soff = static_cast<int>((m_rel + ZROWS * i) * JP * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zhr, (lds_ptr_t)(&s[buf][kXB + i * 1024]), 16, voff,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zhr, (lds_ptr_t)(sb + kXB + i * 1024), 16, voff,
                                                soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zlr, (lds_ptr_t)(&s[buf][kXB + kZB + i * 1024]), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zlr, (lds_ptr_t)(sb + kXB + kZB + i * 1024), 16,
                                                voff, soff, 0, 0);
     }
   };
@@ -149,32 +159,58 @@ __global__ __launch_bounds__(256) void k_tn2(Tn2Args a) {
 #pragma unroll
     for (int jg = 0; jg < JG; ++jg) acc[pg][jg] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nstages > 0) load_stage(0, 0);
-  for (int st = 0; st < nstages; ++st) {
-    const int buf = st & 1;
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (st + 1 < nstages) load_stage(st + 1, buf ^ 1);
-    const uint8_t* xs = s[buf];
-    const uint8_t* zh = s[buf] + kXB;
-    const uint8_t* zl = s[buf] + kXB + kZB;
+  // Stage st sits in ring slot st % kRing.  The loads of stage st + kRing - 1
+  // go into the slot of stage st - 1 after the barrier that ends its use;
+  // every iteration issues them (past the share they read zeros), so the
+  // wait before stage st always leaves exactly kRing - 2 stages in flight.
+  // The stage loop is unrolled by kRing, so that each slot is a fixed array,
+  // and runs whole turns of the ring: the stages past the share hold zeros
+  // and add nothing.  (An early exit inside the turn makes the compiler merge
+  // the pending loads of every slot at the loop head and wait for all of them
+  // before the first read.)
+  static_assert(kZB / 1024 % 4 == 0, "Z plane loads split evenly over the waves");
+  if (nstages > 0) {
 #pragma unroll
-    for (int kb = 0; kb < kTm; kb += 32) {
-      u32x4 af[2];
+    for (int i = 0; i < kRing - 1; ++i)
+      load_stage(i, i == 0 ? s0 : i == 1 ? s1 : s2);
+  }
+  for (int st0 = 0; st0 < nstages; st0 += kRing) {
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg) af[pg] = tn_operand<kXC>(xs, kb + 8 * g, wave * 32 + pg * 16, l16);
+    for (int i = 0; i < kRing; ++i) {
+      const int st = st0 + i;
+      // this wave's loads of stage st have landed and its reads of stage
+      // st - 1 are done, then the waves meet (one asm block: a fence here
+      // would wait for every direct-to-LDS load in flight)
+      if constexpr (kRing == 4)  // 2 stages x (2 X + 2 Z) loads stay in flight
+        __asm__ volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else  // 1 stage x (2 X + 4 Z) loads
+        __asm__ volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const int nx = (i + kRing - 1) % kRing;
+      load_stage(st + kRing - 1, nx == 0 ? s0 : nx == 1 ? s1 : nx == 2 ? s2 : s3);
+      const uint8_t* xs = i == 0 ? s0 : i == 1 ? s1 : i == 2 ? s2 : s3;
+      const uint8_t* zh = xs + kXB;
+      const uint8_t* zl = xs + kXB + kZB;
 #pragma unroll
-      for (int jg = 0; jg < JG; ++jg) {
-        const u32x4 bh = tn_operand<kZC>(zh, kb + 8 * g, jg * 16, l16);
-        const u32x4 bl = tn_operand<kZC>(zl, kb + 8 * g, jg * 16, l16);
+      for (int kb = 0; kb < kTm; kb += 32) {
+        u32x4 af[2];
 #pragma unroll
-        for (int pg = 0; pg < 2; ++pg) {
-          acc[pg][jg] = mfma16(af[pg], bh, acc[pg][jg]);
-          acc[pg][jg] = mfma16(af[pg], bl, acc[pg][jg]);
+        for (int pg = 0; pg < 2; ++pg) af[pg] = tn_operand<kXC>(xs, kb + 8 * g, wave * 32 + pg * 16, l16);
+#pragma unroll
+        for (int jg = 0; jg < JG; ++jg) {
+          const u32x4 bh = tn_operand<kZC>(zh, kb + 8 * g, jg * 16, l16);
+          const u32x4 bl = tn_operand<kZC>(zl, kb + 8 * g, jg * 16, l16);
+#pragma unroll
+          for (int pg = 0; pg < 2; ++pg) {
+            acc[pg][jg] = mfma16(af[pg], bh, acc[pg][jg]);
+            acc[pg][jg] = mfma16(af[pg], bl, acc[pg][jg]);
+          }
         }
       }
     }
   }
+
+  // the loads issued past the share land in LDS before the workgroup ends
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // lane (l16, g) of tile (pg, jg) holds D[p = 32 w + 16 pg + 4 g + v][j = 16 jg + l16]
   const int S = a.splits;

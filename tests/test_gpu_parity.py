@@ -172,6 +172,9 @@ def _check(oracle, got, ref, keys=("y", "u", "dX", "dA", "dB")):
     (1040, 768, 513, 48),
     (512, 4096, 260, 16),     # few tiles, long K: split-K with ticketed fix-up
     (256, 1280, 100, 16),     # split-K with an odd number of K steps per split (a masked pad step)
+    (400, 640, 600, 96),      # MFMA path, adapter wider than 64: three-slot ring in the dA / dB
+                              # reductions, two token shares of 300 (ragged last stage)
+    (272, 1088, 300, 128),    # MFMA path, widest adapter
 ])
 def test_layer_nf4(qb, oracle, d_out, d_in, M, r):
     _, _, got, ref = _layer_case(qb, oracle, d_out, d_in, M, r)
