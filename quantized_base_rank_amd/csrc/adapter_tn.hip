@@ -11,7 +11,7 @@
 // stage of X and of Z is copied to LDS in its natural layout with whole-line
 // direct-to-LDS loads into a ring of stages (four for r <= 64, three above),
 // issued that many stages less one ahead, so that two workgroups per compute
-// unit keep about 48 KB of X in flight; the transposing LDS read (ds_read_b64_tr_b16)
+// unit keep up to 48 KB of X in flight (r <= 64); the transposing LDS read (ds_read_b64_tr_b16)
 // turns 8 consecutive tokens of one column into an MFMA operand, so neither
 // operand is transposed in memory.  Z enters the bf16 MFMA as two planes,
 // hi = bf16(z) and lo = bf16(z - hi), keeping its fp32 precision.  Token
